@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark of deferred-RoPE attention over a position-agnostic paged KV pool on one MI355X.
+
+Workload (one step = one prefill launch over the whole batch): the
+Llama-3.1-8B attention-layer shape in bf16 (32 query heads, 8 KV heads,
+head_dim 128, RoPE theta 5e5, blocks of 16 tokens); 16 requests, each 8
+distinct documents of 512 tokens drawn Zipf(1.0) from a pool of 256
+documents and placed in random order (4096 context tokens), followed by a
+64-token query prefilled causally.  Inputs are seeded synthetic data already
+resident in HBM.  The new tokens' K/V are appended once before timing.
+
+Also reported on the same line: the same launch with rotation disabled
+(deferred-RoPE overhead), decode on the Llama-3.1-8B decode shape (128
+requests x 8 Zipf(1.2) documents, per-step HBM bytes), and the fp64 CPU
+oracle on the same prefill batch.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+  python bench.py --calibrate-copy           # a plain copy kernel, for counter scaling
+  python bench.py --summarize-rocprof DIR    # print a rocprofv3 CSV directory as a summary
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s + decode KV GB/s (% of MI355X peak), deferred-RoPE attention"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "position_agnostic_kv_pool_amd", "csrc", "lazyattn_kernels.hip")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_bf16_llama8b_counters.txt")
+DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_bf16_llama8b_counters.txt")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_counter_summary(path: str):
+    """(bytes per dispatch from FETCH_SIZE + WRITE_SIZE scaled by the copy calibration) if the
+    summary was taken on the current kernel source, else None."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        fetch = float(kv["fetch_kib_per_dispatch"])
+        write = float(kv["write_kib_per_dispatch"])
+        scale = float(kv["copy_scale"])
+    except (KeyError, ValueError):
+        return None
+    return (fetch + write) * 1024.0 * scale
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 CSV summaries
+# ---------------------------------------------------------------------------
+def summarize_rocprof(d: str) -> None:
+    import csv
+    from collections import defaultdict
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        print(f"# kernel stats: {os.path.relpath(path, d)}")
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        for r in rows:
+            name = r.get("Name", r.get("KernelName", "?"))
+            print(f"{name[:90]:90s} calls {r.get('Calls')}  avg_ns {float(r.get('AverageNs', 0)):.0f}  "
+                  f"min_ns {r.get('MinNs')}  max_ns {r.get('MaxNs')}  pct {float(r.get('Percentage', 0)):.2f}")
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        print(f"# counters: {os.path.relpath(path, d)}")
+        acc = defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", r.get("Kernel-Name", "?"))
+                acc[(name, r.get("Counter_Name"))].append(float(r.get("Counter_Value", 0)))
+        for (name, cn), vals in sorted(acc.items()):
+            print(f"{name[:90]:90s} {cn:24s} dispatches {len(vals)}  mean_per_dispatch {sum(vals) / len(vals):.1f}")
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def prefill_flops(pb, head_dim: int, num_q_heads: int) -> float:
+    """4 * D * Hq * sum over queries of the keys each one sees (QK^T and PV, causal)."""
+    tot = 0
+    cu = pb["cu_q_lens"]
+    for r, L in enumerate(pb["ctx_lens"]):
+        m = int(cu[r + 1] - cu[r])
+        p0 = int(L) - m
+        tot += m * p0 + m * (m + 1) // 2        # sum_{j<m} (p0 + j + 1)
+    return 4.0 * head_dim * num_q_heads * tot
+
+
+def decode_bytes(d, wl) -> dict:
+    """Per-step bytes: logical (what a per-request paged kernel streams), unique (each
+    (block, KV head) once), plus queries, outputs and table words."""
+    s = wl.spec
+    esz = 2 if s.dtype == "bf16" else 4
+    R = len(d["ctx_lens"])
+    kv_logical = sum(int(L) for L in d["ctx_lens"]) * s.num_kv_heads * s.head_dim * 2 * esz
+    blocks = set()
+    for i in range(R):
+        n = int(d["num_entries"][i])
+        blocks.update(int(b) for b in d["table_blocks"][i, :n])
+    kv_unique = len(blocks) * s.num_kv_heads * s.block_size * s.head_dim * 2 * esz
+    other = 2 * R * s.num_q_heads * s.head_dim * esz + int(sum(d["num_entries"])) * 8 + R * 8
+    return {"logical": kv_logical + other, "unique": kv_unique + other, "kv_logical": kv_logical}
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def busy(self):
+        # keep the GPU busy while the host enqueues the timed launches, so host
+        # launch latency never shows up between the events
+        if hasattr(self.torch.cuda, "_sleep"):
+            self.torch.cuda._sleep(2_000_000)
+
+    def span(self, fn, n):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        self.busy()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+
+def bench_prefill(torch, args, W, staging, _abi):
+    wl = W.build_workload(W.spec(2))
+    s = wl.spec
+    pools = staging.DevicePools(wl, "cuda")
+    pb = wl.prefill_batch()
+    cfg = staging.config_for(s)
+    staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
+    call = staging.PrefillCall(cfg, s, pb, "cuda")
+    cfg_none = staging.config_for(s, pe="none")
+    call_none = staging.PrefillCall(cfg_none, s, pb, "cuda")
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    for _ in range(args.warmup):
+        call.run(pools)
+    ms = timer.span(lambda: call.run(pools), args.steps)
+    for _ in range(args.warmup):
+        call_none.run(pools)
+    ms_none = timer.span(lambda: call_none.run(pools), args.steps)
+    ms_rope2 = timer.span(lambda: call.run(pools), args.steps)      # rope again, after the control
+    flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
+    splits = _abi.prefill_splits(cfg, len(pb["ctx_lens"]), pb["max_q_len"], pb["table_blocks"].shape[1])
+    return dict(wl=wl, pb=pb, ms=ms, ms_none=ms_none, ms_rope2=ms_rope2, flops=flops, splits=splits,
+                pools=pools)
+
+
+def bench_decode(torch, args, W, staging, _abi, n_steps: int):
+    """Decode steps 0..n_steps-1 of the 8B decode shape; events around each decode launch only."""
+    wl = W.build_workload(W.spec(3, n_decode=max(n_steps, 1)))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    cfg_none = staging.config_for(s, pe="none")
+    pools = staging.DevicePools(wl, "cuda")
+    staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, "cuda")
+    t = torch
+    tot_ms, tot_ms_none, tot_bytes, tot_unique, tokens = 0.0, 0.0, 0, 0, 0
+    for step in range(-2, n_steps):          # two untimed warm-up launches on step 0's inputs
+        d = wl.decode_step(max(step, 0))
+        if step >= 0:
+            staging.append_tokens(cfg, pools, d, s.dtype, "cuda")
+        call = staging.DecodeCall(cfg, s, d, "cuda")
+        call_none = staging.DecodeCall(cfg_none, s, d, "cuda")
+        t.cuda.synchronize()
+        a, b, c = (t.cuda.Event(enable_timing=True) for _ in range(3))
+        Timer(t).busy()
+        a.record()
+        call.run(pools)
+        b.record()
+        call_none.run(pools)
+        c.record()
+        t.cuda.synchronize()
+        if step < 0:
+            continue
+        tot_ms += a.elapsed_time(b)
+        tot_ms_none += b.elapsed_time(c)
+        by = decode_bytes(d, wl)
+        tot_bytes += by["logical"]
+        tot_unique += by["unique"]
+        tokens += len(d["ctx_lens"])
+    n = max(n_steps, 1)
+    return dict(ms=tot_ms / n, ms_none=tot_ms_none / n, bytes=tot_bytes / n, unique=tot_unique / n,
+                tokens=tokens, splits=_abi.decode_splits(cfg, len(wl.requests), wl.table_arrays(wl.requests)[0].shape[1]))
+
+
+def cpu_baseline(pre, W):
+    """The fp64 oracle on the same prefill batch (all 16 requests), host cores."""
+    import numpy as np  # noqa: F401
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    wl, pb = pre["wl"], pre["pb"]
+    s = wl.spec
+    kp, vp = wl.pools()
+    kp, vp = kp.copy(), vp.copy()
+    O.append_kv(kp, vp, pb["k_new"], pb["v_new"], pb["slots"], s.block_size)
+    words = O.pack_table(pb["table_blocks"], pb["table_starts"])
+    t0 = time.perf_counter()
+    O.prefill(q=pb["q"], cu_q_lens=pb["cu_q_lens"], ctx_lens=pb["ctx_lens"], num_entries=pb["num_entries"],
+              table_words=words, k_pool=kp, v_pool=vp, num_kv_heads=s.num_kv_heads, block_size=s.block_size,
+              dtype=s.dtype, pe=s.pe, rope_theta=s.rope_theta)
+    dt = time.perf_counter() - t0
+    return {"value": round(pre["flops"] / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "the whole timed prefill batch (16 requests x 64 queries over ~4.2k tokens), "
+                      "materialised-RoPE fp64 numpy oracle, one call"}
+
+
+def calibrate_copy(torch) -> None:
+    """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB) for counter scaling."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "dispatches": 3}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time the prefill launches only")
+    ap.add_argument("--decode-only", action="store_true", help="run decode launches only (for profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not supported: "
+              "this path runs on a single MI355X and has no multi-GPU leg", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return 0
+
+    import workloads as W
+    from position_agnostic_kv_pool_amd import _abi, staging
+    _abi.lib()
+
+    if args.decode_only:
+        dec = bench_decode(torch, args, W, staging, _abi, args.decode_steps)
+        print(json.dumps({"decode_ms_per_step": dec["ms"], "decode_GBps": dec["bytes"] / dec["ms"] / 1e6}),
+              flush=True)
+        return 0
+
+    pre = bench_prefill(torch, args, W, staging, _abi)
+    print(f"# prefill done: {pre['ms'] * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+    tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+    traffic = read_counter_summary(PREFILL_COUNTERS)
+    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "prefill_bf16_kernel<ROPE>", "flops_per_launch": pre["flops"],
+                "avg_launch_us": round(pre["ms"] * 1e3, 2)}
+    rope_overhead = {"prefill_rope_us": round(pre["ms"] * 1e3, 2), "prefill_rope_repeat_us": round(pre["ms_rope2"] * 1e3, 2),
+                     "prefill_norotation_us": round(pre["ms_none"] * 1e3, 2),
+                     "prefill_overhead": round(min(pre["ms"], pre["ms_rope2"]) / pre["ms_none"] - 1.0, 4)}
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill, Llama-3.1-8B attention layer (Hq 32, Hkv 8, d 128, RoPE theta 5e5, "
+                               "block 16): 16 requests x 8 Zipf(1.0) documents x 512 tokens + 64-token causal "
+                               "query; content-only pool, RoPE applied in-kernel",
+                   "global_batch": 16, "seq_len": int(max(pre["pb"]["ctx_lens"])), "parallelism": "single-gpu",
+                   "key_splits": pre["splits"]},
+        "roofline": roofline,
+        "rope_overhead": rope_overhead,
+    }
+    if not args.prefill_only:
+        del pre["pools"]
+        torch.cuda.empty_cache()
+        dec = bench_decode(torch, args, W, staging, _abi, args.decode_steps)
+        gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
+        dtraffic = read_counter_summary(DECODE_COUNTERS)
+        out["decode"] = {
+            "workload": "decode, Llama-3.1-8B shape: 128 requests x 8 Zipf(1.2) documents x 512 tokens "
+                        "+ 32-token suffix, steps 0..%d" % (args.decode_steps - 1),
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(dec["ms"] * 1e3, 2),
+            "tokens_per_s": round(128 / (dec["ms"] * 1e-3), 1), "splits": dec["splits"],
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dtraffic,
+                         "kernel": "decode_bf16_kernel<ROPE,1>", "bytes_per_launch_logical": round(dec["bytes"]),
+                         "bytes_per_launch_unique": round(dec["unique"])},
+            "norotation_us_per_step": round(dec["ms_none"] * 1e3, 2),
+            "rope_overhead": round(dec["ms"] / dec["ms_none"] - 1.0, 4),
+        }
+        print(f"# decode done: {dec['ms'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pre, W)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,200 @@
+/*
+ * lazyattn.h - attention over a position-agnostic paged KV pool with RoPE
+ * applied lazily inside the kernels (MI355X / gfx950).
+ *
+ * The method is LazyAttention ("LazyAttention: Efficient Retrieval-Augmented
+ * Generation with Deferred Positional Encoding", arXiv 2606.04302).  Its pages
+ * say: the KV cache stores content-only keys and values and positional
+ * information is applied on the fly inside the attention kernel (gist.science
+ * explainer, Technical Summary > Methodology > Core Concept); one physical KV
+ * copy then serves many logical requests at arbitrary positions (shd-paper.top
+ * digest, original English abstract); the result equals attention over keys
+ * re-encoded at their positions, because RoPE scores depend only on the
+ * relative offset (gist.science, Mathematical Equivalence); per-block metadata
+ * (block id, offset) is bit-packed into one register-sized word (gist.science,
+ * Technical Implementation > Decoding).
+ *
+ * Conventions for every entry point below:
+ *  - Ownership: the caller owns every buffer.  The library never allocates or
+ *    frees device memory and keeps no per-call state.
+ *  - Asynchrony: GPU calls enqueue work on `stream` and return; the library
+ *    never synchronises.  Buffers must stay alive until the stream passes.
+ *  - Pointers: "device" pointers address GPU memory of the current device;
+ *    "host" pointers address CPU memory and are read before the call returns.
+ *  - Access: the K/V pools are read-only to prefill and decode (shared blocks
+ *    are never written); `out` must not alias any input.
+ *  - Errors: argument errors detectable on the host return LAZYATTN_EINVAL or
+ *    LAZYATTN_EUNSUPPORTED before any launch; a short workspace returns
+ *    LAZYATTN_EWORKSPACE; a failed launch returns LAZYATTN_EHIP.  Device-side
+ *    contract violations (a malformed table) are undefined behaviour; check
+ *    host copies with lazyattn_validate_tables.  No C++ exception crosses
+ *    this interface.
+ *
+ * Data layout (B = block_size = 16, D = head_dim, Hkv = KV heads, Hq = query
+ * heads, G = Hq / Hkv; element type = config dtype):
+ *  - K pool  [num_blocks][Hkv][B][D]   one block = B token rows of D channels
+ *  - V pool  [num_blocks][Hkv][D][B]   one block = D channel rows of B tokens
+ *    Both hold content only: keys are never rotated in storage.
+ *  - Table word (uint64): bits 63..32 logical start, bits 31..0 block id.
+ *    A request's words are ordered by logical start; the context is dense:
+ *    entry e covers logical positions [start_e, start_{e+1}) (the last one
+ *    up to ctx_len), 1 <= length <= B, first start 0.  Rows of a block past
+ *    the entry's length are padding and are never read into a result.
+ *  - Query head h reads KV head h / G.
+ *  - RoPE pairs are interleaved channels (2i, 2i+1), frequency
+ *    theta^(-2i/D); a query at position p and a key at t score
+ *    scale * q^T R(t - p) k.
+ */
+#ifndef LAZYATTN_H
+#define LAZYATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LAZYATTN_ABI_VERSION 1
+
+typedef enum {
+  LAZYATTN_OK = 0,
+  LAZYATTN_EINVAL = 1,        /* bad argument (null pointer, inconsistent sizes) */
+  LAZYATTN_EUNSUPPORTED = 2,  /* valid but not built (head_dim, block_size, dtype, group size) */
+  LAZYATTN_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_size */
+  LAZYATTN_EHIP = 4           /* a HIP launch failed */
+} lazyattn_status;
+
+typedef enum { LAZYATTN_F32 = 0, LAZYATTN_BF16 = 1 } lazyattn_dtype;
+
+/* Positional encoding applied inside the kernels.  NONE is the rotation-free
+ * control; ALIBI adds -slope_h * (p - t) to the scaled score (gist.science,
+ * Key Contributions > Generalizability, names ALiBi among compatible
+ * encodings). */
+typedef enum { LAZYATTN_PE_ROPE = 0, LAZYATTN_PE_NONE = 1, LAZYATTN_PE_ALIBI = 2 } lazyattn_pe;
+
+typedef struct {
+  int32_t num_q_heads;    /* Hq >= 1 */
+  int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;       /* D: 128 for bf16; 64 or 128 for f32 */
+  int32_t block_size;     /* B: 16 */
+  int32_t dtype;          /* lazyattn_dtype: queries, pools and outputs share it */
+  int32_t pe;             /* lazyattn_pe */
+  double rope_theta;      /* RoPE base (> 0 when pe == ROPE) */
+  float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
+  int32_t reserved;       /* must be 0 */
+  const float* alibi_slopes;  /* device [Hq], or NULL => 2^(-8(h+1)/Hq) */
+} lazyattn_config;
+
+typedef struct {
+  int32_t num_reqs;                /* R >= 0 */
+  int32_t max_entries;             /* row stride of block_tables, >= every num_entries[r] */
+  const uint64_t* block_tables;    /* device [R][max_entries] packed words */
+  const int32_t* num_entries;      /* device [R] entries in use */
+  const int32_t* ctx_lens;         /* device [R] context length L_r, this call's new tokens included */
+} lazyattn_batch;
+
+/* ---- host-only helpers (no GPU needed) ---------------------------------- */
+
+/* Interface version; equals LAZYATTN_ABI_VERSION of the built library. */
+int32_t lazyattn_abi_version(void);
+
+/* Static string naming a status; never NULL. */
+const char* lazyattn_status_string(lazyattn_status s);
+
+/* Table word codec (gist.science, Technical Implementation > Decoding: block
+ * id and offset bit-packed in one register).  pack = (start << 32) | block. */
+uint64_t lazyattn_pack(uint32_t block_id, uint32_t logical_start);
+uint32_t lazyattn_entry_block(uint64_t word);
+uint32_t lazyattn_entry_start(uint64_t word);
+
+/* Pack n host entries: words[i] = lazyattn_pack(blocks[i], starts[i]).
+ * All pointers host; EINVAL if any is NULL with n > 0 or n < 0. */
+lazyattn_status lazyattn_pack_entries(const uint32_t* blocks, const uint32_t* starts, int64_t n,
+                                      uint64_t* words);
+
+/* Check host copies of a batch's tables against the dense contract above and
+ * against num_blocks.  On EINVAL, *bad_req and *bad_entry (host, may be NULL)
+ * name the first offending request and entry (entry -1: the request's
+ * num_entries/ctx_len themselves).  Reads host memory only. */
+lazyattn_status lazyattn_validate_tables(const lazyattn_config* cfg, const uint64_t* tables_h,
+                                         int32_t num_reqs, int32_t max_entries,
+                                         const int32_t* num_entries_h, const int32_t* ctx_lens_h,
+                                         int64_t num_blocks, int32_t* bad_req, int32_t* bad_entry);
+
+/* Number of key splits a call with num_splits == 0 would use. */
+int32_t lazyattn_prefill_splits(const lazyattn_config* cfg, int32_t num_reqs, int32_t max_q_len,
+                                int32_t max_entries);
+int32_t lazyattn_decode_splits(const lazyattn_config* cfg, int32_t num_reqs, int32_t max_entries);
+
+/* Workspace bytes for a prefill/decode call with these sizes (num_splits as
+ * passed to the call; 0 => the heuristic).  0 means no workspace needed.
+ * A call that splits the key range uses its workspace as 256 KiB of per-tile
+ * arrival counters followed by fp32 partial results; the last work-group of
+ * each tile to finish merges the partials inside the same kernel launch and
+ * resets its counter.  Hence: the workspace must be zero-filled before its
+ * first use (allocate it zeroed); every call that completes leaves the
+ * counters zero again, so the same buffer serves later calls of any size that
+ * fits; calls that may run concurrently must not share a workspace. */
+size_t lazyattn_prefill_workspace_size(const lazyattn_config* cfg, int32_t num_reqs, int32_t total_q,
+                                       int32_t max_q_len, int32_t max_entries, int32_t num_splits);
+size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_reqs,
+                                      int32_t max_entries, int32_t num_splits);
+
+/* ---- GPU entry points ---------------------------------------------------- */
+
+/* Causal prefill of each request's new tokens over its whole context
+ * (gist.science, Technical Implementation > Prefilling: the kernel loads KV
+ * blocks from the cache and applies one relative rotation per key tile).
+ *  q          device [total_q][Hq][D]; request r owns rows
+ *             cu_q_lens[r] .. cu_q_lens[r+1]-1 and its j-th row sits at
+ *             logical position ctx_lens[r] - q_len_r + j.  The new tokens'
+ *             K/V must already be in the pool (lazyattn_append_kv).
+ *  cu_q_lens  device [R+1] int32 prefix sums, cu_q_lens[0] = 0
+ *  total_q    host, = cu_q_lens[R]; max_q_len host, >= every q_len_r
+ *  k_pool, v_pool device pools of num_blocks blocks
+ *  batch      host struct holding device arrays
+ *  num_splits 0 => heuristic; else 1..64 splits of the key range
+ *  out        device [total_q][Hq][D]
+ *  workspace  device, >= lazyattn_prefill_workspace_size(...) bytes,
+ *             zero-filled before first use (may be NULL when that size is 0).
+ *  Exactly one kernel is launched.  EUNSUPPORTED when a split call would need
+ *  more than 65536 tiles (query tiles x requests x KV heads). */
+lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
+                                 int32_t total_q, int32_t max_q_len, const void* k_pool,
+                                 const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                 int32_t num_splits, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* One decode step (gist.science, Technical Implementation > Decoding): request
+ * r's single query q[r] sits at position ctx_lens[r]-1 and its own K/V is
+ * already in the pool.
+ *  q    device [R][Hq][D];  out device [R][Hq][D]
+ *  num_splits 0 => heuristic; else 1..256 splits of each request's entries
+ *  workspace as for prefill (>= lazyattn_decode_workspace_size bytes).
+ *  Exactly one kernel is launched.  bf16 supports G = Hq/Hkv <= 32. */
+lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                int32_t num_splits, void* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Write n new tokens' content-only K/V into the pool (gist.science,
+ * Methodology: the cache stores content-based keys and values, no rotation).
+ *  k_new, v_new device [n][Hkv][D]; slots device [n] int64 = block*B + row,
+ *  every slot < num_blocks*B (not checked on the device). */
+lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, void* v_pool,
+                                   int64_t num_blocks, const void* k_new, const void* v_new,
+                                   const int64_t* slots, int32_t n, hipStream_t stream);
+
+/* Decode every table entry on the device exactly as the attention kernels do
+ * and write (block id, logical start, valid length) as int32 triples to
+ * out [R][max_entries][3] (device); entries >= num_entries[r] get (-1,-1,-1). */
+lazyattn_status lazyattn_debug_decode_tables(const lazyattn_batch* batch, int32_t* out,
+                                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAZYATTN_H */

@@ -1,0 +1,221 @@
+"""ctypes binding of liblazyattn.so (argument marshalling only).
+
+Every computation happens in the library's HIP kernels; this module turns
+torch tensors into device pointers and the current HIP stream, and numpy
+arrays into host pointers.  If the built library is missing the import of
+any GPU entry point raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblazyattn.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+PE_ROPE, PE_NONE, PE_ALIBI = 0, 1, 2
+_PE = {"rope": PE_ROPE, "none": PE_NONE, "alibi": PE_ALIBI}
+_DT = {"f32": F32, "bf16": BF16}
+
+
+class LazyAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("pe", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("softmax_scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+        ("alibi_slopes", ctypes.c_void_p),
+    ]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [
+        ("num_reqs", ctypes.c_int32),
+        ("max_entries", ctypes.c_int32),
+        ("block_tables", ctypes.c_void_p),
+        ("num_entries", ctypes.c_void_p),
+        ("ctx_lens", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m position_agnostic_kv_pool_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, U32, U64, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                                      ctypes.c_uint64, ctypes.c_size_t)
+        CP, BP = ctypes.POINTER(Config), ctypes.POINTER(Batch)
+        sig = {
+            "lazyattn_abi_version": (I32, []),
+            "lazyattn_status_string": (ctypes.c_char_p, [I32]),
+            "lazyattn_pack": (U64, [U32, U32]),
+            "lazyattn_entry_block": (U32, [U64]),
+            "lazyattn_entry_start": (U32, [U64]),
+            "lazyattn_pack_entries": (I32, [P, P, I64, P]),
+            "lazyattn_validate_tables": (I32, [CP, P, I32, I32, P, P, I64, P, P]),
+            "lazyattn_prefill_splits": (I32, [CP, I32, I32, I32]),
+            "lazyattn_decode_splits": (I32, [CP, I32, I32]),
+            "lazyattn_prefill_workspace_size": (SZ, [CP, I32, I32, I32, I32, I32]),
+            "lazyattn_decode_workspace_size": (SZ, [CP, I32, I32, I32]),
+            "lazyattn_prefill": (I32, [CP, P, P, I32, I32, P, P, I64, BP, I32, P, P, SZ, P]),
+            "lazyattn_decode": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
+            "lazyattn_append_kv": (I32, [CP, P, P, I64, P, P, P, I32, P]),
+            "lazyattn_debug_decode_tables": (I32, [BP, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().lazyattn_status_string(int(s)).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise LazyAttnError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# host helpers
+# ---------------------------------------------------------------------------
+def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str = "bf16", pe: str = "rope",
+                rope_theta: float = 10000.0, softmax_scale: float = 0.0, alibi_slopes=None,
+                block_size: int = 16) -> Config:
+    c = Config()
+    c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size = num_q_heads, num_kv_heads, head_dim, block_size
+    c.dtype = _DT[dtype] if isinstance(dtype, str) else int(dtype)
+    c.pe = _PE[pe] if isinstance(pe, str) else int(pe)
+    c.rope_theta = float(rope_theta)
+    c.softmax_scale = float(softmax_scale)
+    c.reserved = 0
+    c.alibi_slopes = _ptr(alibi_slopes) if alibi_slopes is not None else None
+    c._keep = alibi_slopes
+    return c
+
+
+def pack_entries(blocks: np.ndarray, starts: np.ndarray) -> np.ndarray:
+    """Pack uint32 arrays (any shape) into uint64 words with the library's host codec."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint32)
+    s = np.ascontiguousarray(starts, dtype=np.uint32)
+    if b.shape != s.shape:
+        raise ValueError("blocks and starts differ in shape")
+    out = np.empty(b.shape, dtype=np.uint64)
+    _check(lib().lazyattn_pack_entries(b.ctypes.data, s.ctypes.data, b.size, out.ctypes.data), "pack_entries")
+    return out
+
+
+def validate_tables(cfg: Config, tables: np.ndarray, num_entries: np.ndarray, ctx_lens: np.ndarray,
+                    num_blocks: int):
+    """(status, bad_req, bad_entry) for host copies of a batch's tables."""
+    t = np.ascontiguousarray(tables, dtype=np.uint64)
+    ne = np.ascontiguousarray(num_entries, dtype=np.int32)
+    cl = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    br, be = ctypes.c_int32(0), ctypes.c_int32(0)
+    st = lib().lazyattn_validate_tables(ctypes.byref(cfg), t.ctypes.data, t.shape[0], t.shape[1] if t.ndim == 2 else 0,
+                                        ne.ctypes.data, cl.ctypes.data, int(num_blocks), ctypes.byref(br),
+                                        ctypes.byref(be))
+    return st, br.value, be.value
+
+
+def prefill_splits(cfg: Config, num_reqs: int, max_q_len: int, max_entries: int) -> int:
+    return lib().lazyattn_prefill_splits(ctypes.byref(cfg), num_reqs, max_q_len, max_entries)
+
+
+def decode_splits(cfg: Config, num_reqs: int, max_entries: int) -> int:
+    return lib().lazyattn_decode_splits(ctypes.byref(cfg), num_reqs, max_entries)
+
+
+def prefill_workspace_size(cfg: Config, num_reqs: int, total_q: int, max_q_len: int, max_entries: int,
+                           num_splits: int = 0) -> int:
+    return lib().lazyattn_prefill_workspace_size(ctypes.byref(cfg), num_reqs, total_q, max_q_len, max_entries,
+                                                 num_splits)
+
+
+def decode_workspace_size(cfg: Config, num_reqs: int, max_entries: int, num_splits: int = 0) -> int:
+    return lib().lazyattn_decode_workspace_size(ctypes.byref(cfg), num_reqs, max_entries, num_splits)
+
+
+# ---------------------------------------------------------------------------
+# GPU entry points (torch tensors in, device pointers out)
+# ---------------------------------------------------------------------------
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_batch(tables, num_entries, ctx_lens) -> Batch:
+    """Batch over device tensors: tables int64/uint64 [R][E] words, num_entries/ctx_lens int32 [R]."""
+    b = Batch()
+    b.num_reqs = int(num_entries.shape[0])
+    b.max_entries = int(tables.shape[1]) if tables.dim() == 2 else 0
+    b.block_tables = _ptr(tables)
+    b.num_entries = _ptr(num_entries)
+    b.ctx_lens = _ptr(ctx_lens)
+    b._keep = (tables, num_entries, ctx_lens)
+    return b
+
+
+def prefill(cfg: Config, q, cu_q_lens, total_q: int, max_q_len: int, k_pool, v_pool, num_blocks: int,
+            batch: Batch, out, workspace=None, num_splits: int = 0, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lazyattn_prefill(ctypes.byref(cfg), _ptr(q), _ptr(cu_q_lens), int(total_q), int(max_q_len),
+                                _ptr(k_pool), _ptr(v_pool), int(num_blocks), ctypes.byref(batch), int(num_splits),
+                                _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "lazyattn_prefill")
+
+
+def decode(cfg: Config, q, k_pool, v_pool, num_blocks: int, batch: Batch, out, workspace=None,
+           num_splits: int = 0, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lazyattn_decode(ctypes.byref(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), int(num_blocks),
+                               ctypes.byref(batch), int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
+                               _stream(stream))
+    _check(st, "lazyattn_decode")
+
+
+def append_kv(cfg: Config, k_pool, v_pool, num_blocks: int, k_new, v_new, slots, stream=None) -> None:
+    st = lib().lazyattn_append_kv(ctypes.byref(cfg), _ptr(k_pool), _ptr(v_pool), int(num_blocks), _ptr(k_new),
+                                  _ptr(v_new), _ptr(slots), int(slots.shape[0]), _stream(stream))
+    _check(st, "lazyattn_append_kv")
+
+
+def debug_decode_tables(batch: Batch, out, stream=None) -> None:
+    st = lib().lazyattn_debug_decode_tables(ctypes.byref(batch), _ptr(out), _stream(stream))
+    _check(st, "lazyattn_debug_decode_tables")

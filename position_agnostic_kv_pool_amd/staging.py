@@ -1,0 +1,120 @@
+"""Put a workload's host arrays into device memory in the library's layouts.
+
+Pure data movement: pools are allocated NaN-filled (so padding rows and
+never-written blocks poison any result that reads them) and the written
+blocks are scattered in; table words are packed with the library's own
+host codec.  No attention arithmetic happens here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _abi
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Host values (bf16 bit patterns or float32) -> device tensor of the matching dtype."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def config_for(spec, pe: str = None, softmax_scale: float = 0.0) -> _abi.Config:
+    return _abi.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype,
+                            pe or spec.pe, spec.rope_theta, softmax_scale, block_size=spec.block_size)
+
+
+class DevicePools:
+    """K pool [nb][Hkv][B][D] and V pool [nb][Hkv][D][B] on the device."""
+
+    def __init__(self, wl, device="cuda", block_permutation: np.ndarray = None):
+        kp, vp = wl.pools()
+        s = wl.spec
+        dt = torch_dtype(s.dtype)
+        nb = wl.num_blocks
+        self.num_blocks = nb
+        self.dtype = s.dtype
+        self.k = torch.full((nb, s.num_kv_heads, s.block_size, s.head_dim), float("nan"), dtype=dt, device=device)
+        self.v = torch.full((nb, s.num_kv_heads, s.head_dim, s.block_size), float("nan"), dtype=dt, device=device)
+        ids = kp.ids if block_permutation is None else block_permutation[kp.ids]
+        idx = torch.from_numpy(np.asarray(ids, dtype=np.int64)).to(device)
+        self.k[idx] = to_device(kp.data, s.dtype, device)
+        self.v[idx] = to_device(vp.data, s.dtype, device)
+
+
+class DeviceTables:
+    """Packed block tables plus per-request counts for one call."""
+
+    def __init__(self, table_blocks: np.ndarray, table_starts: np.ndarray, num_entries: np.ndarray,
+                 ctx_lens: np.ndarray, device="cuda", block_permutation: np.ndarray = None):
+        blocks = table_blocks if block_permutation is None else \
+            block_permutation[table_blocks.astype(np.int64)].astype(np.uint32)
+        self.words_host = _abi.pack_entries(blocks, table_starts)
+        self.tables = torch.from_numpy(self.words_host.view(np.int64)).to(device)
+        self.num_entries = torch.from_numpy(np.ascontiguousarray(num_entries, dtype=np.int32)).to(device)
+        self.ctx_lens = torch.from_numpy(np.ascontiguousarray(ctx_lens, dtype=np.int32)).to(device)
+        self.batch = _abi.make_batch(self.tables, self.num_entries, self.ctx_lens)
+
+    @classmethod
+    def from_inputs(cls, inputs: dict, device="cuda", block_permutation=None):
+        return cls(inputs["table_blocks"], inputs["table_starts"], inputs["num_entries"], inputs["ctx_lens"],
+                   device, block_permutation)
+
+
+def append_tokens(cfg, pools: DevicePools, inputs: dict, dtype: str, device="cuda", block_permutation=None):
+    """Write a batch of new tokens' K/V (inputs k_new, v_new, slots) into the pools."""
+    if inputs is None:
+        return
+    slots = inputs["slots"]
+    if block_permutation is not None:
+        slots = block_permutation[slots // 16] * 16 + slots % 16
+    k = to_device(inputs["k_new"], dtype, device)
+    v = to_device(inputs["v_new"], dtype, device)
+    sl = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(device)
+    _abi.append_kv(cfg, pools.k, pools.v, pools.num_blocks, k, v, sl)
+
+
+class PrefillCall:
+    """Device inputs and output/workspace buffers of one prefill call."""
+
+    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None):
+        self.cfg = cfg
+        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation)
+        self.q = to_device(inputs["q"], spec.dtype, device)
+        self.cu_q = torch.from_numpy(inputs["cu_q_lens"].astype(np.int32)).to(device)
+        self.total_q = int(inputs["total_q"])
+        self.max_q_len = int(inputs["max_q_len"])
+        self.out = torch.empty_like(self.q)
+        self.num_splits = num_splits
+        ws = _abi.prefill_workspace_size(cfg, len(inputs["ctx_lens"]), self.total_q, self.max_q_len,
+                                         self.tables.batch.max_entries, num_splits)
+        # zero-filled: the split-K arrival counters must start at zero
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=device) if ws > 0 else None
+
+    def run(self, pools: DevicePools, stream=None):
+        _abi.prefill(self.cfg, self.q, self.cu_q, self.total_q, self.max_q_len, pools.k, pools.v, pools.num_blocks,
+                     self.tables.batch, self.out, self.workspace, self.num_splits, stream)
+        return self.out
+
+
+class DecodeCall:
+    """Device inputs and output/workspace buffers of one decode step."""
+
+    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None):
+        self.cfg = cfg
+        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation)
+        self.q = to_device(inputs["q"], spec.dtype, device)
+        self.out = torch.empty_like(self.q)
+        self.num_splits = num_splits
+        ws = _abi.decode_workspace_size(cfg, self.q.shape[0], self.tables.batch.max_entries, num_splits)
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=device) if ws > 0 else None
+
+    def run(self, pools: DevicePools, stream=None):
+        _abi.decode(self.cfg, self.q, pools.k, pools.v, pools.num_blocks, self.tables.batch, self.out,
+                    self.workspace, self.num_splits, stream)
+        return self.out

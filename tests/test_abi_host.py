@@ -1,0 +1,194 @@
+"""The C interface on the host: exports, codec, validator, sizing and argument errors (CPU only).
+
+Only entry points that return before touching a GPU are called here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from position_agnostic_kv_pool_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lazyattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lazyattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 15
+    L = _abi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        getattr(L, n)          # resolves the symbol
+
+
+def test_version_and_status_strings():
+    assert _abi.lib().lazyattn_abi_version() == 1
+    for s in range(5):
+        assert len(_abi.status_string(s)) > 0
+    assert _abi.status_string(99) == "unknown status"
+
+
+def test_codec_matches_oracle_bit_exact():
+    L = _abi.lib()
+    rng = np.random.default_rng(0)
+    b = np.concatenate([[0, 0xFFFFFFFF, 1, 0], rng.integers(0, 2**32, 5000)]).astype(np.uint32)
+    s = np.concatenate([[0, 0xFFFFFFFF, 0, 1], rng.integers(0, 2**32, 5000)]).astype(np.uint32)
+    lib_words = _abi.pack_entries(b, s)
+    orc_words = O.pack_table(b, s)
+    assert np.array_equal(lib_words, orc_words)
+    for i in range(0, b.size, 251):
+        w = int(lib_words[i])
+        assert L.lazyattn_pack(int(b[i]), int(s[i])) == w
+        assert (L.lazyattn_entry_block(w), L.lazyattn_entry_start(w)) == O.unpack_entry(w)
+
+
+def _cfg(**kw):
+    d = dict(num_q_heads=4, num_kv_heads=2, head_dim=128, dtype="bf16", pe="rope", rope_theta=10000.0)
+    d.update(kw)
+    return _abi.make_config(**d)
+
+
+def _tables(rows):
+    """rows: list of lists of (block, start)."""
+    E = max(len(r) for r in rows)
+    t = np.zeros((len(rows), E), dtype=np.uint64)
+    for i, r in enumerate(rows):
+        for e, (b, s) in enumerate(r):
+            t[i, e] = O.pack_entry(b, s)
+    return t
+
+
+def test_validator_accepts_dense_tables():
+    t = _tables([[(3, 0), (1, 16), (2, 20)], [(0, 0)]])
+    st, br, be = _abi.validate_tables(_cfg(), t, [3, 1], [30, 5], 4)
+    assert (st, br, be) == (_abi.OK, -1, -1)
+
+
+@pytest.mark.parametrize("case,want", [
+    ("start0", (1, 0)), ("too_long", (1, 1)), ("empty_entry", (1, 1)), ("block_oob", (1, 1)),
+    ("descending", (1, 1)), ("ctx_short", (1, 2)), ("count_too_big", (1, -1)), ("empty_with_ctx", (1, -1)),
+])
+def test_validator_rejects_with_location(case, want):
+    good = [(0, 0), (1, 16), (2, 20)]
+    L, n = 30, 3
+    if case == "start0":
+        good[0] = (0, 1)
+    elif case == "too_long":
+        good[2] = (2, 33); L = 50
+    elif case == "empty_entry":
+        good[2] = (2, 16)
+    elif case == "block_oob":
+        good[1] = (10, 16)
+    elif case == "descending":
+        good[2] = (2, 10)
+    elif case == "ctx_short":
+        L = 20
+    elif case == "count_too_big":
+        n = 4
+    elif case == "empty_with_ctx":
+        n = 0
+    t = _tables([[(0, 0)], good])
+    st, br, be = _abi.validate_tables(_cfg(), t, [1, n], [5, L], 10)
+    assert st == _abi.EINVAL
+    assert (br, be) == want
+    # the oracle's decoder agrees that the table is malformed
+    if n <= 3 and n > 0:
+        with pytest.raises(O.TableError):
+            O.decode_table([int(w) for w in t[1]], n, L, 16, 10)
+
+
+def test_validator_on_generated_workloads():
+    import workloads as W
+    for cfg_id in (1, 2, 5):
+        wl = W.build_workload(W.spec(cfg_id))
+        pb = wl.prefill_batch()
+        words = _abi.pack_entries(pb["table_blocks"], pb["table_starts"])
+        cfg = _abi.make_config(wl.spec.num_q_heads, wl.spec.num_kv_heads, wl.spec.head_dim, wl.spec.dtype)
+        st, _, _ = _abi.validate_tables(cfg, words, pb["num_entries"], pb["ctx_lens"], wl.num_blocks)
+        assert st == _abi.OK
+
+
+def test_config_errors():
+    C = _cfg
+    lib = _abi.lib()
+    check = lambda c: lib.lazyattn_validate_tables(ctypes.byref(c), None, 0, 0, None, None, 0, None, None)
+    assert check(C()) == _abi.OK
+    assert check(C(num_q_heads=6, num_kv_heads=4)) == _abi.EINVAL
+    assert check(C(num_kv_heads=0)) == _abi.EINVAL
+    assert check(C(head_dim=64)) == _abi.EUNSUPPORTED            # bf16 kernels are built for D = 128
+    assert check(C(head_dim=64, dtype="f32")) == _abi.OK
+    assert check(C(block_size=32)) == _abi.EUNSUPPORTED
+    assert check(C(rope_theta=0.0)) == _abi.EINVAL
+    assert check(C(rope_theta=0.0, pe="none")) == _abi.OK
+    c = C(); c.reserved = 1
+    assert check(c) == _abi.EINVAL
+    c = C(); c.dtype = 7
+    assert check(c) == _abi.EINVAL
+    c = C(); c.pe = 9
+    assert check(c) == _abi.EINVAL
+    assert check(C(softmax_scale=-1.0)) == _abi.EINVAL
+
+
+def test_split_heuristics_and_workspace_sizes():
+    c = _cfg(num_q_heads=32, num_kv_heads=8)
+    # 16 requests x 8 KV heads of one 64-position tile -> too few work-groups: split the keys
+    s = _abi.prefill_splits(c, 16, 64, 260)
+    assert s == 2
+    counters = 65536 * 4
+    assert _abi.prefill_workspace_size(c, 16, 1024, 64, 260) == counters + s * 1024 * 32 * 130 * 4
+    assert _abi.prefill_workspace_size(c, 16, 1024, 64, 260, 1) == 0
+    # 128 requests x 8 KV heads is plenty for decode
+    assert _abi.decode_splits(c, 128, 274) == 1
+    assert _abi.decode_workspace_size(c, 128, 274) == 0
+    c70 = _cfg(num_q_heads=64, num_kv_heads=8)
+    s = _abi.decode_splits(c70, 4, 2184)
+    assert s >= 16
+    assert _abi.decode_workspace_size(c70, 4, 2184) == counters + s * 4 * 64 * 130 * 4
+    assert _abi.decode_workspace_size(_cfg(dtype="f32", head_dim=64), 4, 100, 8) == 0
+
+
+def test_gpu_entry_points_reject_bad_arguments_before_launch():
+    lib = _abi.lib()
+    c = _cfg()
+    b = _abi.Batch()
+    b.num_reqs, b.max_entries = 2, 4
+    b.block_tables = b.num_entries = b.ctx_lens = 16   # never dereferenced on the host
+    P = ctypes.c_void_p(64)
+    # null config / batch
+    assert lib.lazyattn_prefill(None, P, P, 1, 1, P, P, 1, ctypes.byref(b), 0, P, None, 0, None) == _abi.EINVAL
+    assert lib.lazyattn_decode(ctypes.byref(c), P, P, P, 1, None, 0, P, None, 0, None) == _abi.EINVAL
+    # null data pointers
+    assert lib.lazyattn_prefill(ctypes.byref(c), None, P, 1, 1, P, P, 1, ctypes.byref(b), 0, P, None, 0, None) == _abi.EINVAL
+    assert lib.lazyattn_decode(ctypes.byref(c), P, None, P, 1, ctypes.byref(b), 0, P, None, 0, None) == _abi.EINVAL
+    assert lib.lazyattn_append_kv(ctypes.byref(c), P, P, 1, P, None, P, 3, None) == _abi.EINVAL
+    # out-of-range sizes
+    assert lib.lazyattn_prefill(ctypes.byref(c), P, P, -1, 1, P, P, 1, ctypes.byref(b), 0, P, None, 0, None) == _abi.EINVAL
+    assert lib.lazyattn_prefill(ctypes.byref(c), P, P, 1, 1, P, P, 1, ctypes.byref(b), 65, P, None, 0, None) == _abi.EINVAL
+    assert lib.lazyattn_decode(ctypes.byref(c), P, P, P, 1, ctypes.byref(b), 257, P, None, 0, None) == _abi.EINVAL
+    assert lib.lazyattn_prefill(ctypes.byref(c), P, P, 1, 1, P, P, 0, ctypes.byref(b), 0, P, None, 0, None) == _abi.EINVAL
+    # unsupported shapes
+    c33 = _cfg(num_q_heads=66, num_kv_heads=2)
+    assert lib.lazyattn_decode(ctypes.byref(c33), P, P, P, 1, ctypes.byref(b), 0, P, None, 0, None) == _abi.EUNSUPPORTED
+    # a split call without its workspace
+    assert lib.lazyattn_decode(ctypes.byref(c), P, P, P, 1, ctypes.byref(b), 8, P, None, 0, None) == _abi.EWORKSPACE
+    assert lib.lazyattn_prefill(ctypes.byref(c), P, P, 1, 1, P, P, 1, ctypes.byref(b), 4, P, P, 16, None) == _abi.EWORKSPACE
+    # malformed batch
+    b2 = _abi.Batch()
+    b2.num_reqs, b2.max_entries = 1, 0
+    assert lib.lazyattn_decode(ctypes.byref(c), P, P, P, 1, ctypes.byref(b2), 0, P, None, 0, None) == _abi.EINVAL
+    assert lib.lazyattn_debug_decode_tables(ctypes.byref(b2), P, None) == _abi.EINVAL
+    # empty work is a no-op that succeeds without a launch
+    b0 = _abi.Batch()
+    assert lib.lazyattn_decode(ctypes.byref(c), None, None, None, 0, ctypes.byref(b0), 0, None, None, 0, None) == _abi.OK
+    assert lib.lazyattn_prefill(ctypes.byref(c), None, None, 0, 0, None, None, 0, ctypes.byref(b), 0, None, None, 0, None) == _abi.OK
+    assert lib.lazyattn_append_kv(ctypes.byref(c), None, None, 0, None, None, None, 0, None) == _abi.OK

@@ -1,0 +1,419 @@
+"""Parity of the HIP path (through the C interface) with the fp64 oracle, on an MI355X.
+
+Every case prints its name before touching the GPU so that a failure is
+attributable.  Sizes: the tiny fp32 case in full; the Llama-3.1-8B prefill
+case in full; the other cases at their real shapes with requests or query
+tokens sampled where the oracle would take minutes.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import workloads as W  # noqa: E402
+from position_agnostic_kv_pool_amd import _abi, staging  # noqa: E402
+from _helpers import OracleState, assert_parity, diff_stats, gpu_f64, within  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    _abi.lib()  # raises if the library was not built
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# helpers running one phase on both sides
+# ---------------------------------------------------------------------------
+def run_prefill(wl, num_splits=0, pe=None, block_permutation=None, pools=None):
+    s = wl.spec
+    cfg = staging.config_for(s, pe=pe)
+    pb = wl.prefill_batch()
+    if pools is None:
+        pools = staging.DevicePools(wl, DEV, block_permutation)
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV, block_permutation)
+    call = staging.PrefillCall(cfg, s, pb, DEV, num_splits, block_permutation)
+    out = call.run(pools)
+    sync()
+    return pb, gpu_f64(out), pools
+
+
+def sample_tokens(q_len, k, rng):
+    if q_len <= k:
+        return np.arange(q_len)
+    pick = set([0, q_len - 1]) | set(rng.choice(q_len, k - 2, replace=False).tolist())
+    return np.array(sorted(pick))
+
+
+def compare_prefill(wl, pb, got, orc, requests=None, token_subset=None, pe=None, label=""):
+    ref = orc.prefill(pb, token_subset=token_subset, requests=requests, pe=pe)
+    cu = pb["cu_q_lens"]
+    gs, rs = [], []
+    for r, o in ref.items():
+        local = np.arange(cu[r + 1] - cu[r]) if token_subset is None else np.asarray(token_subset[r])
+        gs.append(got[cu[r] + local])
+        rs.append(o)
+    g, rr = np.concatenate(gs), np.concatenate(rs)
+    mx, mn = assert_parity(g, rr, wl.spec.dtype, label)
+    say(f"{label}: max {mx:.2e} mean {mn:.2e} over {g.shape[0]} tokens")
+    return g, rr
+
+
+# ---------------------------------------------------------------------------
+# metadata and append: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg_id,kw", [(1, {}), (2, {}), (4, {"requests": [2]}), (5, {"skew": 1.2})])
+def test_debug_decode_tables_bit_exact(cfg_id, kw):
+    say("debug-decode", cfg_id, kw)
+    wl = W.build_workload(W.spec(cfg_id, **kw))
+    inputs = wl.prefill_batch() or wl.decode_step(0)
+    dt = staging.DeviceTables.from_inputs(inputs, DEV)
+    E = dt.batch.max_entries
+    out = torch.empty((len(inputs["ctx_lens"]), E, 3), dtype=torch.int32, device=DEV)
+    _abi.debug_decode_tables(dt.batch, out)
+    sync()
+    got = out.cpu().numpy()
+    words = O.pack_table(inputs["table_blocks"], inputs["table_starts"])
+    for r in range(len(inputs["ctx_lens"])):
+        n = int(inputs["num_entries"][r])
+        b, s, l = O.decode_table(words[r], n, int(inputs["ctx_lens"][r]), 16, wl.num_blocks)
+        assert np.array_equal(got[r, :n, 0], b)
+        assert np.array_equal(got[r, :n, 1], s)
+        assert np.array_equal(got[r, :n, 2], l)
+        assert np.array_equal(got[r, :n, 0], inputs["table_blocks"][r, :n].astype(np.int64))
+        assert np.all(got[r, n:] == -1)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 5])
+def test_append_kv_bit_exact(cfg_id):
+    say("append", cfg_id)
+    wl = W.build_workload(W.spec(cfg_id, requests=[4, 4]) if cfg_id == 5 else W.spec(cfg_id))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    k_before = pools.k.clone()
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    sync()
+    orc = OracleState(wl)
+    orc.append(pb)
+    blocks = np.unique(pb["slots"] // 16)
+    view = np.int16 if s.dtype == "bf16" else np.float32
+    gk = pools.k[torch.from_numpy(blocks).to(DEV)].cpu().view(torch.int16 if s.dtype == "bf16" else torch.float32).numpy()
+    gv = pools.v[torch.from_numpy(blocks).to(DEV)].cpu().view(torch.int16 if s.dtype == "bf16" else torch.float32).numpy()
+    ok_k = orc.k[blocks].view(view)
+    ok_v = orc.v[blocks].view(view)
+    # compare bit patterns (NaN padding included)
+    assert np.array_equal(gk.view(np.uint8), np.ascontiguousarray(ok_k).view(np.uint8))
+    assert np.array_equal(gv.view(np.uint8), np.ascontiguousarray(ok_v).view(np.uint8))
+    # nothing else in the pool moved
+    mask = torch.ones(wl.num_blocks, dtype=torch.bool, device=DEV)
+    mask[torch.from_numpy(blocks).to(DEV)] = False
+    a = pools.k[mask].view(torch.int16 if s.dtype == "bf16" else torch.int32)
+    b = k_before[mask].view(torch.int16 if s.dtype == "bf16" else torch.int32)
+    assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# parity on the five configurations
+# ---------------------------------------------------------------------------
+def test_parity_tiny_f32_prefill_and_decode():
+    say("tiny fp32: prefill + 8 decode steps")
+    wl = W.build_workload(W.spec(1))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb, got, pools = run_prefill(wl)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="tiny prefill")
+    for step in range(8):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+        out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+        ref = orc.decode(d)
+        mx, mn = assert_parity(out, np.stack([ref[r] for r in range(len(ref))]), "f32", f"tiny decode {step}")
+    say(f"tiny decode last step: max {mx:.2e}")
+
+
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_parity_llama8b_prefill_full(num_splits):
+    say("8B prefill full, splits", num_splits)
+    wl = W.build_workload(W.spec(2))
+    pb, got, _ = run_prefill(wl, num_splits=num_splits)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label=f"8B prefill splits={num_splits}")
+
+
+def test_parity_llama8b_decode():
+    say("8B decode: 16 requests, suffix prefill then steps 0, 1, 15, 16, 40")
+    wl = W.build_workload(W.spec(3, requests=[16], n_decode=41))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb, got, pools = run_prefill(wl)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="8B suffix prefill")
+    for step in range(41):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+        if step in (0, 1, 15, 16, 40):
+            out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+            ref = orc.decode(d)
+            mx, mn = assert_parity(out, np.stack([ref[r] for r in range(len(ref))]), "bf16", f"8B decode {step}")
+            say(f"8B decode step {step}: max {mx:.2e} mean {mn:.2e}")
+
+
+def test_parity_llama70b_long_context():
+    say("70B 32k: one request, 2048-token chunk (sampled rows), decode steps 0 and 127 with split-K")
+    wl = W.build_workload(W.spec(4, requests=[1], n_decode=128))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb, got, pools = run_prefill(wl)
+    orc = OracleState(wl)
+    orc.append(pb)
+    rng = np.random.default_rng(0)
+    toks = sorted(set([0, 1, 31, 32, 33, 1023, 1024, 2046, 2047]) | set(rng.choice(2048, 12, replace=False).tolist()))
+    compare_prefill(wl, pb, got, orc, token_subset={0: toks}, label="70B chunk prefill")
+    hist = wl.tokens_before_step(127)
+    # decode step 0 first, then jump to step 127
+    d0 = wl.decode_step(0)
+    staging.append_tokens(cfg, pools, d0, s.dtype, DEV)
+    orc.append(d0)
+    for splits in (0, 1, 7, 64):
+        out = gpu_f64(staging.DecodeCall(cfg, s, d0, DEV, num_splits=splits).run(pools))
+        ref = orc.decode(d0)
+        mx, mn = assert_parity(out, ref[0][None], "bf16", f"70B decode step 0 splits={splits}")
+        say(f"70B decode step 0 splits={splits}: max {mx:.2e} mean {mn:.2e}")
+    rest = {k: v[pb["slots"].size + 1:] for k, v in hist.items()}
+    staging.append_tokens(cfg, pools, rest, s.dtype, DEV)
+    orc.append(rest)
+    d = wl.decode_step(127)
+    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+    orc.append(d)
+    out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+    ref = orc.decode(d)
+    mx, mn = assert_parity(out, ref[0][None], "bf16", "70B decode step 127")
+    say(f"70B decode step 127: max {mx:.2e} mean {mn:.2e}")
+
+
+@pytest.mark.parametrize("skew", W.CFG5_SKEWS)
+@pytest.mark.parametrize("pe", W.CFG5_PES)
+def test_parity_mqa_stress(skew, pe):
+    say(f"MQA stress skew={skew} pe={pe}: 32 prefill requests (sampled rows), 96 decode requests steps 0..7")
+    wl = W.build_workload(W.spec(5, skew=skew, pe=pe))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb, got, pools = run_prefill(wl)
+    orc = OracleState(wl)
+    orc.append(pb)
+    rng = np.random.default_rng(1)
+    subset = {r: sample_tokens(128, 10, rng) for r in range(len(pb["ctx_lens"]))}
+    compare_prefill(wl, pb, got, orc, token_subset=subset, label=f"MQA prefill {skew}/{pe}")
+    for step in range(8):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+        if step in (0, 7):
+            out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+            reqs = list(range(0, len(d["ctx_lens"]), 4))      # every 4th of the 96 for the oracle
+            ref = orc.decode(d, requests=reqs)
+            mx, mn = assert_parity(out[reqs], np.stack([ref[r] for r in reqs]), "bf16",
+                                   f"MQA decode {skew}/{pe} step {step}")
+            say(f"MQA decode step {step}: max {mx:.2e} mean {mn:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# invariances the method relies on
+# ---------------------------------------------------------------------------
+def test_physical_relocation_is_bit_identical():
+    say("relocation: same logical inputs, permuted physical blocks")
+    wl = W.build_workload(W.spec(2, requests=[4]))
+    perm = np.random.default_rng(5).permutation(wl.num_blocks).astype(np.int64)
+    _, a, _ = run_prefill(wl)
+    _, b, _ = run_prefill(wl, block_permutation=perm)
+    assert np.array_equal(a, b)
+
+
+def test_pool_is_read_only_and_padding_poison_stays_out():
+    say("pools unchanged by prefill and decode; outputs finite despite NaN padding")
+    wl = W.build_workload(W.spec(5, requests=[6, 6], skew=1.6))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    d = wl.decode_step(0)
+    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+    k0, v0 = pools.k.view(torch.int16).clone(), pools.v.view(torch.int16).clone()
+    o1 = staging.PrefillCall(cfg, s, pb, DEV).run(pools)
+    o2 = staging.DecodeCall(cfg, s, d, DEV).run(pools)
+    sync()
+    assert torch.equal(pools.k.view(torch.int16), k0) and torch.equal(pools.v.view(torch.int16), v0)
+    assert torch.isfinite(o1.float()).all() and torch.isfinite(o2.float()).all()
+
+
+def test_decode_split_count_invariance():
+    say("decode split counts 1..37 agree")
+    wl = W.build_workload(W.spec(4, requests=[2], n_decode=1))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, DEV)
+    d = wl.decode_step(0)
+    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+    outs = [gpu_f64(staging.DecodeCall(cfg, s, d, DEV, num_splits=k).run(pools)) for k in (1, 2, 5, 37, 256)]
+    for o in outs[1:]:
+        mx, mn = diff_stats(o, outs[0])
+        assert mx <= 4e-3 and mn <= 2e-4
+
+
+def test_decode_matches_last_prefill_row():
+    say("decode == last row of prefill over the same context")
+    wl = W.build_workload(W.spec(3, requests=[8], n_decode=0, q_len=17))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb, got, pools = run_prefill(wl)
+    # decode inputs built from the prefill batch: the last query row of each request
+    cu = pb["cu_q_lens"]
+    d = dict(pb)
+    d["q"] = pb["q"][cu[1:] - 1]
+    out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+    mx, mn = diff_stats(out, got[cu[1:] - 1])
+    assert mx <= 1e-2 and mn <= 1e-3
+
+
+def test_prefill_split_count_invariance_and_empty_splits():
+    say("prefill split counts 1..64 (many splits are empty) agree")
+    wl = W.build_workload(W.spec(2, requests=[2], docs=(1, 1)))
+    outs = [run_prefill(wl, num_splits=k)[1] for k in (1, 3, 64)]
+    for o in outs[1:]:
+        mx, mn = diff_stats(o, outs[0])
+        assert mx <= 4e-3 and mn <= 2e-4
+
+
+# ---------------------------------------------------------------------------
+# rotation-free and ALiBi instantiations on the same inputs
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("pe", ["none", "alibi"])
+def test_other_encodings_llama8b_prefill(pe):
+    say("8B prefill with pe", pe)
+    wl = W.build_workload(W.spec(2, requests=[4]))
+    pb, got, _ = run_prefill(wl, pe=pe)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, pe=pe, label=f"8B prefill pe={pe}")
+
+
+# ---------------------------------------------------------------------------
+# negative controls: planted mistakes in the oracle must fail the bar
+# ---------------------------------------------------------------------------
+def test_negative_controls_fail_the_tolerance():
+    say("negative controls (oracle with planted mistakes vs the GPU output)")
+    wl = W.build_workload(W.spec(2, requests=[2]))
+    pb, got, _ = run_prefill(wl)
+    orc = OracleState(wl)
+    orc.append(pb)
+    cu = pb["cu_q_lens"]
+    good = orc.prefill(pb)
+    g = np.concatenate([got[cu[r]:cu[r + 1]] for r in good])
+    assert within(g, np.concatenate(list(good.values())), "bf16")
+    D = wl.spec.head_dim
+    half = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])
+    for name, bad in (("off by one", orc.prefill(pb, q_shift=1)),
+                      ("rotation off", orc.prefill(pb, pe="none")),
+                      ("half-split pairs", orc.prefill(pb, pair_perm=half))):
+        b = np.concatenate(list(bad.values()))
+        mx, mn = diff_stats(g, b)
+        say(f"control {name}: max {mx:.2e} mean {mn:.2e}")
+        assert not within(g, b, "bf16"), name
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_edge_single_token_contexts_and_zero_length_queries():
+    say("edge: requests without documents (context = the query itself) and zero-length query rows")
+    wl = W.build_workload(W.spec(2, requests=[3], docs=(0, 0), q_len=1))
+    pb, got, _ = run_prefill(wl)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="single-token contexts")
+    # add a request with no new tokens in the middle of the batch
+    wl2 = W.build_workload(W.spec(2, requests=[3], q_len=5))
+    s = wl2.spec
+    cfg = staging.config_for(s)
+    pb2 = wl2.prefill_batch()
+    pools = staging.DevicePools(wl2, DEV)
+    staging.append_tokens(cfg, pools, pb2, s.dtype, DEV)
+    orc2 = OracleState(wl2)
+    orc2.append(pb2)
+    ref = orc2.prefill(pb2)
+    ins = dict(pb2)
+    # request 1 contributes nothing this call: its context ends before its new tokens
+    ins["cu_q_lens"] = np.array([0, 5, 5, 10], dtype=np.int32)
+    ins["q"] = np.concatenate([pb2["q"][0:5], pb2["q"][10:15]])
+    ins["total_q"] = 10
+    ctx = pb2["ctx_lens"].copy()
+    ctx[1] -= 5
+    ins["ctx_lens"] = ctx
+    ne = pb2["num_entries"].copy()
+    ne[1] = wl2.requests[1].n_doc_entries
+    ins["num_entries"] = ne
+    out = gpu_f64(staging.PrefillCall(cfg, s, ins, DEV).run(pools))
+    assert_parity(out[0:5], ref[0], "bf16", "zero-length row: request 0")
+    assert_parity(out[5:10], ref[2], "bf16", "zero-length row: request 2")
+
+
+def test_split_workspace_reuse_across_calls_of_different_sizes():
+    say("one zero-filled workspace reused by split prefill and decode calls of different sizes")
+    wl = W.build_workload(W.spec(4, requests=[2], n_decode=1, q_len=100))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    d = wl.decode_step(0)
+    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+    orc = OracleState(wl)
+    orc.append(pb)
+    ref_p = orc.prefill(pb, token_subset={0: [0, 99], 1: [0, 50, 99]})
+    orc.append(d)
+    ref_d = orc.decode(d)
+    big = max([_abi.prefill_workspace_size(cfg, 2, pb["total_q"], pb["max_q_len"], pb["table_blocks"].shape[1], k)
+               for k in (9, 3, 17)] + [_abi.decode_workspace_size(cfg, 2, d["table_blocks"].shape[1], k)
+                                       for k in (50, 4)])
+    ws = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    pc = staging.PrefillCall(cfg, s, pb, DEV)
+    dc = staging.DecodeCall(cfg, s, d, DEV)
+    for rep in range(2):
+        for k in (9, 3, 17):
+            _abi.prefill(cfg, pc.q, pc.cu_q, pc.total_q, pc.max_q_len, pools.k, pools.v, pools.num_blocks,
+                         pc.tables.batch, pc.out, ws, k)
+            got = gpu_f64(pc.out)
+            for r, toks in ((0, [0, 99]), (1, [0, 50, 99])):
+                assert_parity(got[pb["cu_q_lens"][r] + np.array(toks)], ref_p[r], "bf16", f"prefill splits {k}")
+            for kd in (50, 4):
+                _abi.decode(cfg, dc.q, pools.k, pools.v, pools.num_blocks, dc.tables.batch, dc.out, ws, kd)
+                out = gpu_f64(dc.out)
+                assert_parity(out, np.stack([ref_d[0], ref_d[1]]), "bf16", f"decode splits {kd}")
+    sync()
+    assert int(ws[:65536 * 4].view(torch.int32).abs().sum().item()) == 0   # counters left at zero

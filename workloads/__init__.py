@@ -8,6 +8,8 @@ binding, and is shared by both sides of every parity test.
 """
 from .synth import (  # noqa: F401
     CONFIGS,
+    CFG5_PES,
+    CFG5_SKEWS,
     WorkloadSpec,
     Workload,
     RequestLayout,
