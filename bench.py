@@ -58,12 +58,11 @@ def read_counter_summary(path: str):
     if kv.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     try:
-        fetch = float(kv["fetch_kib_per_dispatch"])
-        write = float(kv["write_kib_per_dispatch"])
-        scale = float(kv["copy_scale"])
+        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])
     except (KeyError, ValueError):
         return None
-    return (fetch + write) * 1024.0 * scale
+    return round((fetch + write) * 1024.0)
 
 
 # ---------------------------------------------------------------------------
