@@ -144,6 +144,22 @@ class Timer:
         t.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    def steps(self, attend, merge, n):
+        """n steps of [attention kernel, merge kernel]: (ms per step, ms per attention launch)."""
+        t = self.torch
+        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
+        end = t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        self.busy()
+        for a, b in ev:
+            a.record()
+            attend()
+            b.record()
+            merge()
+        end.record()
+        t.cuda.synchronize()
+        return ev[0][0].elapsed_time(end) / n, sum(a.elapsed_time(b) for a, b in ev) / n
+
 
 def bench_prefill(torch, args, W, staging, _abi):
     wl = W.build_workload(W.spec(2))
@@ -159,19 +175,25 @@ def bench_prefill(torch, args, W, staging, _abi):
     timer = Timer(torch)
     for _ in range(args.warmup):
         call.run(pools)
+    # the step (attention kernel, then the split merge), and the attention kernel alone, each timed
+    # over back-to-back launches between two events
     ms = timer.span(lambda: call.run(pools), args.steps)
+    ms_attend = timer.span(lambda: call.attend(pools), args.steps)
     for _ in range(args.warmup):
         call_none.run(pools)
     ms_none = timer.span(lambda: call_none.run(pools), args.steps)
-    ms_rope2 = timer.span(lambda: call.run(pools), args.steps)      # rope again, after the control
+    ms_none_attend = timer.span(lambda: call_none.attend(pools), args.steps)
+    ms_rope2 = timer.span(lambda: call.run(pools), args.steps)          # again, after the control
+    ms_rope2_attend = timer.span(lambda: call.attend(pools), args.steps)
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
-    splits = _abi.prefill_splits(cfg, len(pb["ctx_lens"]), pb["max_q_len"], pb["table_blocks"].shape[1])
-    return dict(wl=wl, pb=pb, ms=ms, ms_none=ms_none, ms_rope2=ms_rope2, flops=flops, splits=splits,
-                pools=pools)
+    return dict(wl=wl, pb=pb, ms=ms, ms_attend=ms_attend, ms_none=ms_none, ms_none_attend=ms_none_attend,
+                ms_rope2=ms_rope2, ms_rope2_attend=ms_rope2_attend, flops=flops, splits=call.splits, pools=pools)
 
 
 def bench_decode(torch, args, W, staging, _abi, n_steps: int):
-    """Decode steps 0..n_steps-1 of the 8B decode shape; events around each decode launch only."""
+    """Decode steps 0..n_steps-1 of the 8B decode shape.  Each step's new token is appended
+    untimed; then 3 back-to-back launches of its attention kernel are timed (they re-read the same
+    step's pool, as the step itself would), with and without the merge, and rotation-free."""
     wl = W.build_workload(W.spec(3, n_decode=max(n_steps, 1)))
     s = wl.spec
     cfg = staging.config_for(s)
@@ -179,32 +201,29 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int):
     pools = staging.DevicePools(wl, "cuda")
     staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, "cuda")
     t = torch
-    tot_ms, tot_ms_none, tot_bytes, tot_unique, tokens = 0.0, 0.0, 0, 0, 0
+    tot_ms, tot_merge_ms, tot_ms_none, tot_bytes, tot_unique, tokens = 0.0, 0.0, 0.0, 0, 0, 0
     for step in range(-2, n_steps):          # two untimed warm-up launches on step 0's inputs
         d = wl.decode_step(max(step, 0))
         if step >= 0:
             staging.append_tokens(cfg, pools, d, s.dtype, "cuda")
         call = staging.DecodeCall(cfg, s, d, "cuda")
         call_none = staging.DecodeCall(cfg_none, s, d, "cuda")
-        t.cuda.synchronize()
-        a, b, c = (t.cuda.Event(enable_timing=True) for _ in range(3))
-        Timer(t).busy()
-        a.record()
-        call.run(pools)
-        b.record()
-        call_none.run(pools)
-        c.record()
-        t.cuda.synchronize()
+        timer = Timer(t)
+        ms_att = timer.span(lambda: call.attend(pools), 3)
+        ms_step = timer.span(lambda: call.run(pools), 3)
+        ms_none = timer.span(lambda: call_none.attend(pools), 3)
         if step < 0:
             continue
-        tot_ms += a.elapsed_time(b)
-        tot_ms_none += b.elapsed_time(c)
+        tot_ms += ms_att
+        tot_merge_ms += max(ms_step - ms_att, 0.0)
+        tot_ms_none += ms_none
         by = decode_bytes(d, wl)
         tot_bytes += by["logical"]
         tot_unique += by["unique"]
         tokens += len(d["ctx_lens"])
     n = max(n_steps, 1)
-    return dict(ms=tot_ms / n, ms_none=tot_ms_none / n, bytes=tot_bytes / n, unique=tot_unique / n,
+    return dict(ms=tot_ms / n, merge_ms=tot_merge_ms / n, ms_none=tot_ms_none / n, bytes=tot_bytes / n,
+                unique=tot_unique / n,
                 tokens=tokens, splits=_abi.decode_splits(cfg, len(wl.requests), wl.table_arrays(wl.requests)[0].shape[1]))
 
 
@@ -288,16 +307,21 @@ def main() -> int:
         return 0
 
     pre = bench_prefill(torch, args, W, staging, _abi)
-    print(f"# prefill done: {pre['ms'] * 1e3:.1f} us/launch", file=sys.stderr, flush=True)
+    print(f"# prefill done: {pre['ms'] * 1e3:.1f} us/step, attention kernel {pre['ms_attend'] * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
     tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+    kernel_tflops = pre["flops"] / (pre["ms_attend"] * 1e-3) / 1e12
     traffic = read_counter_summary(PREFILL_COUNTERS)
-    roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+    roofline = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "prefill_bf16_kernel<ROPE>", "flops_per_launch": pre["flops"],
-                "avg_launch_us": round(pre["ms"] * 1e3, 2)}
-    rope_overhead = {"prefill_rope_us": round(pre["ms"] * 1e3, 2), "prefill_rope_repeat_us": round(pre["ms_rope2"] * 1e3, 2),
-                     "prefill_norotation_us": round(pre["ms_none"] * 1e3, 2),
-                     "prefill_overhead": round(min(pre["ms"], pre["ms_rope2"]) / pre["ms_none"] - 1.0, 4)}
+                "avg_launch_us": round(pre["ms_attend"] * 1e3, 2),
+                "merge_kernel_us": round((pre["ms"] - pre["ms_attend"]) * 1e3, 2)}
+    rope_overhead = {"prefill_rope_us": round(pre["ms_attend"] * 1e3, 2),
+                     "prefill_rope_repeat_us": round(pre["ms_rope2_attend"] * 1e3, 2),
+                     "prefill_norotation_us": round(pre["ms_none_attend"] * 1e3, 2),
+                     "prefill_overhead": round(min(pre["ms_attend"], pre["ms_rope2_attend"]) /
+                                               pre["ms_none_attend"] - 1.0, 4)}
     out = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(pre["ms"], 5), "higher_is_better": True, "scaling": "weak",
@@ -319,8 +343,9 @@ def main() -> int:
         out["decode"] = {
             "workload": "decode, Llama-3.1-8B shape: 128 requests x 8 Zipf(1.2) documents x 512 tokens "
                         "+ 32-token suffix, steps 0..%d" % (args.decode_steps - 1),
-            "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round(dec["ms"] * 1e3, 2),
-            "tokens_per_s": round(128 / (dec["ms"] * 1e-3), 1), "splits": dec["splits"],
+            "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round((dec["ms"] + dec["merge_ms"]) * 1e3, 2),
+            "attention_kernel_us": round(dec["ms"] * 1e3, 2), "merge_kernel_us": round(dec["merge_ms"] * 1e3, 2),
+            "tokens_per_s": round(128 / ((dec["ms"] + dec["merge_ms"]) * 1e-3), 1), "splits": dec["splits"],
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dtraffic,
                          "kernel": "decode_bf16_kernel<ROPE,1>", "bytes_per_launch_logical": round(dec["bytes"]),

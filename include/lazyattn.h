@@ -130,13 +130,11 @@ int32_t lazyattn_decode_splits(const lazyattn_config* cfg, int32_t num_reqs, int
 
 /* Workspace bytes for a prefill/decode call with these sizes (num_splits as
  * passed to the call; 0 => the heuristic).  0 means no workspace needed.
- * A call that splits the key range uses its workspace as 256 KiB of per-tile
- * arrival counters followed by fp32 partial results; the last work-group of
- * each tile to finish merges the partials inside the same kernel launch and
- * resets its counter.  Hence: the workspace must be zero-filled before its
- * first use (allocate it zeroed); every call that completes leaves the
- * counters zero again, so the same buffer serves later calls of any size that
- * fits; calls that may run concurrently must not share a workspace. */
+ * A call that splits the key range into S > 1 parts writes fp32 partial
+ * results to the workspace: o [S][rows][Hq][D] then (m, l) [S][rows][Hq][2]
+ * (rows = total_q for prefill, num_reqs for decode); the merge kernel then
+ * combines them.  The workspace needs no initialisation; calls that may run
+ * concurrently must not share one. */
 size_t lazyattn_prefill_workspace_size(const lazyattn_config* cfg, int32_t num_reqs, int32_t total_q,
                                        int32_t max_q_len, int32_t max_entries, int32_t num_splits);
 size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_reqs,
@@ -157,10 +155,10 @@ size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_re
  *  batch      host struct holding device arrays
  *  num_splits 0 => heuristic; else 1..64 splits of the key range
  *  out        device [total_q][Hq][D]
- *  workspace  device, >= lazyattn_prefill_workspace_size(...) bytes,
- *             zero-filled before first use (may be NULL when that size is 0).
- *  Exactly one kernel is launched.  EUNSUPPORTED when a split call would need
- *  more than 65536 tiles (query tiles x requests x KV heads). */
+ *  workspace  device, >= lazyattn_prefill_workspace_size(...) bytes (may be
+ *             NULL when that size is 0).
+ *  Launches the attention kernel and, when the key range is split, the merge
+ *  kernel (lazyattn_prefill_attend followed by lazyattn_merge_splits). */
 lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
                                  int32_t total_q, int32_t max_q_len, const void* k_pool,
                                  const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
@@ -173,11 +171,37 @@ lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, cons
  *  q    device [R][Hq][D];  out device [R][Hq][D]
  *  num_splits 0 => heuristic; else 1..256 splits of each request's entries
  *  workspace as for prefill (>= lazyattn_decode_workspace_size bytes).
- *  Exactly one kernel is launched.  bf16 supports G = Hq/Hkv <= 32. */
+ *  Launches the attention kernel and, when split, the merge kernel.  bf16
+ *  supports G = Hq/Hkv <= 32. */
 lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const void* k_pool,
                                 const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
                                 int32_t num_splits, void* out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/* The attention kernel of lazyattn_prefill / lazyattn_decode alone (same
+ * arguments).  With one split it writes `out` directly; with S > 1 splits
+ * (see lazyattn_prefill_splits / lazyattn_decode_splits for num_splits 0) it
+ * writes partials to `workspace` and leaves `out` untouched until
+ * lazyattn_merge_splits runs on the same stream.  For callers that schedule
+ * or time the two kernels separately. */
+lazyattn_status lazyattn_prefill_attend(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
+                                        int32_t total_q, int32_t max_q_len, const void* k_pool,
+                                        const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                        int32_t num_splits, void* out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+lazyattn_status lazyattn_decode_attend(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                       const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                       int32_t num_splits, void* out, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/* Log-sum-exp merge of S split partials into out [num_rows][Hq][D] (bf16):
+ * out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, summed in
+ * split order.  num_rows = total_q (prefill) or num_reqs (decode); workspace as
+ * written by the matching *_attend call with S = num_splits.  num_splits 1 is a
+ * no-op.  EWORKSPACE if workspace_bytes is short of S*num_rows*Hq*(D+2)*4. */
+lazyattn_status lazyattn_merge_splits(const lazyattn_config* cfg, int32_t num_rows, int32_t num_splits,
+                                      const void* workspace, size_t workspace_bytes, void* out,
+                                      hipStream_t stream);
 
 /* Write n new tokens' content-only K/V into the pool (gist.science,
  * Methodology: the cache stores content-based keys and values, no rotation).

@@ -82,6 +82,9 @@ def lib() -> ctypes.CDLL:
             "lazyattn_decode_workspace_size": (SZ, [CP, I32, I32, I32]),
             "lazyattn_prefill": (I32, [CP, P, P, I32, I32, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_decode": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
+            "lazyattn_prefill_attend": (I32, [CP, P, P, I32, I32, P, P, I64, BP, I32, P, P, SZ, P]),
+            "lazyattn_decode_attend": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
+            "lazyattn_merge_splits": (I32, [CP, I32, I32, P, SZ, P, P]),
             "lazyattn_append_kv": (I32, [CP, P, P, I64, P, P, P, I32, P]),
             "lazyattn_debug_decode_tables": (I32, [BP, P, P]),
         }
@@ -208,6 +211,31 @@ def decode(cfg: Config, q, k_pool, v_pool, num_blocks: int, batch: Batch, out, w
                                ctypes.byref(batch), int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
                                _stream(stream))
     _check(st, "lazyattn_decode")
+
+
+def prefill_attend(cfg: Config, q, cu_q_lens, total_q: int, max_q_len: int, k_pool, v_pool, num_blocks: int,
+                   batch: Batch, out, workspace=None, num_splits: int = 0, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lazyattn_prefill_attend(ctypes.byref(cfg), _ptr(q), _ptr(cu_q_lens), int(total_q), int(max_q_len),
+                                       _ptr(k_pool), _ptr(v_pool), int(num_blocks), ctypes.byref(batch),
+                                       int(num_splits), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "lazyattn_prefill_attend")
+
+
+def decode_attend(cfg: Config, q, k_pool, v_pool, num_blocks: int, batch: Batch, out, workspace=None,
+                  num_splits: int = 0, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lazyattn_decode_attend(ctypes.byref(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), int(num_blocks),
+                                      ctypes.byref(batch), int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
+                                      _stream(stream))
+    _check(st, "lazyattn_decode_attend")
+
+
+def merge_splits(cfg: Config, num_rows: int, num_splits: int, workspace, out, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lazyattn_merge_splits(ctypes.byref(cfg), int(num_rows), int(num_splits), _ptr(workspace), ws_bytes,
+                                     _ptr(out), _stream(stream))
+    _check(st, "lazyattn_merge_splits")
 
 
 def append_kv(cfg: Config, k_pool, v_pool, num_blocks: int, k_new, v_new, slots, stream=None) -> None:

@@ -12,10 +12,6 @@ namespace lazyattn {
 constexpr int kBlock = 16;        // tokens per pool block
 constexpr int kMaxPairs = 64;     // head_dim <= 128
 
-// Split-K workspace: a fixed region of per-tile arrival counters first (so
-// its place never depends on a call's sizes), then the partial results.
-constexpr int kMaxSplitTiles = 65536;
-constexpr size_t kCounterBytes = static_cast<size_t>(kMaxSplitTiles) * sizeof(unsigned);
 
 // RoPE frequencies as revolutions per position: rev_i = theta^(-2i/D) / (2 pi),
 // computed in double on the host.  Angles are reduced in double on the device

@@ -96,22 +96,6 @@ __device__ __forceinline__ f32x4 mfma16x16x16(const s16x4& a, const s16x4& b, co
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Split-K completion: every work-group of a tile publishes its partial
-// result, then increments the tile's counter; the one that brings it to
-// `splits` sees every partial and merges them.  Device-scope fences order the
-// partial stores before the increment and the merge loads after it (the
-// XCDs' L2 caches are not coherent with each other without them).
-__device__ __forceinline__ bool arrive_last(unsigned* counter, int splits) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == static_cast<unsigned>(splits - 1);
-  __syncthreads();
-  if (!s_last) return false;
-  __threadfence();
-  return true;
-}
-
 // ---------------------------------------------------------------------------
 // Prefill, bf16, MFMA.
 //
@@ -123,7 +107,21 @@ __device__ __forceinline__ bool arrive_last(unsigned* counter, int splits) {
 //   online softmax over the keys of each row (base 2, scale folded into Q~)
 //   O^T (D x rows)   += V^T (D x keys) . P^T         16x16x32 MFMA, V^T from LDS
 // The S^T accumulator leaves each lane with 4 consecutive keys of one row,
-// which is exactly a P^T operand slice, so P never leaves registers.
+// which is exactly a P^T operand slice, so P never leaves registers.  A ninth
+// O tile multiplies P by a row of ones, so the softmax denominator is the sum
+// of exactly the bf16 weights that enter P.V, at no vector-ALU cost.
+//
+// Schedule.  Key tile j is staged (rotated K, transposed V) into one of two
+// LDS buffers by all 512 threads; K runs two tiles ahead of its use and V
+// one, with global loads one iteration ahead of staging and a single barrier
+// per iteration.  Each tile's entries (block, start, length) are decoded once
+// into a small LDS ring by wave 0, one iteration ahead of their first use.
+// The two waves sharing a SIMD (w and w+4) run the same iteration in opposite
+// phase order, so one's MFMA work overlaps the other's vector work:
+//   waves 0-3:  [QK(i+1), PV(i)]  [softmax(i+1)]  [staging]
+//   waves 4-7:  [softmax(i)]  [staging]  [PV(i), QK(i+1)]
+// With the key range split, each split writes unnormalised (o, m, l) and the
+// merge kernel combines them.
 // ---------------------------------------------------------------------------
 struct PrefillArgs {
   const uint16_t* q;
@@ -137,7 +135,6 @@ struct PrefillArgs {
   uint16_t* out;
   float* o_part;
   float* ml_part;
-  unsigned* counters;
   int32_t Hq, Hkv, G, max_entries, total_q, m_q, eps, splits;
   float scale_log2;
   RopeRev rope;
@@ -145,17 +142,24 @@ struct PrefillArgs {
 
 constexpr int kPD = 128;        // head dim of the bf16 kernels
 constexpr int kKS = kPD + 8;    // K tile row stride in bf16 (272 B: conflict-free 16-lane reads)
-constexpr int kVS = 40;         // V tile row stride in bf16 (80 B)
+constexpr int kVS = 40;         // V tile row stride in bf16 (80 B: conflict-free 16-lane reads)
+constexpr int kBS = 10;         // phase chunk stride in float2 (80 B: conflict-free reads)
+constexpr float kRescaleSlack = 8.0f;   // running max is raised only when it grows by more than 2^8
 
 template <int PE>
 __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs A) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * kPD * kVS];
-  __shared__ __attribute__((aligned(16))) float2 base_s[2][4][64];
-  __shared__ __attribute__((aligned(16))) float2 rtab[16][64];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][2 * kPD * kVS];
+  __shared__ __attribute__((aligned(16))) float2 base_s[2][4][8][kBS];
+  __shared__ __attribute__((aligned(16))) float2 rtab[16][8][kBS];
+  __shared__ __attribute__((aligned(16))) float2 r16tab[16][64];
+  __shared__ __attribute__((aligned(16))) int4 tinfo[8][4];   // (block, start, length, 0) per entry
 
   const int tid = threadIdx.x;
+  // the wave index stays a vector value: as a scalar it turns the phase-order
+  // test below into a uniform branch, and register allocation across it spills
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int grp = (wave >> 2) & 1;
   const int qt = blockIdx.x, r = blockIdx.y;
   const int kvh = blockIdx.z % A.Hkv, split = blockIdx.z / A.Hkv;
   const int q0 = A.cu_q[r];
@@ -172,15 +176,63 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs A) 
   const int e_end = min(ne, e_begin + A.eps);
   const int G = A.G, Hq = A.Hq, Hkv = A.Hkv;
 
-  // ---- rows owned by this lane, and the query fragments -------------------
-  int p_row[2], tok[2], head[2];
+  // Entries past the last query position contribute nothing: stop before them.
+  // Usually the split's last entry is visible already; otherwise a 64-way
+  // vector search over table words finds the first invisible entry.
+  int e_stop = max(e_begin, e_end);
+  if (e_end > e_begin && static_cast<int>(word_start(trow[e_end - 1])) > p_last) {
+    int lo = e_begin, hi = e_end - 1;               // start(hi) > p_last; all before lo are visible
+    while (lo < hi) {
+      const int stride = (hi - lo + 63) >> 6;
+      const int e = lo + lane * stride;
+      const bool past = (e < hi) ? static_cast<int>(word_start(trow[e])) > p_last : true;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(past);
+      if (bal == 0) {                              // all 64 probes are visible and below hi
+        lo = lo + 63 * stride + 1;
+        continue;
+      }
+      const int k = __builtin_ctzll(bal);
+      if (k == 0) {
+        hi = lo;
+      } else {
+        const int ek = min(lo + k * stride, hi);
+        lo = lo + (k - 1) * stride + 1;
+        hi = ek;
+      }
+    }
+    e_stop = lo;
+  }
+  const int T = (e_stop - e_begin + 3) >> 2;          // key tiles of this work-group
+
+  // ---- tile metadata: wave 0, lane x handles entry x of a tile ------------------
+  const uint64_t sentinel = static_cast<uint64_t>(static_cast<uint32_t>(L)) << 32;   // start = L
+  auto fetch_words = [&](int j, int x, uint64_t& w, uint64_t& wn) {
+    const int e = e_begin + 4 * j + x;
+    w = wn = sentinel;
+    if (e < e_stop) {
+      w = trow[e];
+      wn = (e + 1 < ne) ? trow[e + 1] : sentinel;
+    }
+  };
+  auto write_info = [&](int j, int x, uint64_t w, uint64_t wn) {
+    const int e = e_begin + 4 * j + x;
+    const int st = static_cast<int>(word_start(w));
+    tinfo[j & 7][x] = (e < e_stop) ? make_int4(static_cast<int>(word_block(w)), st,
+                                               static_cast<int>(word_start(wn)) - st, 0)
+                                   : make_int4(0, 0, 0, 0);
+  };
+
+  // ---- rows owned by this lane, and the raw query fragments ----------------
+  int p_row[2], tok[2], head[2], mrow[2];
   bool row_ok[2];
   float slope[2];
+  uint4 qraw[2][4];
   bf16x8 qf[2][4];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int rho = wave * 32 + nt * 16 + n;
     const int m = rho / G, gh = rho - m * G;
+    mrow[nt] = m;
     row_ok[nt] = m < mq;
     p_row[nt] = p0 + m;
     tok[nt] = q0 + m0 + m;
@@ -188,231 +240,279 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs A) 
     slope[nt] = (PE == LAZYATTN_PE_ALIBI) ? alibi_slope(A.alibi, head[nt], Hq) * kLog2e : 0.0f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
+      qraw[nt][s] = make_uint4(0, 0, 0, 0);
       if (row_ok[nt])
-        raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(tok[nt]) * Hq + head[nt]) * kPD +
-                                              32 * s + 8 * g);
-      uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
-        if (PE == LAZYATTN_PE_ROPE) {
-          const float2 ph = unit_phase(m, A.rope.rev[16 * s + 4 * g + jj]);
-          const float y0 = x0 * ph.x - x1 * ph.y;
-          const float y1 = x0 * ph.y + x1 * ph.x;
-          x0 = y0;
-          x1 = y1;
-        }
-        w4[jj] = pack_bf16x2(x0 * A.scale_log2, x1 * A.scale_log2);
-      }
-      qf[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        qraw[nt][s] = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(tok[nt]) * Hq + head[nt]) * kPD +
+                                                      32 * s + 8 * g);
     }
   }
 
-  // ---- per-lane key rotation table R(r) for r = 0..15 ----------------------
-  if (PE == LAZYATTN_PE_ROPE) {
-    for (int i = tid; i < 16 * 64; i += 512) rtab[i >> 6][i & 63] = unit_phase(i >> 6, A.rope.rev[i & 63]);
-  }
+  // staging roles: thread -> (entry se, key row sr, channel pairs 8sc..8sc+7) for K,
+  //                thread -> (entry se, channel sd) for V; se is uniform per wave
+  const int se = __builtin_amdgcn_readfirstlane(tid >> 7), sr = (tid >> 3) & 15, sc = tid & 7, sd = tid & 127;
 
-  // staging roles: thread -> (entry se, key row sr, channel chunk sc) for K,
-  //                thread -> (entry se, channel sd) for V
-  const int se = tid >> 7, sr = (tid >> 3) & 15, sc = tid & 7, sd = tid & 127;
-
-  f32x4 O[8][2];
+  f32x4 O[9][2];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt][0] = O[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
+  for (int dt = 0; dt < 9; ++dt) O[dt][0] = O[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {kNegInf, kNegInf};
+  // A operand of the ones tile: row 0 of the 16-row slab is all ones
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, n == 0 ? make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u)
+                                                         : make_uint4(0u, 0u, 0u, 0u));
 
-  // entries of tile starting at et: valid when inside the split, in the table
-  // and not entirely after the tile's last query position
-  auto tile_entry = [&](int et, int i, EntryInfo& inf) -> bool {
-    const int e = et + i;
-    if (e >= e_end) return false;
-    inf = entry_info(trow, e, ne, L);
-    return inf.start <= p_last;
-  };
-
+  // ---- helpers ---------------------------------------------------------------
   uint4 kr0 = make_uint4(0, 0, 0, 0), kr1 = kr0, vr0 = kr0, vr1 = kr0;
-  auto load_tile = [&](int et) {
-    EntryInfo inf;
-    if (tile_entry(et, se, inf)) {
-      const uint16_t* kb = A.kpool + (static_cast<size_t>(inf.blk) * Hkv + kvh) * (kBlock * kPD);
-      const uint4* kp = reinterpret_cast<const uint4*>(kb + sr * kPD + 16 * sc);
-      kr0 = kp[0];
-      kr1 = kp[1];
-      const uint16_t* vb = A.vpool + (static_cast<size_t>(inf.blk) * Hkv + kvh) * (kPD * kBlock);
-      const uint4* vp = reinterpret_cast<const uint4*>(vb + sd * kBlock);
+  auto load_k = [&](int j, uint4& a, uint4& b) {
+    const int4 inf = tinfo[j & 7][se];
+    if (inf.z > 0) {
+      const uint4* kp = reinterpret_cast<const uint4*>(
+          A.kpool + (static_cast<size_t>(static_cast<uint32_t>(inf.x)) * Hkv + kvh) * (kBlock * kPD) + sr * kPD + 16 * sc);
+      a = kp[0];
+      b = kp[1];
+    }
+  };
+  auto load_v = [&](int j) {
+    const int4 inf = tinfo[j & 7][se];
+    if (inf.z > 0) {
+      const uint4* vp = reinterpret_cast<const uint4*>(
+          A.vpool + (static_cast<size_t>(static_cast<uint32_t>(inf.x)) * Hkv + kvh) * (kPD * kBlock) + sd * kBlock);
       vr0 = vp[0];
       vr1 = vp[1];
     }
   };
-  auto tile_bases = [&](int et, int buf) {
+  // phase R(start_e - p0) of each entry e and channel pair, for tile j
+  auto compute_base = [&](int j) {
     if (PE == LAZYATTN_PE_ROPE && tid < 256) {
-      const int e = tid >> 6, pr = tid & 63;
-      EntryInfo inf;
-      float2 ph = make_float2(1.f, 0.f);
-      if (tile_entry(et, e, inf)) ph = unit_phase(inf.start - p0, A.rope.rev[pr]);
-      base_s[buf][e][pr] = ph;
+      const int e = __builtin_amdgcn_readfirstlane(tid >> 6), pr = tid & 63;
+      const int4 inf = tinfo[j & 7][e];
+      const float2 ph = inf.z > 0 ? unit_phase(inf.y - p0, A.rope.rev[pr]) : make_float2(1.f, 0.f);
+      base_s[j & 1][e][pr >> 3][pr & 7] = ph;
     }
   };
-
-  int et = e_begin;
-  bool have = e_begin < e_end && entry_info(trow, e_begin, ne, L).start <= p_last;
-  if (have) {
-    load_tile(et);
-    tile_bases(et, 0);
-  }
-  __syncthreads();
-
-  for (int it = 0; have; ++it) {
-    const int buf = it & 1;
-    // ---- stage tile `et` into LDS: rotate K, transpose V into MFMA order --
-    {
-      EntryInfo inf;
-      const bool ok = tile_entry(et, se, inf);
-      const int len = ok ? inf.len : 0;
-      // K: rows past the entry's length are written as zeros
-      uint32_t kw[8] = {kr0.x, kr0.y, kr0.z, kr0.w, kr1.x, kr1.y, kr1.z, kr1.w};
-      if (sr >= len) {
+  // rotate this thread's K slice of tile j by R(start - p0 + sr) and store it
+  auto stage_k = [&](int j, const uint4& a, const uint4& b) {
+    const int len = tinfo[j & 7][se].z;
+    uint32_t kw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    if (sr >= len) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kw[i] = 0;
-      } else if (PE == LAZYATTN_PE_ROPE) {
+      for (int i = 0; i < 8; ++i) kw[i] = 0;
+    } else if (PE == LAZYATTN_PE_ROPE) {
+      const float2* bp = base_s[j & 1][se][sc];
+      const float2* rp = rtab[sr][sc];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kw[i] = rotate_pair(kw[i], cmul(base_s[buf][se][8 * sc + i], rtab[sr][8 * sc + i]));
-      }
-      uint4* kd = reinterpret_cast<uint4*>(&Ks[(16 * se + sr) * kKS + 16 * sc]);
-      kd[0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-      kd[1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
-      // V: channel sd of entry se, keys 4gg..4gg+3 -> Vs[se/2][sd][gg*8 + (se&1)*4 ..]
-      uint32_t vw[8] = {vr0.x, vr0.y, vr0.z, vr0.w, vr1.x, vr1.y, vr1.z, vr1.w};
-      if (len < kBlock) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int k0 = 2 * i, k1 = 2 * i + 1;
-          uint32_t lo = (k0 < len) ? (vw[i] & 0xffffu) : 0u;
-          uint32_t hi = (k1 < len) ? (vw[i] & 0xffff0000u) : 0u;
-          vw[i] = lo | hi;
-        }
-      }
-      uint16_t* vrow = &Vs[((se >> 1) * kPD + sd) * kVS + (se & 1) * 4];
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        *reinterpret_cast<uint2*>(vrow + gg * 8) = make_uint2(vw[2 * gg], vw[2 * gg + 1]);
+      for (int i = 0; i < 8; ++i) kw[i] = rotate_pair(kw[i], cmul(bp[i], rp[i]));
     }
-    // ---- prefetch the next tile ---------------------------------------------
-    const int et_next = et + 4;
-    const bool have_next = et_next < e_end && entry_info(trow, et_next, ne, L).start <= p_last;
-    if (have_next) {
-      load_tile(et_next);
-      tile_bases(et_next, buf ^ 1);
-    }
-    __syncthreads();
-
-    // ---- tile masks (wave-uniform) --------------------------------------------
-    int t_start[4], t_len[4];
-    bool full = true;
+    uint4* kd = reinterpret_cast<uint4*>(&Ks[j & 1][(16 * se + sr) * kKS + 16 * sc]);
+    kd[0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    kd[1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
+  };
+  // channel sd of entry se, keys 4gg..4gg+3 -> Vs[.][se/2][sd][gg*8 + (se&1)*4 ..]
+  auto stage_v = [&](int j) {
+    const int len = tinfo[j & 7][se].z;
+    uint32_t vw[8] = {vr0.x, vr0.y, vr0.z, vr0.w, vr1.x, vr1.y, vr1.z, vr1.w};
+    if (len < kBlock) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      EntryInfo inf;
-      if (tile_entry(et, i, inf)) {
-        t_start[i] = inf.start;
-        t_len[i] = inf.len;
-      } else {
-        t_start[i] = 0;
-        t_len[i] = 0;
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo16 = (2 * i < len) ? (vw[i] & 0xffffu) : 0u;
+        const uint32_t hi16 = (2 * i + 1 < len) ? (vw[i] & 0xffff0000u) : 0u;
+        vw[i] = lo16 | hi16;
       }
-      full = full && t_len[i] == kBlock;
     }
-    full = full && (t_start[3] + kBlock - 1 <= p0);
-
-    // ---- S^T = K~ Q~^T ---------------------------------------------------------
-    f32x4 S[4][2];
+    uint16_t* vrow = &Vs[j & 1][((se >> 1) * kPD + sd) * kVS + (se & 1) * 4];
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+      *reinterpret_cast<uint2*>(vrow + gg * 8) = make_uint2(vw[2 * gg], vw[2 * gg + 1]);
+  };
+  auto qk = [&](int j, f32x4 (&S)[4][2]) {
+    const uint16_t* kb = Ks[j & 1];
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       S[tau][0] = S[tau][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(16 * tau + n) * kKS + 32 * s + 8 * g]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[(16 * tau + n) * kKS + 32 * s + 8 * g]);
         S[tau][0] = mfma16x16x32(a, qf[0][s], S[tau][0]);
         S[tau][1] = mfma16x16x32(a, qf[1][s], S[tau][1]);
       }
     }
-
-    // ---- online softmax, per row ------------------------------------------------
-    uint32_t pk[4][2][2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v = S[tau][nt][j];
-          const int kr = 4 * g + j;
-          const int t = t_start[tau] + kr;
-          if (!full) {
-            const bool vis = (kr < t_len[tau]) && (t <= p_row[nt]);
-            v = vis ? v : kNegInf;
-          }
-          if (PE == LAZYATTN_PE_ALIBI) v -= slope[nt] * static_cast<float>(p_row[nt] - t);
-          S[tau][nt][j] = v;
-          mx = fmaxf(mx, v);
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-      // the row sum uses the bf16-rounded weights that enter P.V, so the
-      // output is an exact convex combination of the V rows
-      float rs = 0.f;
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        float pe[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pe[j] = __builtin_amdgcn_exp2f(S[tau][nt][j] - m_use);
-        pk[tau][nt][0] = pack_bf16x2(pe[0], pe[1]);
-        pk[tau][nt][1] = pack_bf16x2(pe[2], pe[3]);
-        rs += (bf_lo(pk[tau][nt][0]) + bf_hi(pk[tau][nt][0])) + (bf_lo(pk[tau][nt][1]) + bf_hi(pk[tau][nt][1]));
-      }
-      l_run[nt] = l_run[nt] * alpha + rs;
-      m_run[nt] = m_new;
-      if (alpha != 1.0f) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) O[dt][nt] *= alpha;
-      }
-    }
-
-    // ---- O^T += V^T P^T -----------------------------------------------------------
+  };
+  auto pv = [&](int j, const uint32_t (&pk)[4][2][2]) {
+    const uint16_t* vb = Vs[j & 1];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(pk[2 * u][0][0], pk[2 * u][0][1], pk[2 * u + 1][0][0], pk[2 * u + 1][0][1]));
-      bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(pk[2 * u][1][0], pk[2 * u][1][1], pk[2 * u + 1][1][0], pk[2 * u + 1][1][1]));
+      const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(pk[2 * u][0][0], pk[2 * u][0][1], pk[2 * u + 1][0][0], pk[2 * u + 1][0][1]));
+      const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(pk[2 * u][1][0], pk[2 * u][1][1], pk[2 * u + 1][1][0], pk[2 * u + 1][1][1]));
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vs[(u * kPD + 16 * dt + n) * kVS + 8 * g]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vb[(u * kPD + 16 * dt + n) * kVS + 8 * g]);
         O[dt][0] = mfma16x16x32(a, b0, O[dt][0]);
         O[dt][1] = mfma16x16x32(a, b1, O[dt][1]);
       }
+      O[8][0] = mfma16x16x32(ones, b0, O[8][0]);
+      O[8][1] = mfma16x16x32(ones, b1, O[8][1]);
+    }
+  };
+  // scores of tile j -> bf16 weights; raises the running maxima (rescaling O) when needed
+  auto softmax = [&](int j, f32x4 (&S)[4][2], uint32_t (&pk)[4][2][2]) {
+    int t_start[4], t_len[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int4 inf = tinfo[j & 7][i];
+      t_start[i] = __builtin_amdgcn_readfirstlane(inf.y);
+      t_len[i] = __builtin_amdgcn_readfirstlane(inf.z);
+    }
+    const bool full = (t_len[0] == kBlock) && (t_len[1] == kBlock) && (t_len[2] == kBlock) &&
+                      (t_len[3] == kBlock) && (t_start[3] + kBlock - 1 <= p0);
+    if (!full || PE == LAZYATTN_PE_ALIBI) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int kr = 4 * g + jj;
+            const int t = t_start[tau] + kr;
+            float v = S[tau][nt][jj];
+            if (PE == LAZYATTN_PE_ALIBI) v -= slope[nt] * static_cast<float>(p_row[nt] - t);
+            if (!full) v = ((kr < t_len[tau]) && (t <= p_row[nt])) ? v : kNegInf;
+            S[tau][nt][jj] = v;
+          }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float mx = fmaxf(fmaxf(fmaxf(S[0][nt][0], S[0][nt][1]), fmaxf(S[0][nt][2], S[0][nt][3])),
+                       fmaxf(fmaxf(S[1][nt][0], S[1][nt][1]), fmaxf(S[1][nt][2], S[1][nt][3])));
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(S[2][nt][0], S[2][nt][1]), fmaxf(S[2][nt][2], S[2][nt][3])),
+                           fmaxf(fmaxf(S[3][nt][0], S[3][nt][1]), fmaxf(S[3][nt][2], S[3][nt][3]))));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // raise the reference maximum only when the row's scores outgrow it by 2^8;
+      // exact: numerator and denominator share the reference
+      const bool raise = mx > m_run[nt] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float m_new = raise ? mx : m_run[nt];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);   // 0 when m_run = -inf
+#pragma unroll
+        for (int dt = 0; dt < 9; ++dt) O[dt][nt] *= alpha;
+        m_run[nt] = m_new;
+      }
+      const float m_use = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const float e0 = __builtin_amdgcn_exp2f(S[tau][nt][0] - m_use);
+        const float e1 = __builtin_amdgcn_exp2f(S[tau][nt][1] - m_use);
+        const float e2 = __builtin_amdgcn_exp2f(S[tau][nt][2] - m_use);
+        const float e3 = __builtin_amdgcn_exp2f(S[tau][nt][3] - m_use);
+        pk[tau][nt][0] = pack_bf16x2(e0, e1);
+        pk[tau][nt][1] = pack_bf16x2(e2, e3);
+      }
+    }
+  };
+  // query rows rotated by R(m) = R(16 (m / 16)) R(m % 16), scaled by scale*log2(e), rounded to bf16
+  auto rotate_q = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 raw = qraw[nt][s];
+        uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
+          if (PE == LAZYATTN_PE_ROPE) {
+            const int pr = 16 * s + 4 * g + jj, m = mrow[nt] & 255;
+            const float2 ph = cmul(r16tab[m >> 4][pr], rtab[m & 15][pr >> 3][pr & 7]);
+            const float y0 = x0 * ph.x - x1 * ph.y;
+            const float y1 = x0 * ph.y + x1 * ph.x;
+            x0 = y0;
+            x1 = y1;
+          }
+          w4[jj] = pack_bf16x2(x0 * A.scale_log2, x1 * A.scale_log2);
+        }
+        qf[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      }
+  };
+
+  // ---- pipeline ------------------------------------------------------------------
+  if (T > 0) {
+    // P0: tile metadata for tiles 0..3 (wave 0) and the rotation tables
+    if (tid < 16) {
+      uint64_t w, wn;
+      fetch_words(tid >> 2, tid & 3, w, wn);
+      write_info(tid >> 2, tid & 3, w, wn);
+    }
+    if (PE == LAZYATTN_PE_ROPE) {
+      for (int i = tid; i < 16 * 64; i += 512) {
+        rtab[i >> 6][(i & 63) >> 3][i & 7] = unit_phase(i >> 6, A.rope.rev[i & 63]);
+        r16tab[i >> 6][i & 63] = unit_phase(16 * (i >> 6), A.rope.rev[i & 63]);
+      }
     }
     __syncthreads();
-    et = et_next;
-    have = have_next;
+    // P1: phases of tiles 0 and 1, first loads, metadata words of tile 4
+    uint64_t pw = sentinel, pwn = sentinel;          // tile metadata one iteration ahead (wave 0)
+    compute_base(0);
+    compute_base(1);
+    uint4 ka0 = kr0, ka1 = kr0;
+    load_k(0, ka0, ka1);
+    load_k(1, kr0, kr1);
+    load_v(0);
+    if (tid < 4) fetch_words(4, tid, pw, pwn);
+    __syncthreads();
+    // P2: query rotation, staging of K(0), K(1), V(0); loads of K(2), V(1)
+    rotate_q();
+    stage_k(0, ka0, ka1);
+    stage_k(1, kr0, kr1);
+    stage_v(0);
+    load_k(2, kr0, kr1);
+    load_v(1);
+    __syncthreads();
+    // P3: phases of tile 2, first scores
+    compute_base(2);
+    f32x4 S[4][2];
+    uint32_t pk[4][2][2];
+    qk(0, S);
+    if (grp == 0) softmax(0, S, pk);
+    __syncthreads();
+    for (int i = 0; i < T; ++i) {
+      const bool nxt = i + 1 < T;
+      if (grp == 0) {
+        if (nxt) qk(i + 1, S);
+        pv(i, pk);
+        if (nxt) softmax(i + 1, S, pk);
+      } else {
+        softmax(i, S, pk);
+      }
+      if (i + 2 < T) stage_k(i + 2, kr0, kr1);
+      if (nxt) stage_v(i + 1);
+      if (i + 3 < T) {
+        load_k(i + 3, kr0, kr1);
+        compute_base(i + 3);
+      }
+      if (i + 2 < T) load_v(i + 2);
+      if (tid < 4) {
+        write_info(i + 4, tid, pw, pwn);
+        fetch_words(i + 5, tid, pw, pwn);
+      }
+      if (grp == 1) {
+        pv(i, pk);
+        if (nxt) qk(i + 1, S);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------------
+  // row sums: the ones tile holds them in register 0 of the lanes with g == 0
   float lt[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    lt[nt] = l_run[nt] + __shfl_xor(l_run[nt], 16);
+    lt[nt] = O[8][nt][0] + __shfl_xor(O[8][nt][0], 16);
     lt[nt] += __shfl_xor(lt[nt], 32);
   }
-  if (A.splits == 1) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      if (!row_ok[nt]) continue;
-      const size_t rowoff = static_cast<size_t>(tok[nt]) * Hq + head[nt];
+  for (int nt = 0; nt < 2; ++nt) {
+    if (!row_ok[nt]) continue;
+    const size_t rowoff = static_cast<size_t>(tok[nt]) * Hq + head[nt];
+    if (A.splits == 1) {
       const float inv = 1.0f / lt[nt];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -420,60 +520,49 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs A) 
         *reinterpret_cast<uint2*>(A.out + rowoff * kPD + 16 * dt + 4 * g) =
             make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
       }
+    } else {
+      // this split's unnormalised output, reference maximum and sum
+      const size_t prow = static_cast<size_t>(split) * A.total_q * Hq + rowoff;
+      if (lt[nt] > 0.f) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<f32x4*>(A.o_part + prow * kPD + 16 * dt + 4 * g) = O[dt][nt];
+      }
+      if (g == 0)
+        *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(lt[nt] > 0.f ? m_run[nt] : kNegInf, lt[nt]);
     }
-    return;
   }
-  // Split keys: publish this split's (o, m, l); the last work-group of the
-  // tile to arrive merges all splits with log-sum-exp weights.
-  const size_t rows_total = static_cast<size_t>(A.total_q) * Hq;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    if (!row_ok[nt]) continue;
-    const size_t prow = static_cast<size_t>(split) * rows_total + static_cast<size_t>(tok[nt]) * Hq + head[nt];
-    if (lt[nt] > 0.f) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4*>(A.o_part + prow * kPD + 16 * dt + 4 * g) = O[dt][nt];
-    }
-    if (g == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(m_run[nt], lt[nt]);
-  }
-  const unsigned tile = (static_cast<unsigned>(qt) * gridDim.y + r) * Hkv + kvh;
-  if (!arrive_last(A.counters + tile, A.splits)) return;
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    if (!row_ok[nt]) continue;
-    const size_t rowoff = static_cast<size_t>(tok[nt]) * Hq + head[nt];
-    // merge in split order whichever work-group arrived last, so the result
-    // is bit-for-bit reproducible; this work-group's own partial comes from
-    // registers, which hold exactly what it stored
-    float M = kNegInf;
-    for (int sp = 0; sp < A.splits; ++sp)
-      M = fmaxf(M, sp == split ? m_run[nt] : A.ml_part[(static_cast<size_t>(sp) * rows_total + rowoff) * 2]);
-    float Lsum = 0.f;
-    f32x4 acc[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < A.splits; ++sp) {
-      const size_t prow = static_cast<size_t>(sp) * rows_total + rowoff;
-      const float2 ml = sp == split ? make_float2(m_run[nt], lt[nt])
-                                    : *reinterpret_cast<const float2*>(A.ml_part + prow * 2);
+}
+
+// ---------------------------------------------------------------------------
+// Split merge: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s, summed in split order (bit-for-bit reproducible).  One
+// 32-lane group per (row, head), 4 channels per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(const float* o_part, const float* ml_part, uint16_t* out,
+                                                    int rows, int splits) {
+  const int idx = blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int c = threadIdx.x & 31;
+  if (idx >= rows) return;
+  float M = kNegInf;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml_part[(static_cast<size_t>(s) * rows + idx) * 2]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  if (M != kNegInf) {
+    for (int s = 0; s < splits; ++s) {
+      const size_t row = static_cast<size_t>(s) * rows + idx;
+      const float2 ml = *reinterpret_cast<const float2*>(ml_part + row * 2);
       if (ml.x == kNegInf) continue;
       const float w = __builtin_amdgcn_exp2f(ml.x - M);
-      Lsum = fmaf(w, ml.y, Lsum);
+      lsum = fmaf(w, ml.y, lsum);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(o_part + row * kPD + 4 * c);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 o = sp == split ? O[dt][nt] : *reinterpret_cast<const f32x4*>(A.o_part + prow * kPD + 16 * dt + 4 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[dt][j] = fmaf(w, o[j], acc[dt][j]);
-      }
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, o[j], acc[j]);
     }
-    const float inv = 1.0f / Lsum;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<uint2*>(A.out + rowoff * kPD + 16 * dt + 4 * g) =
-          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv), pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
   }
-  if (tid == 0) A.counters[tile] = 0u;  // leave the counter ready for the next call
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  *reinterpret_cast<uint2*>(out + static_cast<size_t>(idx) * kPD + 4 * c) =
+      make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
 }
 
 // ---------------------------------------------------------------------------
@@ -498,7 +587,6 @@ struct DecodeArgs {
   uint16_t* out;
   float* o_part;
   float* ml_part;
-  unsigned* counters;
   int32_t R, Hq, Hkv, G, max_entries, eps, splits;
   float scale_log2;
   RopeRev rope;
@@ -708,31 +796,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
       if (d == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(M, lsum);
     }
   }
-  if (A.splits == 1) return;
-  // the last split of this (request, KV head) to finish merges all splits
-  const unsigned tile = static_cast<unsigned>(r) * Hkv + kvh;
-  if (!arrive_last(A.counters + tile, A.splits)) return;
-  const size_t rows_total = static_cast<size_t>(A.R) * Hq;
-  for (int idx = tid; idx < G * kPD; idx += 256) {
-    const int col = idx / kPD, d = idx - col * kPD;
-    const size_t rowoff = static_cast<size_t>(r) * Hq + kvh * G + col;
-    float M = kNegInf;
-    for (int sp = 0; sp < A.splits; ++sp) M = fmaxf(M, A.ml_part[(sp * rows_total + rowoff) * 2]);
-    float lsum = 0.f, osum = 0.f;
-    if (M != kNegInf) {
-      for (int sp = 0; sp < A.splits; ++sp) {
-        const size_t prow = sp * rows_total + rowoff;
-        const float2 ml = *reinterpret_cast<const float2*>(A.ml_part + prow * 2);
-        if (ml.x == kNegInf) continue;
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        lsum = fmaf(w, ml.y, lsum);
-        osum = fmaf(w, A.o_part[prow * kPD + d], osum);
-      }
-    }
-    const float val = lsum > 0.f ? osum / lsum : 0.f;
-    A.out[rowoff * kPD + d] = static_cast<uint16_t>(pack_bf16x2(val, 0.f) & 0xffffu);
-  }
-  if (tid == 0) A.counters[tile] = 0u;  // leave the counter ready for the next call
 }
 
 // ---------------------------------------------------------------------------
@@ -868,16 +931,24 @@ static size_t decode_lds_bytes(int nt, int group) {
   return (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(group) * kOS) * sizeof(float);
 }
 
-}  // namespace lazyattn
+// ---------------------------------------------------------------------------
+// launchers (host)
+// ---------------------------------------------------------------------------
 
-using namespace lazyattn;
+static lazyattn_status merge_launch(int rows_total, int splits, const void* workspace, void* out, hipStream_t stream) {
+  const float* o_part = static_cast<const float*>(workspace);
+  const float* ml_part = o_part + static_cast<size_t>(splits) * rows_total * kPD;
+  hipLaunchKernelGGL(merge_kernel, dim3((rows_total + 7) / 8), dim3(256), 0, stream, o_part, ml_part,
+                     static_cast<uint16_t*>(out), rows_total, splits);
+  return launched();
+}
 
-extern "C" {
-
-lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
-                                 int32_t total_q, int32_t max_q_len, const void* k_pool, const void* v_pool,
-                                 int64_t num_blocks, const lazyattn_batch* batch, int32_t num_splits, void* out,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Validates and launches the prefill attention kernel; *splits_out = splits used.
+static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
+                                      int32_t total_q, int32_t max_q_len, const void* k_pool, const void* v_pool,
+                                      int64_t num_blocks, const lazyattn_batch* batch, int32_t num_splits, void* out,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream, int* splits_out) {
+  *splits_out = 1;
   lazyattn_status st = check_config(cfg);
   if (st != LAZYATTN_OK) return st;
   if ((st = check_batch(batch)) != LAZYATTN_OK) return st;
@@ -889,12 +960,11 @@ lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, cons
   const float scale = softmax_scale_of(cfg);
 
   if (cfg->dtype == LAZYATTN_F32) {
-    if (max_q_len > 65535 * 64) return LAZYATTN_EUNSUPPORTED;
+    if (max_q_len > 0x7fffffff || R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), cu_q_lens, static_cast<const float*>(k_pool),
                 static_cast<const float*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
                 cfg->alibi_slopes, static_cast<float*>(out), Hq, Hkv, G, cfg->head_dim, batch->max_entries,
                 cfg->pe, scale, rope};
-    if (R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     hipLaunchKernelGGL(attn_f32_kernel, dim3(max_q_len, R, Hq), dim3(64), 0, stream, a);
     return launched();
   }
@@ -907,14 +977,11 @@ lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, cons
   const long long gx = (max_q_len + m_q - 1) / m_q;
   const long long gz = static_cast<long long>(Hkv) * splits;
   if (R > 65535 || gz > 65535 || gx > 0x7fffffff) return LAZYATTN_EUNSUPPORTED;
-  if (splits > 1 && gx * R * Hkv > kMaxSplitTiles) return LAZYATTN_EUNSUPPORTED;
-  unsigned* counters = splits > 1 ? static_cast<unsigned*>(workspace) : nullptr;
-  float* o_part = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+  float* o_part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   float* ml_part = splits > 1 ? o_part + static_cast<size_t>(splits) * total_q * Hq * kPD : nullptr;
   PrefillArgs a{static_cast<const uint16_t*>(q), cu_q_lens, static_cast<const uint16_t*>(k_pool),
                 static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
-                cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, counters, Hq, Hkv, G,
-                batch->max_entries,
+                cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, Hq, Hkv, G, batch->max_entries,
                 total_q, m_q, prefill_entries_per_split(batch->max_entries, splits), splits, scale * kLog2e, rope};
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(gz));
   switch (cfg->pe) {
@@ -922,12 +989,15 @@ lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, cons
     case LAZYATTN_PE_NONE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_NONE>, grid, dim3(512), 0, stream, a); break;
     default: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ALIBI>, grid, dim3(512), 0, stream, a); break;
   }
+  *splits_out = splits;
   return launched();
 }
 
-lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const void* k_pool, const void* v_pool,
-                                int64_t num_blocks, const lazyattn_batch* batch, int32_t num_splits, void* out,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                     const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                     int32_t num_splits, void* out, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream, int* splits_out) {
+  *splits_out = 1;
   lazyattn_status st = check_config(cfg);
   if (st != LAZYATTN_OK) return st;
   if ((st = check_batch(batch)) != LAZYATTN_OK) return st;
@@ -939,11 +1009,11 @@ lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const
   const float scale = softmax_scale_of(cfg);
 
   if (cfg->dtype == LAZYATTN_F32) {
+    if (R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), nullptr, static_cast<const float*>(k_pool),
                 static_cast<const float*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
                 cfg->alibi_slopes, static_cast<float*>(out), Hq, Hkv, G, cfg->head_dim, batch->max_entries,
                 cfg->pe, scale, rope};
-    if (R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     hipLaunchKernelGGL(attn_f32_kernel, dim3(1, R, Hq), dim3(64), 0, stream, a);
     return launched();
   }
@@ -953,13 +1023,11 @@ lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const
   const size_t need = lazyattn_decode_workspace_size(cfg, R, batch->max_entries, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return LAZYATTN_EWORKSPACE;
   if (R > 65535 || Hkv > 65535) return LAZYATTN_EUNSUPPORTED;
-  if (splits > 1 && static_cast<long long>(R) * Hkv > kMaxSplitTiles) return LAZYATTN_EUNSUPPORTED;
-  unsigned* counters = splits > 1 ? static_cast<unsigned*>(workspace) : nullptr;
-  float* o_part = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+  float* o_part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   float* ml_part = splits > 1 ? o_part + static_cast<size_t>(splits) * R * Hq * kPD : nullptr;
   DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
-               cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, counters, R, Hq, Hkv, G,
+               cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, R, Hq, Hkv, G,
                batch->max_entries, decode_entries_per_split(batch->max_entries, splits), splits, scale * kLog2e,
                rope};
   const dim3 grid(splits, Hkv, R);
@@ -986,7 +1054,68 @@ lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const
     }
   }
 #undef LAZYATTN_DECODE
+  *splits_out = splits;
   return launched();
+}
+
+}  // namespace lazyattn
+
+using namespace lazyattn;
+
+extern "C" {
+
+lazyattn_status lazyattn_prefill_attend(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
+                                        int32_t total_q, int32_t max_q_len, const void* k_pool, const void* v_pool,
+                                        int64_t num_blocks, const lazyattn_batch* batch, int32_t num_splits,
+                                        void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int splits;
+  return prefill_attend(cfg, q, cu_q_lens, total_q, max_q_len, k_pool, v_pool, num_blocks, batch, num_splits, out,
+                        workspace, workspace_bytes, stream, &splits);
+}
+
+lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
+                                 int32_t total_q, int32_t max_q_len, const void* k_pool, const void* v_pool,
+                                 int64_t num_blocks, const lazyattn_batch* batch, int32_t num_splits, void* out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int splits;
+  lazyattn_status st = prefill_attend(cfg, q, cu_q_lens, total_q, max_q_len, k_pool, v_pool, num_blocks, batch,
+                                      num_splits, out, workspace, workspace_bytes, stream, &splits);
+  if (st != LAZYATTN_OK || splits <= 1) return st;
+  return merge_launch(total_q * cfg->num_q_heads, splits, workspace, out, stream);
+}
+
+lazyattn_status lazyattn_decode_attend(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                       const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                       int32_t num_splits, void* out, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  int splits;
+  return decode_attend(cfg, q, k_pool, v_pool, num_blocks, batch, num_splits, out, workspace, workspace_bytes,
+                       stream, &splits);
+}
+
+lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const void* k_pool, const void* v_pool,
+                                int64_t num_blocks, const lazyattn_batch* batch, int32_t num_splits, void* out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int splits;
+  lazyattn_status st = decode_attend(cfg, q, k_pool, v_pool, num_blocks, batch, num_splits, out, workspace,
+                                     workspace_bytes, stream, &splits);
+  if (st != LAZYATTN_OK || splits <= 1) return st;
+  return merge_launch(batch->num_reqs * cfg->num_q_heads, splits, workspace, out, stream);
+}
+
+lazyattn_status lazyattn_merge_splits(const lazyattn_config* cfg, int32_t num_rows, int32_t num_splits,
+                                      const void* workspace, size_t workspace_bytes, void* out, hipStream_t stream) {
+  lazyattn_status st = check_config(cfg);
+  if (st != LAZYATTN_OK) return st;
+  if (num_rows < 0 || num_splits < 1 || num_splits > 256) return LAZYATTN_EINVAL;
+  if (num_splits == 1 || num_rows == 0) return LAZYATTN_OK;
+  if (cfg->dtype != LAZYATTN_BF16) return LAZYATTN_EUNSUPPORTED;
+  if (!workspace || !out) return LAZYATTN_EINVAL;
+  const long long rows_total = static_cast<long long>(num_rows) * cfg->num_q_heads;
+  const size_t need = static_cast<size_t>(num_splits) * rows_total * (kPD + 2) * sizeof(float);
+  if (workspace_bytes < need) return LAZYATTN_EWORKSPACE;
+  if (rows_total > 0x7fffffffLL - 8) return LAZYATTN_EUNSUPPORTED;
+  return merge_launch(static_cast<int>(rows_total), num_splits, workspace, out, stream);
 }
 
 lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, void* v_pool, int64_t num_blocks,

@@ -91,15 +91,24 @@ class PrefillCall:
         self.max_q_len = int(inputs["max_q_len"])
         self.out = torch.empty_like(self.q)
         self.num_splits = num_splits
-        ws = _abi.prefill_workspace_size(cfg, len(inputs["ctx_lens"]), self.total_q, self.max_q_len,
-                                         self.tables.batch.max_entries, num_splits)
-        # zero-filled: the split-K arrival counters must start at zero
-        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=device) if ws > 0 else None
+        R = len(inputs["ctx_lens"])
+        self.splits = num_splits if num_splits > 0 else \
+            _abi.prefill_splits(cfg, R, self.max_q_len, self.tables.batch.max_entries)
+        ws = _abi.prefill_workspace_size(cfg, R, self.total_q, self.max_q_len, self.tables.batch.max_entries,
+                                         num_splits)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws > 0 else None
 
     def run(self, pools: DevicePools, stream=None):
         _abi.prefill(self.cfg, self.q, self.cu_q, self.total_q, self.max_q_len, pools.k, pools.v, pools.num_blocks,
                      self.tables.batch, self.out, self.workspace, self.num_splits, stream)
         return self.out
+
+    def attend(self, pools: DevicePools, stream=None):
+        _abi.prefill_attend(self.cfg, self.q, self.cu_q, self.total_q, self.max_q_len, pools.k, pools.v,
+                            pools.num_blocks, self.tables.batch, self.out, self.workspace, self.num_splits, stream)
+
+    def merge(self, stream=None):
+        _abi.merge_splits(self.cfg, self.total_q, self.splits, self.workspace, self.out, stream)
 
 
 class DecodeCall:
@@ -111,10 +120,19 @@ class DecodeCall:
         self.q = to_device(inputs["q"], spec.dtype, device)
         self.out = torch.empty_like(self.q)
         self.num_splits = num_splits
-        ws = _abi.decode_workspace_size(cfg, self.q.shape[0], self.tables.batch.max_entries, num_splits)
-        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=device) if ws > 0 else None
+        R = self.q.shape[0]
+        self.splits = num_splits if num_splits > 0 else _abi.decode_splits(cfg, R, self.tables.batch.max_entries)
+        ws = _abi.decode_workspace_size(cfg, R, self.tables.batch.max_entries, num_splits)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws > 0 else None
 
     def run(self, pools: DevicePools, stream=None):
         _abi.decode(self.cfg, self.q, pools.k, pools.v, pools.num_blocks, self.tables.batch, self.out,
                     self.workspace, self.num_splits, stream)
         return self.out
+
+    def attend(self, pools: DevicePools, stream=None):
+        _abi.decode_attend(self.cfg, self.q, pools.k, pools.v, pools.num_blocks, self.tables.batch, self.out,
+                           self.workspace, self.num_splits, stream)
+
+    def merge(self, stream=None):
+        _abi.merge_splits(self.cfg, self.q.shape[0], self.splits, self.workspace, self.out, stream)

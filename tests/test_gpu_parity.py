@@ -384,7 +384,7 @@ def test_edge_single_token_contexts_and_zero_length_queries():
 
 
 def test_split_workspace_reuse_across_calls_of_different_sizes():
-    say("one zero-filled workspace reused by split prefill and decode calls of different sizes")
+    say("one workspace reused by split prefill and decode calls of different sizes")
     wl = W.build_workload(W.spec(4, requests=[2], n_decode=1, q_len=100))
     s = wl.spec
     cfg = staging.config_for(s)
@@ -416,4 +416,32 @@ def test_split_workspace_reuse_across_calls_of_different_sizes():
                 out = gpu_f64(dc.out)
                 assert_parity(out, np.stack([ref_d[0], ref_d[1]]), "bf16", f"decode splits {kd}")
     sync()
-    assert int(ws[:65536 * 4].view(torch.int32).abs().sum().item()) == 0   # counters left at zero
+
+
+def test_attend_then_merge_equals_single_call():
+    say("attend + merge as two calls == one prefill call; decode likewise")
+    wl = W.build_workload(W.spec(2, requests=[3]))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    for k in (1, 3):
+        one = staging.PrefillCall(cfg, s, pb, DEV, num_splits=k)
+        two = staging.PrefillCall(cfg, s, pb, DEV, num_splits=k)
+        a = gpu_f64(one.run(pools))
+        two.attend(pools)
+        two.merge()
+        assert np.array_equal(a, gpu_f64(two.out))
+    wl2 = W.build_workload(W.spec(4, requests=[1], n_decode=1))
+    pools2 = staging.DevicePools(wl2, DEV)
+    staging.append_tokens(cfg, pools2, wl2.tokens_before_step(0), s.dtype, DEV)
+    d = wl2.decode_step(0)
+    staging.append_tokens(cfg, pools2, d, s.dtype, DEV)
+    cfg4 = staging.config_for(wl2.spec)
+    one = staging.DecodeCall(cfg4, wl2.spec, d, DEV, num_splits=9)
+    two = staging.DecodeCall(cfg4, wl2.spec, d, DEV, num_splits=9)
+    a = gpu_f64(one.run(pools2))
+    two.attend(pools2)
+    two.merge()
+    assert np.array_equal(a, gpu_f64(two.out))
