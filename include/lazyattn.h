@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LAZYATTN_ABI_VERSION 1
+#define LAZYATTN_ABI_VERSION 2
 
 typedef enum {
   LAZYATTN_OK = 0,
@@ -74,6 +74,13 @@ typedef enum { LAZYATTN_F32 = 0, LAZYATTN_BF16 = 1 } lazyattn_dtype;
  * encodings). */
 typedef enum { LAZYATTN_PE_ROPE = 0, LAZYATTN_PE_NONE = 1, LAZYATTN_PE_ALIBI = 2 } lazyattn_pe;
 
+/* Config flags.  EXACT_MAX: the bf16 prefill first computes every query
+ * row's exact score maximum over its keys (a scores-only pass) and uses it as
+ * the softmax reference, instead of taking the reference from the first key
+ * tile and redoing only when a later score outgrows it; same results up to
+ * rounding, for validation. */
+#define LAZYATTN_FLAG_EXACT_MAX 1
+
 typedef struct {
   int32_t num_q_heads;    /* Hq >= 1 */
   int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
@@ -83,7 +90,7 @@ typedef struct {
   int32_t pe;             /* lazyattn_pe */
   double rope_theta;      /* RoPE base (> 0 when pe == ROPE) */
   float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
-  int32_t reserved;       /* must be 0 */
+  int32_t flags;          /* LAZYATTN_FLAG_* bits; other bits must be 0 */
   const float* alibi_slopes;  /* device [Hq], or NULL => 2^(-8(h+1)/Hq) */
 } lazyattn_config;
 

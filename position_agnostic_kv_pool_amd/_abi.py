@@ -17,6 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblazyattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+FLAG_EXACT_MAX = 1          # LAZYATTN_FLAG_EXACT_MAX
 F32, BF16 = 0, 1
 PE_ROPE, PE_NONE, PE_ALIBI = 0, 1, 2
 _PE = {"rope": PE_ROPE, "none": PE_NONE, "alibi": PE_ALIBI}
@@ -39,7 +40,7 @@ class Config(ctypes.Structure):
         ("pe", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
         ("softmax_scale", ctypes.c_float),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
     ]
 
@@ -110,14 +111,14 @@ def _check(status: int, where: str):
 # ---------------------------------------------------------------------------
 def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str = "bf16", pe: str = "rope",
                 rope_theta: float = 10000.0, softmax_scale: float = 0.0, alibi_slopes=None,
-                block_size: int = 16) -> Config:
+                block_size: int = 16, exact_max: bool = False) -> Config:
     c = Config()
     c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size = num_q_heads, num_kv_heads, head_dim, block_size
     c.dtype = _DT[dtype] if isinstance(dtype, str) else int(dtype)
     c.pe = _PE[pe] if isinstance(pe, str) else int(pe)
     c.rope_theta = float(rope_theta)
     c.softmax_scale = float(softmax_scale)
-    c.reserved = 0
+    c.flags = FLAG_EXACT_MAX if exact_max else 0
     c.alibi_slopes = _ptr(alibi_slopes) if alibi_slopes is not None else None
     c._keep = alibi_slopes
     return c

@@ -15,7 +15,7 @@ lazyattn_status check_config(const lazyattn_config* cfg) {
   if (!cfg) return LAZYATTN_EINVAL;
   if (cfg->num_q_heads < 1 || cfg->num_kv_heads < 1) return LAZYATTN_EINVAL;
   if (cfg->num_q_heads % cfg->num_kv_heads != 0) return LAZYATTN_EINVAL;
-  if (cfg->reserved != 0) return LAZYATTN_EINVAL;
+  if ((cfg->flags & ~LAZYATTN_FLAG_EXACT_MAX) != 0) return LAZYATTN_EINVAL;
   if (cfg->dtype != LAZYATTN_F32 && cfg->dtype != LAZYATTN_BF16) return LAZYATTN_EINVAL;
   if (cfg->pe != LAZYATTN_PE_ROPE && cfg->pe != LAZYATTN_PE_NONE && cfg->pe != LAZYATTN_PE_ALIBI)
     return LAZYATTN_EINVAL;

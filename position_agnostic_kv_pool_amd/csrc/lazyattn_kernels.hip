@@ -21,6 +21,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lazyattn_common.hpp"
 
 namespace lazyattn {
@@ -99,30 +101,57 @@ __device__ __forceinline__ f32x4 mfma16x16x16(const s16x4& a, const s16x4& b, co
 // ---------------------------------------------------------------------------
 // Prefill, bf16, MFMA.
 //
-// Work-group = 8 waves = 256 query rows: the G heads of one KV group at
-// m_q = 256 / G consecutive positions (row rho -> position rho / G, head
-// rho % G).  Each wave owns 32 rows as two 16-row tiles.  A key tile is four
-// table entries (64 key slots).  Per tile:
-//   S^T (keys x rows) = K~ (keys x D) . Q~^T          16x16x32 MFMA, K~ from LDS
-//   online softmax over the keys of each row (base 2, scale folded into Q~)
-//   O^T (D x rows)   += V^T (D x keys) . P^T         16x16x32 MFMA, V^T from LDS
-// The S^T accumulator leaves each lane with 4 consecutive keys of one row,
-// which is exactly a P^T operand slice, so P never leaves registers.  A ninth
-// O tile multiplies P by a row of ones, so the softmax denominator is the sum
-// of exactly the bf16 weights that enter P.V, at no vector-ALU cost.
+// Work-group = 8 waves (two per SIMD) = 256 query rows: the G heads of one
+// KV group at m_q = 256 / G consecutive positions (row rho -> position
+// rho / G, head rho % G).  Each wave owns 32 rows, one 32-column MFMA tile.
+// A key tile is four table entries (64 key slots).  Per tile and wave:
+//   S^T (keys x rows) = K~ (keys x D) . Q~^T       16  32x32x16 MFMA
+//   P = 2^(S - m), rounded to bf16                 (base 2, scale folded into Q~)
+//   O^T (D x rows)   += V^T (D x keys) . P^T       16  32x32x16 MFMA
+// plus 4 MFMAs of a ones matrix by P^T, whose every row is the sum of exactly
+// the bf16 weights that enter P.V (the softmax denominator).
 //
-// Schedule.  Key tile j is staged (rotated K, transposed V) into one of two
-// LDS buffers by all 512 threads; K runs two tiles ahead of its use and V
-// one, with global loads one iteration ahead of staging and a single barrier
-// per iteration.  Each tile's entries (block, start, length) are decoded once
-// into a small LDS ring by wave 0, one iteration ahead of their first use.
-// The two waves sharing a SIMD (w and w+4) run the same iteration in opposite
-// phase order, so one's MFMA work overlaps the other's vector work:
-//   waves 0-3:  [QK(i+1), PV(i)]  [softmax(i+1)]  [staging]
-//   waves 4-7:  [softmax(i)]  [staging]  [PV(i), QK(i+1)]
-// With the key range split, each split writes unnormalised (o, m, l) and the
-// merge kernel combines them.
+// Key order.  Within a 32-key half (tau) of the tile, S^T row i holds the key
+// that `krow_of` maps to it, chosen so that the accumulator leaves each lane,
+// for its query column, keys 8h..8h+7 of two consecutive entries
+// (h = lane / 32) in register order.  Those eight weights are exactly a P^T
+// operand slice, so P never leaves registers, and the matching V^T operand
+// is 8 consecutive keys of one channel: 16 bytes of the pool's own
+// channel-major block layout, copied to LDS unchanged.
+//
+// Reference maximum.  Scores are formed relative to a fixed per-row
+// reference m that enters the QK chain as the MFMA's initial accumulator
+// (-m): the exact maximum of the row over the work-group's first key tile.
+// Numerator and denominator share it, so the result is exact whatever m is,
+// as long as 2^(s - m) stays finite; a row sum above 2^64 flags the rare case
+// where a later score outgrew m by that much, and the work-group then redoes
+// its rows with m set to the exact row maximum over all its keys (one QK-only
+// pass first).  ALiBi, whose bias grows toward the diagonal, always takes
+// that two-pass route.
+//
+// Staging.  Wave w stages rows 8 (w % 2) .. + 7 of entry w / 2 of the next
+// tile: lane l loads channel pair l of those 8 key rows (4 B each) and
+// 2 x 16 B of V one iteration ahead, rotates the keys by R(t - p0) (phase
+// R(start - p0 + row) stepped by R(1) per row) between the QK products, and
+// writes K~ and V into the other LDS buffer.  One barrier per tile.  Table words are fetched three tiles ahead
+// and decoded per wave with lane reads.  With the key range split, each
+// split writes unnormalised (o, m, l) and the merge kernel combines them.
 // ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// e^{i n f} with f = 2 pi rev, the angle reduced to a fraction of a turn in
+// double; the hardware sine/cosine take their argument in turns.
+__device__ __forceinline__ float2 unit_phase_turns(int n, double rev) {
+  double x = static_cast<double>(n) * rev;
+  x -= floor(x);
+  const float t = static_cast<float>(x);
+  return make_float2(__builtin_amdgcn_cosf(t), __builtin_amdgcn_sinf(t));
+}
+
 struct PrefillArgs {
   const uint16_t* q;
   const int32_t* cu_q;
@@ -136,30 +165,32 @@ struct PrefillArgs {
   float* o_part;
   float* ml_part;
   int32_t Hq, Hkv, G, max_entries, total_q, m_q, eps, splits;
+  int32_t exact;                 // nonzero: always take the two-pass exact-maximum route
   float scale_log2;
   RopeRev rope;
 };
 
-constexpr int kPD = 128;        // head dim of the bf16 kernels
-constexpr int kKS = kPD + 8;    // K tile row stride in bf16 (272 B: conflict-free 16-lane reads)
-constexpr int kVS = 40;         // V tile row stride in bf16 (80 B: conflict-free 16-lane reads)
-constexpr int kBS = 10;         // phase chunk stride in float2 (80 B: conflict-free reads)
-constexpr float kRescaleSlack = 8.0f;   // running max is raised only when it grows by more than 2^8
+constexpr int kPD = 128;                 // head dim of the bf16 kernels
+constexpr int kPrefillThreads = 512;    // threads per prefill work-group
+constexpr int kKS = kPD + 8;             // K~ row stride in bf16 (272 B: conflict-free 16 B reads)
+constexpr int kVE = kPD * kBlock;        // one entry of V, channel-major [D][16], in bf16
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64: larger row sums redo with the exact maximum
+
+// LDS row of tile-local key (entry E, row rho) in the K~ buffer (S^T row order)
+__device__ __forceinline__ int krow_of(int E, int rho) {
+  return 16 * E + 8 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
+}
 
 template <int PE>
-__global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs A) {
+__global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const PrefillArgs A) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][2 * kPD * kVS];
-  __shared__ __attribute__((aligned(16))) float2 base_s[2][4][8][kBS];
-  __shared__ __attribute__((aligned(16))) float2 rtab[16][8][kBS];
-  __shared__ __attribute__((aligned(16))) float2 r16tab[16][64];
-  __shared__ __attribute__((aligned(16))) int4 tinfo[8][4];   // (block, start, length, 0) per entry
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][4 * kVE];
+  __shared__ int redo_s;
 
   const int tid = threadIdx.x;
-  // the wave index stays a vector value: as a scalar it turns the phase-order
-  // test below into a uniform branch, and register allocation across it spills
-  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
-  const int grp = (wave >> 2) & 1;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int ws = __builtin_amdgcn_readfirstlane(wave);
+  const int c = lane & 31, h = lane >> 5;
   const int qt = blockIdx.x, r = blockIdx.y;
   const int kvh = blockIdx.z % A.Hkv, split = blockIdx.z / A.Hkv;
   const int q0 = A.cu_q[r];
@@ -204,332 +235,334 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs A) 
   }
   const int T = (e_stop - e_begin + 3) >> 2;          // key tiles of this work-group
 
-  // ---- tile metadata: wave 0, lane x handles entry x of a tile ------------------
-  const uint64_t sentinel = static_cast<uint64_t>(static_cast<uint32_t>(L)) << 32;   // start = L
-  auto fetch_words = [&](int j, int x, uint64_t& w, uint64_t& wn) {
-    const int e = e_begin + 4 * j + x;
-    w = wn = sentinel;
-    if (e < e_stop) {
-      w = trow[e];
-      wn = (e + 1 < ne) ? trow[e + 1] : sentinel;
-    }
-  };
-  auto write_info = [&](int j, int x, uint64_t w, uint64_t wn) {
-    const int e = e_begin + 4 * j + x;
-    const int st = static_cast<int>(word_start(w));
-    tinfo[j & 7][x] = (e < e_stop) ? make_int4(static_cast<int>(word_block(w)), st,
-                                               static_cast<int>(word_start(wn)) - st, 0)
-                                   : make_int4(0, 0, 0, 0);
-  };
-
-  // ---- rows owned by this lane, and the raw query fragments ----------------
-  int p_row[2], tok[2], head[2], mrow[2];
-  bool row_ok[2];
-  float slope[2];
-  uint4 qraw[2][4];
-  bf16x8 qf[2][4];
+  // ---- this lane's query row: column c of the wave's 32-row tile -------------------
+  constexpr int NT = 1;
+  int p_row[NT], tok[NT], head[NT];
+  bool row_ok[NT];
+  float slope[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int rho = wave * 32 + nt * 16 + n;
-    const int m = rho / G, gh = rho - m * G;
-    mrow[nt] = m;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int rho = 32 * wave + 32 * nt + c;
+    const int m = rho / G;
     row_ok[nt] = m < mq;
     p_row[nt] = p0 + m;
     tok[nt] = q0 + m0 + m;
-    head[nt] = kvh * G + gh;
+    head[nt] = kvh * G + (rho - m * G);
     slope[nt] = (PE == LAZYATTN_PE_ALIBI) ? alibi_slope(A.alibi, head[nt], Hq) * kLog2e : 0.0f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qraw[nt][s] = make_uint4(0, 0, 0, 0);
-      if (row_ok[nt])
-        qraw[nt][s] = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(tok[nt]) * Hq + head[nt]) * kPD +
-                                                      32 * s + 8 * g);
-    }
   }
 
-  // staging roles: thread -> (entry se, key row sr, channel pairs 8sc..8sc+7) for K,
-  //                thread -> (entry se, channel sd) for V; se is uniform per wave
-  const int se = __builtin_amdgcn_readfirstlane(tid >> 7), sr = (tid >> 3) & 15, sc = tid & 7, sd = tid & 127;
+  // ---- table words: lanes x = 0..4 (mod 8) hold word e0 + x of a tile ------------
+  const uint64_t sentinel = static_cast<uint64_t>(static_cast<uint32_t>(L)) << 32;   // start = L
+  auto load_words = [&](int j) -> uint64_t {
+    const int x = lane & 7;
+    const int e = e_begin + 4 * j + x;
+    const uint64_t w = trow[min(e, ne - 1)];
+    return (x < 5 && e < ne) ? w : sentinel;
+  };
+  // entry x of the tile whose words are in wv: (block, start, length); past the
+  // split's last entry the length is 0 and the start L
+  auto entry_of = [&](uint64_t wv, int j, int x, int& blk, int& st, int& ln) {
+    const uint32_t lo_w = static_cast<uint32_t>(wv), hi_w = static_cast<uint32_t>(wv >> 32);
+    const int b = __builtin_amdgcn_readlane(static_cast<int>(lo_w), x);
+    const int s0 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x);
+    const int s1 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x + 1);
+    const bool valid = e_begin + 4 * j + x < e_stop;
+    blk = valid ? b : 0;
+    st = valid ? s0 : L;
+    ln = valid ? s1 - s0 : 0;
+  };
 
-  f32x4 O[9][2];
+  // ---- staging: wave w handles rows 8 part .. 8 part + 7 of entry E = w / 2 --------
+  // K: lane l holds channel pair l of the 8 key rows (4 B each); V: lane l holds
+  // keys 8 (l % 2) .. + 7 of channels 64 part + 32 cc + l / 2, cc = 0, 1
+  const int E_own = ws >> 1, part = ws & 1;
+  float2 r1 = make_float2(1.f, 0.f);               // R(1) at this lane's pair
+  if (PE == LAZYATTN_PE_ROPE) r1 = unit_phase(1, A.rope.rev[lane]);
+  uint32_t kr[8];
+  uint4 vr[2];
+  // entries past the split's end (length 0) read block 0: their keys are
+  // masked out of the scores and their V rows zeroed when staged
+  auto load_kv = [&](int blk) {
+    const size_t base = static_cast<size_t>(static_cast<uint32_t>(blk)) * Hkv + kvh;
+    const uint32_t* kp = reinterpret_cast<const uint32_t*>(A.kpool + base * (kBlock * kPD) + 8 * part * kPD) + lane;
+    const uint16_t* vp = A.vpool + base * (kPD * kBlock) + (64 * part + (lane >> 1)) * kBlock + 8 * (lane & 1);
 #pragma unroll
-  for (int dt = 0; dt < 9; ++dt) O[dt][0] = O[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {kNegInf, kNegInf};
-  // A operand of the ones tile: row 0 of the 16-row slab is all ones
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, n == 0 ? make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u)
-                                                         : make_uint4(0u, 0u, 0u, 0u));
+    for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) vr[cc] = *reinterpret_cast<const uint4*>(vp + 32 * cc * kBlock);
+  };
+  // zero V rows past the entry's length (their weights are 0, but the pool's
+  // padding may hold anything)
+  auto mask_v = [&](int ln) {
+    const int k0 = 8 * (lane & 1);
+    uint32_t keep[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      keep[k] = ((k0 + 2 * k < ln) ? 0xffffu : 0u) | ((k0 + 2 * k + 1 < ln) ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      vr[cc] = make_uint4(vr[cc].x & keep[0], vr[cc].y & keep[1], vr[cc].z & keep[2], vr[cc].w & keep[3]);
+  };
+  // write the staged K~ and V into LDS buffer b
+  auto stage_write = [&](int b) {
+    uint32_t* kdst = reinterpret_cast<uint32_t*>(Ks[b]) + lane;
+    uint16_t* vdst = Vs[b] + E_own * kVE;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) kdst[krow_of(E_own, 8 * part + k) * (kKS / 2)] = kr[k];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      *reinterpret_cast<uint4*>(&vdst[(64 * part + 32 * cc + (lane >> 1)) * kBlock + 8 * (lane & 1)]) = vr[cc];
+  };
 
-  // ---- helpers ---------------------------------------------------------------
-  uint4 kr0 = make_uint4(0, 0, 0, 0), kr1 = kr0, vr0 = kr0, vr1 = kr0;
-  auto load_k = [&](int j, uint4& a, uint4& b) {
-    const int4 inf = tinfo[j & 7][se];
-    if (inf.z > 0) {
-      const uint4* kp = reinterpret_cast<const uint4*>(
-          A.kpool + (static_cast<size_t>(static_cast<uint32_t>(inf.x)) * Hkv + kvh) * (kBlock * kPD) + sr * kPD + 16 * sc);
-      a = kp[0];
-      b = kp[1];
-    }
-  };
-  auto load_v = [&](int j) {
-    const int4 inf = tinfo[j & 7][se];
-    if (inf.z > 0) {
-      const uint4* vp = reinterpret_cast<const uint4*>(
-          A.vpool + (static_cast<size_t>(static_cast<uint32_t>(inf.x)) * Hkv + kvh) * (kPD * kBlock) + sd * kBlock);
-      vr0 = vp[0];
-      vr1 = vp[1];
-    }
-  };
-  // phase R(start_e - p0) of each entry e and channel pair, for tile j
-  auto compute_base = [&](int j) {
-    if (PE == LAZYATTN_PE_ROPE && tid < 256) {
-      const int e = __builtin_amdgcn_readfirstlane(tid >> 6), pr = tid & 63;
-      const int4 inf = tinfo[j & 7][e];
-      const float2 ph = inf.z > 0 ? unit_phase(inf.y - p0, A.rope.rev[pr]) : make_float2(1.f, 0.f);
-      base_s[j & 1][e][pr >> 3][pr & 7] = ph;
-    }
-  };
-  // rotate this thread's K slice of tile j by R(start - p0 + sr) and store it
-  auto stage_k = [&](int j, const uint4& a, const uint4& b) {
-    const int len = tinfo[j & 7][se].z;
-    uint32_t kw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    if (sr >= len) {
+  // ---- query: rotated by R(m), scaled by scale*log2(e), rounded to bf16 -----------
+  // B operand of k-step kk: channels 16 kk + 8 h .. + 7 of the row
+  bf16x8 qf[8 * NT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kw[i] = 0;
-    } else if (PE == LAZYATTN_PE_ROPE) {
-      const float2* bp = base_s[j & 1][se][sc];
-      const float2* rp = rtab[sr][sc];
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kw[i] = rotate_pair(kw[i], cmul(bp[i], rp[i]));
-    }
-    uint4* kd = reinterpret_cast<uint4*>(&Ks[j & 1][(16 * se + sr) * kKS + 16 * sc]);
-    kd[0] = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-    kd[1] = make_uint4(kw[4], kw[5], kw[6], kw[7]);
-  };
-  // channel sd of entry se, keys 4gg..4gg+3 -> Vs[.][se/2][sd][gg*8 + (se&1)*4 ..]
-  auto stage_v = [&](int j) {
-    const int len = tinfo[j & 7][se].z;
-    uint32_t vw[8] = {vr0.x, vr0.y, vr0.z, vr0.w, vr1.x, vr1.y, vr1.z, vr1.w};
-    if (len < kBlock) {
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (row_ok[nt])
+        raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(tok[nt]) * Hq + head[nt]) * kPD + 16 * kk +
+                                              8 * h);
+      uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo16 = (2 * i < len) ? (vw[i] & 0xffffu) : 0u;
-        const uint32_t hi16 = (2 * i + 1 < len) ? (vw[i] & 0xffff0000u) : 0u;
-        vw[i] = lo16 | hi16;
-      }
-    }
-    uint16_t* vrow = &Vs[j & 1][((se >> 1) * kPD + sd) * kVS + (se & 1) * 4];
-#pragma unroll
-    for (int gg = 0; gg < 4; ++gg)
-      *reinterpret_cast<uint2*>(vrow + gg * 8) = make_uint2(vw[2 * gg], vw[2 * gg + 1]);
-  };
-  auto qk = [&](int j, f32x4 (&S)[4][2]) {
-    const uint16_t* kb = Ks[j & 1];
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      S[tau][0] = S[tau][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[(16 * tau + n) * kKS + 32 * s + 8 * g]);
-        S[tau][0] = mfma16x16x32(a, qf[0][s], S[tau][0]);
-        S[tau][1] = mfma16x16x32(a, qf[1][s], S[tau][1]);
-      }
-    }
-  };
-  auto pv = [&](int j, const uint32_t (&pk)[4][2][2]) {
-    const uint16_t* vb = Vs[j & 1];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, make_uint4(pk[2 * u][0][0], pk[2 * u][0][1], pk[2 * u + 1][0][0], pk[2 * u + 1][0][1]));
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, make_uint4(pk[2 * u][1][0], pk[2 * u][1][1], pk[2 * u + 1][1][0], pk[2 * u + 1][1][1]));
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vb[(u * kPD + 16 * dt + n) * kVS + 8 * g]);
-        O[dt][0] = mfma16x16x32(a, b0, O[dt][0]);
-        O[dt][1] = mfma16x16x32(a, b1, O[dt][1]);
-      }
-      O[8][0] = mfma16x16x32(ones, b0, O[8][0]);
-      O[8][1] = mfma16x16x32(ones, b1, O[8][1]);
-    }
-  };
-  // scores of tile j -> bf16 weights; raises the running maxima (rescaling O) when needed
-  auto softmax = [&](int j, f32x4 (&S)[4][2], uint32_t (&pk)[4][2][2]) {
-    int t_start[4], t_len[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int4 inf = tinfo[j & 7][i];
-      t_start[i] = __builtin_amdgcn_readfirstlane(inf.y);
-      t_len[i] = __builtin_amdgcn_readfirstlane(inf.z);
-    }
-    const bool full = (t_len[0] == kBlock) && (t_len[1] == kBlock) && (t_len[2] == kBlock) &&
-                      (t_len[3] == kBlock) && (t_start[3] + kBlock - 1 <= p0);
-    if (!full || PE == LAZYATTN_PE_ALIBI) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int kr = 4 * g + jj;
-            const int t = t_start[tau] + kr;
-            float v = S[tau][nt][jj];
-            if (PE == LAZYATTN_PE_ALIBI) v -= slope[nt] * static_cast<float>(p_row[nt] - t);
-            if (!full) v = ((kr < t_len[tau]) && (t <= p_row[nt])) ? v : kNegInf;
-            S[tau][nt][jj] = v;
-          }
-    }
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mx = fmaxf(fmaxf(fmaxf(S[0][nt][0], S[0][nt][1]), fmaxf(S[0][nt][2], S[0][nt][3])),
-                       fmaxf(fmaxf(S[1][nt][0], S[1][nt][1]), fmaxf(S[1][nt][2], S[1][nt][3])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(S[2][nt][0], S[2][nt][1]), fmaxf(S[2][nt][2], S[2][nt][3])),
-                           fmaxf(fmaxf(S[3][nt][0], S[3][nt][1]), fmaxf(S[3][nt][2], S[3][nt][3]))));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // raise the reference maximum only when the row's scores outgrow it by 2^8;
-      // exact: numerator and denominator share the reference
-      const bool raise = mx > m_run[nt] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float m_new = raise ? mx : m_run[nt];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);   // 0 when m_run = -inf
-#pragma unroll
-        for (int dt = 0; dt < 9; ++dt) O[dt][nt] *= alpha;
-        m_run[nt] = m_new;
-      }
-      const float m_use = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        const float e0 = __builtin_amdgcn_exp2f(S[tau][nt][0] - m_use);
-        const float e1 = __builtin_amdgcn_exp2f(S[tau][nt][1] - m_use);
-        const float e2 = __builtin_amdgcn_exp2f(S[tau][nt][2] - m_use);
-        const float e3 = __builtin_amdgcn_exp2f(S[tau][nt][3] - m_use);
-        pk[tau][nt][0] = pack_bf16x2(e0, e1);
-        pk[tau][nt][1] = pack_bf16x2(e2, e3);
-      }
-    }
-  };
-  // query rows rotated by R(m) = R(16 (m / 16)) R(m % 16), scaled by scale*log2(e), rounded to bf16
-  auto rotate_q = [&]() {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 raw = qraw[nt][s];
-        uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
-          if (PE == LAZYATTN_PE_ROPE) {
-            const int pr = 16 * s + 4 * g + jj, m = mrow[nt] & 255;
-            const float2 ph = cmul(r16tab[m >> 4][pr], rtab[m & 15][pr >> 3][pr & 7]);
-            const float y0 = x0 * ph.x - x1 * ph.y;
-            const float y1 = x0 * ph.y + x1 * ph.x;
-            x0 = y0;
-            x1 = y1;
-          }
-          w4[jj] = pack_bf16x2(x0 * A.scale_log2, x1 * A.scale_log2);
+      for (int jj = 0; jj < 4; ++jj) {
+        float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
+        if (PE == LAZYATTN_PE_ROPE) {
+          const float2 ph = unit_phase_turns(p_row[nt] - p0, A.rope.rev[8 * kk + 4 * h + jj]);
+          const float y0 = x0 * ph.x - x1 * ph.y;
+          const float y1 = x0 * ph.y + x1 * ph.x;
+          x0 = y0;
+          x1 = y1;
         }
-        qf[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        w4[jj] = pack_bf16x2(x0 * A.scale_log2, x1 * A.scale_log2);
       }
-  };
+      qf[8 * nt + kk] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+    }
 
-  // ---- pipeline ------------------------------------------------------------------
-  if (T > 0) {
-    // P0: tile metadata for tiles 0..3 (wave 0) and the rotation tables
-    if (tid < 16) {
-      uint64_t w, wn;
-      fetch_words(tid >> 2, tid & 3, w, wn);
-      write_info(tid >> 2, tid & 3, w, wn);
-    }
-    if (PE == LAZYATTN_PE_ROPE) {
-      for (int i = tid; i < 16 * 64; i += 512) {
-        rtab[i >> 6][(i & 63) >> 3][i & 7] = unit_phase(i >> 6, A.rope.rev[i & 63]);
-        r16tab[i >> 6][i & 63] = unit_phase(16 * (i >> 6), A.rope.rev[i & 63]);
+  f32x16 O[4][NT], O1[NT];
+  float m_ref[NT] = {0.f};                           // reference per row (raw score units)
+  f32x16 negm[NT];
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+
+  // One pass over the key tiles.  maxpass: scores only, folded into the exact
+  // row maximum mx[].  Otherwise P.V with the reference m_ref (taken from the
+  // first tile when `fresh`).
+  float mx[NT] = {kNegInf};
+  auto pass = [&](const bool maxpass, const bool fresh) __attribute__((always_inline)) {
+    uint64_t wv0 = load_words(0), wv1 = load_words(1), wv2 = load_words(2);
+    {
+      int blk, st, ln;
+      entry_of(wv0, 0, E_own, blk, st, ln);
+      load_kv(blk);
+      if (PE == LAZYATTN_PE_ROPE) {
+        float2 ph = unit_phase_turns(st - p0 + 8 * part, A.rope.rev[lane]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          kr[k] = rotate_pair(kr[k], ph);
+          ph = cmul(ph, r1);
+        }
       }
+      mask_v(ln);
+      stage_write(0);
+      entry_of(wv1, 1, E_own, blk, st, ln);
+      load_kv(blk);
     }
-    __syncthreads();
-    // P1: phases of tiles 0 and 1, first loads, metadata words of tile 4
-    uint64_t pw = sentinel, pwn = sentinel;          // tile metadata one iteration ahead (wave 0)
-    compute_base(0);
-    compute_base(1);
-    uint4 ka0 = kr0, ka1 = kr0;
-    load_k(0, ka0, ka1);
-    load_k(1, kr0, kr1);
-    load_v(0);
-    if (tid < 4) fetch_words(4, tid, pw, pwn);
-    __syncthreads();
-    // P2: query rotation, staging of K(0), K(1), V(0); loads of K(2), V(1)
-    rotate_q();
-    stage_k(0, ka0, ka1);
-    stage_k(1, kr0, kr1);
-    stage_v(0);
-    load_k(2, kr0, kr1);
-    load_v(1);
-    __syncthreads();
-    // P3: phases of tile 2, first scores
-    compute_base(2);
-    f32x4 S[4][2];
-    uint32_t pk[4][2][2];
-    qk(0, S);
-    if (grp == 0) softmax(0, S, pk);
     __syncthreads();
     for (int i = 0; i < T; ++i) {
-      const bool nxt = i + 1 < T;
-      if (grp == 0) {
-        if (nxt) qk(i + 1, S);
-        pv(i, pk);
-        if (nxt) softmax(i + 1, S, pk);
-      } else {
-        softmax(i, S, pk);
+      // stage tile i + 1 (loaded during the previous iteration) between the
+      // products that form S for tile i; buffer (i + 1) & 1 is free since the
+      // barrier that ended iteration i - 1
+      int nblk, nst, nln;
+      entry_of(wv1, i + 1, E_own, nblk, nst, nln);
+      const uint16_t* kb = Ks[i & 1];
+      f32x16 S[2][NT];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) S[tau][nt] = negm[nt];
+      float2 ph = make_float2(1.f, 0.f);
+      if (PE == LAZYATTN_PE_ROPE) ph = unit_phase_turns(nst - p0 + 8 * part, A.rope.rev[lane]);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[(32 * tau + c) * kKS + 16 * kk + 8 * h]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) S[tau][nt] = mfma32x32x16(a, qf[8 * nt + kk], S[tau][nt]);
+        }
+        if (PE == LAZYATTN_PE_ROPE) {
+          kr[kk] = rotate_pair(kr[kk], ph);
+          ph = cmul(ph, r1);
+        }
+        if (kk == 3) mask_v(nln);
       }
-      if (i + 2 < T) stage_k(i + 2, kr0, kr1);
-      if (nxt) stage_v(i + 1);
-      if (i + 3 < T) {
-        load_k(i + 3, kr0, kr1);
-        compute_base(i + 3);
+      stage_write((i + 1) & 1);
+      // loads of tile i + 2, words of tile i + 3
+      int lblk, lst, lln;
+      entry_of(wv2, i + 2, E_own, lblk, lst, lln);
+      load_kv(lblk);
+      const uint64_t wv3 = load_words(i + 3);
+
+      int st[4], ln[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        int b_unused;
+        entry_of(wv0, i, x, b_unused, st[x], ln[x]);
       }
-      if (i + 2 < T) load_v(i + 2);
-      if (tid < 4) {
-        write_info(i + 4, tid, pw, pwn);
-        fetch_words(i + 5, tid, pw, pwn);
+      const bool full = (ln[0] == kBlock) && (ln[1] == kBlock) && (ln[2] == kBlock) && (ln[3] == kBlock) &&
+                        (st[3] + kBlock - 1 <= p0);
+      // register r of half tau: key row 8 h + (r % 8) of entry 2 tau + r / 8
+      if (PE == LAZYATTN_PE_ALIBI) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const int t = st[2 * tau + (rr >> 3)] + 8 * h + (rr & 7);
+              S[tau][nt][rr] -= slope[nt] * static_cast<float>(p_row[nt] - t);
+            }
       }
-      if (grp == 1) {
-        pv(i, pk);
-        if (nxt) qk(i + 1, S);
+      if (!full) {
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int E = 2 * tau + (rr >> 3), kr_ = 8 * h + (rr & 7);
+            const int t = st[E] + kr_;
+            const bool live = kr_ < ln[E];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) S[tau][nt][rr] = (live && t <= p_row[nt]) ? S[tau][nt][rr] : kNegInf;
+          }
       }
+      if (maxpass || (fresh && i == 0)) {
+        // row maximum of this tile (lanes c and c + 32 hold the two key halves)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          float lm = kNegInf;
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int rr = 0; rr < 16; rr += 2) lm = fmaxf(lm, fmaxf(S[tau][nt][rr], S[tau][nt][rr + 1]));
+          lm = fmaxf(lm, __shfl_xor(lm, 32));
+          if (maxpass) {
+            mx[nt] = fmaxf(mx[nt], lm);
+          } else {
+            const float mr = (lm == kNegInf) ? 0.f : lm;      // a fully masked row keeps reference 0
+            m_ref[nt] = mr;
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) S[tau][nt] -= mr;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) negm[nt][rr] = -mr;
+          }
+        }
+      }
+      if (!maxpass) {
+        // P^T operands (weights of keys 8 h .. 8 h + 7 of entry 2 tau + ks) and
+        // O^T += V^T P^T, V of entry E read in the pool's channel-major layout;
+        // the exponentials of one entry overlap the products of the previous
+        const uint16_t* vb = Vs[i & 1];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int E = 2 * tau + ks;
+            bf16x8 Pk[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              uint32_t pw[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                pw[k] = pack_bf16x2(__builtin_amdgcn_exp2f(S[tau][nt][8 * ks + 2 * k]),
+                                    __builtin_amdgcn_exp2f(S[tau][nt][8 * ks + 2 * k + 1]));
+              Pk[nt] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vb[E * kVE + (32 * dt + c) * kBlock + 8 * h]);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma32x32x16(a, Pk[nt], O[dt][nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) O1[nt] = mfma32x32x16(ones, Pk[nt], O1[nt]);
+          }
+      }
+      wv0 = wv1;
+      wv1 = wv2;
+      wv2 = wv3;
       __syncthreads();
     }
+  };
+
+  auto clear_acc = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[dt][nt] = f32x16{};
+      O1[nt] = f32x16{};
+      negm[nt] = f32x16{};
+    }
+  };
+  clear_acc();
+  bool two_pass = (PE == LAZYATTN_PE_ALIBI) || (A.exact != 0);
+  if (T > 0 && !two_pass) {
+    pass(false, true);
+    // a row sum this large means some score outgrew the first tile's maximum:
+    // redo the work-group with the exact maximum
+    bool bad = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bad = bad || (row_ok[nt] && !(O1[nt][0] < kSumLimit));
+    if (tid == 0) redo_s = 0;
+    __syncthreads();
+    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo_s = 1;
+    __syncthreads();
+    two_pass = redo_s != 0;
+  }
+  if (T > 0 && two_pass) {
+    clear_acc();                                     // scores of the max pass are raw (reference 0)
+    pass(true, false);
+    clear_acc();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      m_ref[nt] = (mx[nt] == kNegInf) ? 0.f : mx[nt];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) negm[nt][rr] = -m_ref[nt];
+    }
+    pass(false, false);
   }
 
-  // ---- epilogue ------------------------------------------------------------------
-  // row sums: the ones tile holds them in register 0 of the lanes with g == 0
-  float lt[2];
+  // ---- epilogue ----------------------------------------------------------------
+  // every row of the ones tile holds the row sum; O register r: channel
+  // 32 dt + 8 (r / 4) + 4 h + r % 4
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    lt[nt] = O[8][nt][0] + __shfl_xor(O[8][nt][0], 16);
-    lt[nt] += __shfl_xor(lt[nt], 32);
-  }
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lt = O1[nt][0];
     if (!row_ok[nt]) continue;
     const size_t rowoff = static_cast<size_t>(tok[nt]) * Hq + head[nt];
     if (A.splits == 1) {
-      const float inv = 1.0f / lt[nt];
+      const float inv = 1.0f / lt;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 o = O[dt][nt];
-        *reinterpret_cast<uint2*>(A.out + rowoff * kPD + 16 * dt + 4 * g) =
-            make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
-      }
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          *reinterpret_cast<uint2*>(A.out + rowoff * kPD + 32 * dt + 8 * qq + 4 * h) =
+              make_uint2(pack_bf16x2(O[dt][nt][4 * qq] * inv, O[dt][nt][4 * qq + 1] * inv),
+                         pack_bf16x2(O[dt][nt][4 * qq + 2] * inv, O[dt][nt][4 * qq + 3] * inv));
     } else {
       // this split's unnormalised output, reference maximum and sum
       const size_t prow = static_cast<size_t>(split) * A.total_q * Hq + rowoff;
-      if (lt[nt] > 0.f) {
+      if (lt > 0.f) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          *reinterpret_cast<f32x4*>(A.o_part + prow * kPD + 16 * dt + 4 * g) = O[dt][nt];
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq)
+            *reinterpret_cast<f32x4*>(A.o_part + prow * kPD + 32 * dt + 8 * qq + 4 * h) =
+                f32x4{O[dt][nt][4 * qq], O[dt][nt][4 * qq + 1], O[dt][nt][4 * qq + 2], O[dt][nt][4 * qq + 3]};
       }
-      if (g == 0)
-        *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(lt[nt] > 0.f ? m_run[nt] : kNegInf, lt[nt]);
+      if (h == 0)
+        *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(lt > 0.f ? m_ref[nt] : kNegInf, lt);
     }
   }
 }
@@ -982,12 +1015,13 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   PrefillArgs a{static_cast<const uint16_t*>(q), cu_q_lens, static_cast<const uint16_t*>(k_pool),
                 static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
                 cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, Hq, Hkv, G, batch->max_entries,
-                total_q, m_q, prefill_entries_per_split(batch->max_entries, splits), splits, scale * kLog2e, rope};
+                total_q, m_q, prefill_entries_per_split(batch->max_entries, splits), splits,
+                (cfg->flags & LAZYATTN_FLAG_EXACT_MAX) ? 1 : 0, scale * kLog2e, rope};
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(gz));
   switch (cfg->pe) {
-    case LAZYATTN_PE_ROPE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ROPE>, grid, dim3(512), 0, stream, a); break;
-    case LAZYATTN_PE_NONE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_NONE>, grid, dim3(512), 0, stream, a); break;
-    default: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ALIBI>, grid, dim3(512), 0, stream, a); break;
+    case LAZYATTN_PE_ROPE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ROPE>, grid, dim3(kPrefillThreads), 0, stream, a); break;
+    case LAZYATTN_PE_NONE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_NONE>, grid, dim3(kPrefillThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ALIBI>, grid, dim3(kPrefillThreads), 0, stream, a); break;
   }
   *splits_out = splits;
   return launched();

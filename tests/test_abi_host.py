@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _abi.lib().lazyattn_abi_version() == 1
+    assert _abi.lib().lazyattn_abi_version() == 2
     for s in range(5):
         assert len(_abi.status_string(s)) > 0
     assert _abi.status_string(99) == "unknown status"
@@ -130,7 +130,9 @@ def test_config_errors():
     assert check(C(block_size=32)) == _abi.EUNSUPPORTED
     assert check(C(rope_theta=0.0)) == _abi.EINVAL
     assert check(C(rope_theta=0.0, pe="none")) == _abi.OK
-    c = C(); c.reserved = 1
+    c = C(); c.flags = _abi.FLAG_EXACT_MAX
+    assert check(c) == _abi.OK
+    c = C(); c.flags = 2
     assert check(c) == _abi.EINVAL
     c = C(); c.dtype = 7
     assert check(c) == _abi.EINVAL

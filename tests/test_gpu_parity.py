@@ -41,10 +41,11 @@ def sync():
 # ---------------------------------------------------------------------------
 # helpers running one phase on both sides
 # ---------------------------------------------------------------------------
-def run_prefill(wl, num_splits=0, pe=None, block_permutation=None, pools=None):
+def run_prefill(wl, num_splits=0, pe=None, block_permutation=None, pools=None, exact_max=False, pb=None):
     s = wl.spec
-    cfg = staging.config_for(s, pe=pe)
-    pb = wl.prefill_batch()
+    cfg = staging.config_for(s, pe=pe, exact_max=exact_max)
+    if pb is None:
+        pb = wl.prefill_batch()
     if pools is None:
         pools = staging.DevicePools(wl, DEV, block_permutation)
     staging.append_tokens(cfg, pools, pb, s.dtype, DEV, block_permutation)
@@ -321,6 +322,51 @@ def test_other_encodings_llama8b_prefill(pe):
     orc = OracleState(wl)
     orc.append(pb)
     compare_prefill(wl, pb, got, orc, pe=pe, label=f"8B prefill pe={pe}")
+
+
+# ---------------------------------------------------------------------------
+# softmax reference: the exact two-pass route, forced and triggered
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("pe", ["rope", "none"])
+def test_prefill_exact_maximum_route(pe):
+    say("8B prefill, exact-maximum route forced, pe", pe)
+    wl = W.build_workload(W.spec(2, requests=[4]))
+    pb, got, _ = run_prefill(wl, pe=pe, exact_max=True)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, pe=pe, label=f"8B prefill exact route pe={pe}")
+    _, fast, _ = run_prefill(wl, pe=pe)
+    mx, mn = diff_stats(fast, got)
+    say(f"fast vs exact route: max {mx:.2e} mean {mn:.2e}")
+    assert mx <= 4e-3 and mn <= 2e-4
+
+
+def test_prefill_redo_when_scores_outgrow_the_first_tile():
+    # queries scaled by 64 (exact in bf16) spread each row's scores over
+    # hundreds of base-2 units, so later key tiles exceed the first tile's
+    # maximum by far more than 2^64 and the work-groups must redo their rows
+    # with the exact maximum: the result is then the exact route's, bit for
+    # bit (without the redo it would overflow)
+    say("8B prefill with queries scaled by 64 (redo route)")
+    wl = W.build_workload(W.spec(2, requests=[2]))
+    pb = dict(wl.prefill_batch())
+    pb["q"] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(pb["q"]) * np.float32(64.0))
+    for splits in (1, 2):
+        _, fast, _ = run_prefill(wl, pb=pb, num_splits=splits)
+        _, exact, _ = run_prefill(wl, pb=pb, num_splits=splits, exact_max=True)
+        assert np.all(np.isfinite(fast))
+        assert np.array_equal(fast, exact)
+    # the peaked softmax still follows the oracle (scores carry bf16 rounding
+    # of a few tenths of a base-2 unit at this scale, hence the loose bound)
+    orc = OracleState(wl)
+    orc.append(pb)
+    ref = orc.prefill(pb)
+    cu = pb["cu_q_lens"]
+    g = np.concatenate([exact[cu[r]:cu[r + 1]] for r in ref])
+    rr = np.concatenate([ref[r] for r in ref])
+    mx, mn = diff_stats(g, rr)
+    say(f"scaled queries vs oracle: max {mx:.2e} mean {mn:.2e}")
+    assert mn <= 5e-2
 
 
 # ---------------------------------------------------------------------------
