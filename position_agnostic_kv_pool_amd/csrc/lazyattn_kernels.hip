@@ -384,14 +384,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         for (int nt = 0; nt < NT; ++nt) S[tau][nt] = negm[nt];
       float2 ph = make_float2(1.f, 0.f);
       if (PE == LAZYATTN_PE_ROPE) ph = unit_phase_turns(nst - p0 + 8 * part, A.rope.rev[lane]);
+      // K~ operands are read one k-step ahead of their products
+      bf16x8 ak[2][2];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) ak[0][tau] = *reinterpret_cast<const bf16x8*>(&kb[(32 * tau + c) * kKS + 8 * h]);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
+        if (kk + 1 < 8) {
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kb[(32 * tau + c) * kKS + 16 * kk + 8 * h]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) S[tau][nt] = mfma32x32x16(a, qf[8 * nt + kk], S[tau][nt]);
+          for (int tau = 0; tau < 2; ++tau)
+            ak[(kk + 1) & 1][tau] =
+                *reinterpret_cast<const bf16x8*>(&kb[(32 * tau + c) * kKS + 16 * (kk + 1) + 8 * h]);
         }
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) S[tau][nt] = mfma32x32x16(ak[kk & 1][tau], qf[8 * nt + kk], S[tau][nt]);
         if (PE == LAZYATTN_PE_ROPE) {
           kr[kk] = rotate_pair(kr[kk], ph);
           ph = cmul(ph, r1);
@@ -464,11 +472,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         // O^T += V^T P^T, V of entry E read in the pool's channel-major layout;
         // the exponentials of one entry overlap the products of the previous
         const uint16_t* vb = Vs[i & 1];
+        // V operands (entry E, channel tile dt: read number 4 E + dt) two reads ahead
+        auto vread = [&](int n) {
+          return *reinterpret_cast<const bf16x8*>(&vb[(n >> 2) * kVE + (32 * (n & 3) + c) * kBlock + 8 * h]);
+        };
+        bf16x8 av[3];
+        av[0] = vread(0);
+        av[1] = vread(1);
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const int E = 2 * tau + ks;
             bf16x8 Pk[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -481,9 +495,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
             }
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-              const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vb[E * kVE + (32 * dt + c) * kBlock + 8 * h]);
+              const int n = 4 * (2 * tau + ks) + dt;
+              if (n + 2 < 16) av[(n + 2) % 3] = vread(n + 2);
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma32x32x16(a, Pk[nt], O[dt][nt]);
+              for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma32x32x16(av[n % 3], Pk[nt], O[dt][nt]);
             }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) O1[nt] = mfma32x32x16(ones, Pk[nt], O1[nt]);
