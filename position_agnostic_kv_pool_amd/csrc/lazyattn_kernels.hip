@@ -623,6 +623,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* o_part, const f
 // with the group's G heads padded to NT tiles of 16.  Lane (g, n) loads key
 // row n, channels 32g..32g+31 (64 contiguous bytes) and V channel rows
 // 16dt + n, keys 4g..4g+3 (8 bytes each); the whole 8 KB block is read once.
+// Scores are formed relative to a per-head reference m that enters the QK
+// chain as the MFMA's initial accumulator (-m); the reference is raised, and O
+// rescaled, only when a score outgrows it by more than 2^8, so the common
+// block spends no vector instructions on maxima or rescaling.
 // ---------------------------------------------------------------------------
 struct DecodeArgs {
   const uint16_t* q;
@@ -641,6 +645,7 @@ struct DecodeArgs {
 };
 
 constexpr int kOS = kPD + 4;  // LDS row stride (floats) of the wave-merge buffer
+constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
 template <int PE, int NT>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
@@ -660,7 +665,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
   const int e_begin = split * A.eps;
   const int e_end = min(ne, e_begin + A.eps);
 
-  // query fragments: lane (g, n) holds head column nt*16+n, channels 32g + 8s + 0..7
+  // query fragments: lane (g, n) holds head column nt*16+n, channels 32g + 8s + 0..7,
+  // scaled by scale*log2(e) and rounded to bf16
   bf16x8 qb[NT][4];
   float slope[NT];
 #pragma unroll
@@ -673,7 +679,11 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
     for (int s = 0; s < 4; ++s) {
       uint4 raw = make_uint4(0, 0, 0, 0);
       if (ok) raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(r) * Hq + h) * kPD + 32 * g + 8 * s);
-      qb[nt][s] = __builtin_bit_cast(bf16x8, raw);
+      uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        w4[jj] = pack_bf16x2(bf_lo(w4[jj]) * A.scale_log2, bf_hi(w4[jj]) * A.scale_log2);
+      qb[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
     }
   }
   // R(n) for this lane's key row and pairs 16g..16g+15; this lane's pair for R(S - p)
@@ -690,11 +700,16 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) O[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NT], l_run[NT];
+  // per head column: reference m_run (raw score units, -inf until the first
+  // visible key), its finite stand-in m_use, and the running sum
+  float m_run[NT], m_use[NT], l_run[NT];
+  f32x4 negm[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m_run[nt] = kNegInf;
+    m_use[nt] = 0.f;
     l_run[nt] = 0.f;
+    negm[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   uint4 kr[4];
@@ -726,7 +741,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
     bf16x8 ka[4];
     if (PE == LAZYATTN_PE_ROPE) {
       float2* bw = bsh + (wave * 2 + (it & 1)) * 64;
-      bw[lane] = unit_phase(inf.start - p, my_rev);
+      bw[lane] = unit_phase_turns(inf.start - p, my_rev);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -744,10 +759,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) ka[s] = __builtin_bit_cast(bf16x8, k[s]);
     }
-    if (n >= inf.len) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ka[s] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    }
     if (inf.len < kBlock) {
       // zero V rows past the entry's length (they may hold anything, even NaN)
 #pragma unroll
@@ -762,36 +773,48 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+      // scores relative to the reference: the chain starts from -m
+      f32x4 S = negm[nt];
 #pragma unroll
       for (int s = 0; s < 4; ++s) S = mfma16x16x32(ka[s], qb[nt][s], S);
-      float mx = kNegInf;
+      float lm = kNegInf;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int krow = 4 * g + j;
-        float x = (krow < inf.len) ? S[j] * A.scale_log2 : kNegInf;
+        float x = S[j];
         if (PE == LAZYATTN_PE_ALIBI) x -= slope[nt] * static_cast<float>(p - (inf.start + krow));
+        x = (krow < inf.len) ? x : kNegInf;
         S[j] = x;
-        mx = fmaxf(mx, x);
+        lm = fmaxf(lm, x);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      // raise the reference only when a score outgrows it by 2^8 (exact:
+      // numerator and denominator share it); the test is one compare and a ballot
+      const bool want = (lm > kRescaleSlack) || (m_run[nt] == kNegInf && lm > kNegInf);
+      if (__builtin_amdgcn_ballot_w64(want)) {
+        float pm = fmaxf(lm, __shfl_xor(lm, 16));
+        pm = fmaxf(pm, __shfl_xor(pm, 32));
+        const bool raise = (pm > kRescaleSlack) || (m_run[nt] == kNegInf && pm > kNegInf);
+        const float m_new = raise ? m_use[nt] + pm : m_run[nt];
+        const float mu_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float delta = mu_new - m_use[nt];
+        const float alpha = (m_new == m_run[nt]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        S -= delta;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) O[dt][nt] *= alpha;
+        l_run[nt] *= alpha;
+        m_run[nt] = m_new;
+        m_use[nt] = mu_new;
+        negm[nt] = f32x4{-mu_new, -mu_new, -mu_new, -mu_new};
+      }
       float pe[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pe[j] = __builtin_amdgcn_exp2f(S[j] - m_use);
+      for (int j = 0; j < 4; ++j) pe[j] = __builtin_amdgcn_exp2f(S[j]);
       const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
       // row sum of the bf16-rounded weights that enter P.V
-      const float rs = (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23));
-      l_run[nt] = l_run[nt] * alpha + rs;
-      m_run[nt] = m_new;
+      l_run[nt] += (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23));
       const s16x4 pb = __builtin_bit_cast(s16x4, make_uint2(p01, p23));
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        O[dt][nt] = mfma16x16x16(__builtin_bit_cast(s16x4, v[dt]), pb, O[dt][nt] * alpha);
-      }
+      for (int dt = 0; dt < 8; ++dt) O[dt][nt] = mfma16x16x16(__builtin_bit_cast(s16x4, v[dt]), pb, O[dt][nt]);
     }
     e = e_next;
   }
