@@ -218,6 +218,36 @@ lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, voi
                                    int64_t num_blocks, const void* k_new, const void* v_new,
                                    const int64_t* slots, int32_t n, hipStream_t stream);
 
+/* ---- materialise-then-attend baseline (for comparison only) -------------
+ * The approach deferred positional encoding replaces: existing systems give
+ * each request its own copy of a cached document with positions re-encoded,
+ * paying memory and bandwidth for the copy (shd-paper.top digest, original
+ * abstract; gist.science, Technical Summary > Problem Statement).  These two
+ * calls build that copy so its cost can be measured next to the deferred
+ * kernels: materialise the KV, rotate the queries, then run lazyattn_prefill
+ * with pe = NONE on the copy (same result up to rounding, since
+ * R(p)^T R(t) = R(t - p)).  bf16, D = 128, pe ROPE only. */
+
+/* Copy every entry of every request from the shared pool into the private
+ * block that dst_tables names at the same (request, entry), K rows rotated by
+ * R(t) at their logical position t = start + row, V unchanged.
+ *  batch       the source tables (device), as for prefill
+ *  dst_tables  device [R][batch->max_entries] packed words; only the block ids
+ *              are used, each < dst_num_blocks and written by one entry only
+ *  dst_k_pool, dst_v_pool  device pools of dst_num_blocks blocks, same layout
+ *              as the source pools; the source pools are only read.
+ *  Rows past an entry's length are copied as they are. */
+lazyattn_status lazyattn_materialize_kv(const lazyattn_config* cfg, const void* k_pool, const void* v_pool,
+                                        int64_t num_blocks, const lazyattn_batch* batch,
+                                        const uint64_t* dst_tables, void* dst_k_pool, void* dst_v_pool,
+                                        int64_t dst_num_blocks, hipStream_t stream);
+
+/* Rotate every query row by R(p) at its logical position p (laid out and
+ * positioned as for lazyattn_prefill) into q_out device [total_q][Hq][D]. */
+lazyattn_status lazyattn_rotate_queries(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
+                                        int32_t total_q, int32_t max_q_len, const lazyattn_batch* batch,
+                                        void* q_out, hipStream_t stream);
+
 /* Decode every table entry on the device exactly as the attention kernels do
  * and write (block id, logical start, valid length) as int32 triples to
  * out [R][max_entries][3] (device); entries >= num_entries[r] get (-1,-1,-1). */

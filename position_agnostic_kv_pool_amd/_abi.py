@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             "lazyattn_merge_splits": (I32, [CP, I32, I32, P, SZ, P, P]),
             "lazyattn_append_kv": (I32, [CP, P, P, I64, P, P, P, I32, P]),
             "lazyattn_debug_decode_tables": (I32, [BP, P, P]),
+            "lazyattn_materialize_kv": (I32, [CP, P, P, I64, BP, P, P, P, I64, P]),
+            "lazyattn_rotate_queries": (I32, [CP, P, P, I32, I32, BP, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -243,6 +245,21 @@ def append_kv(cfg: Config, k_pool, v_pool, num_blocks: int, k_new, v_new, slots,
     st = lib().lazyattn_append_kv(ctypes.byref(cfg), _ptr(k_pool), _ptr(v_pool), int(num_blocks), _ptr(k_new),
                                   _ptr(v_new), _ptr(slots), int(slots.shape[0]), _stream(stream))
     _check(st, "lazyattn_append_kv")
+
+
+def materialize_kv(cfg: Config, k_pool, v_pool, num_blocks: int, batch: Batch, dst_tables, dst_k_pool, dst_v_pool,
+                   dst_num_blocks: int, stream=None) -> None:
+    st = lib().lazyattn_materialize_kv(ctypes.byref(cfg), _ptr(k_pool), _ptr(v_pool), int(num_blocks),
+                                       ctypes.byref(batch), _ptr(dst_tables), _ptr(dst_k_pool), _ptr(dst_v_pool),
+                                       int(dst_num_blocks), _stream(stream))
+    _check(st, "lazyattn_materialize_kv")
+
+
+def rotate_queries(cfg: Config, q, cu_q_lens, total_q: int, max_q_len: int, batch: Batch, q_out,
+                   stream=None) -> None:
+    st = lib().lazyattn_rotate_queries(ctypes.byref(cfg), _ptr(q), _ptr(cu_q_lens), int(total_q), int(max_q_len),
+                                       ctypes.byref(batch), _ptr(q_out), _stream(stream))
+    _check(st, "lazyattn_rotate_queries")
 
 
 def debug_decode_tables(batch: Batch, out, stream=None) -> None:

@@ -870,6 +870,56 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
 }
 
 // ---------------------------------------------------------------------------
+// Materialise-then-attend baseline: per-request copies of the KV with K rows
+// rotated at their absolute positions, and queries rotated at theirs, so a
+// rotation-free kernel can attend over the copy.  Comparison only.
+// One work-group per (entry, request, KV head): lane l of each wave rotates
+// channel pair l of 4 key rows (phase R(t) stepped by R(1) per row); V is
+// copied 16 B per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void materialize_kernel(const uint16_t* kpool, const uint16_t* vpool,
+                                                          const uint64_t* src_tab, const uint64_t* dst_tab,
+                                                          const int32_t* n_ent, int max_entries, int Hkv,
+                                                          uint16_t* dk, uint16_t* dv, RopeRev rope) {
+  const int e = blockIdx.x, r = blockIdx.y, h = blockIdx.z;
+  if (e >= n_ent[r]) return;
+  const uint64_t w = src_tab[static_cast<size_t>(r) * max_entries + e];
+  const uint32_t src = word_block(w), dst = word_block(dst_tab[static_cast<size_t>(r) * max_entries + e]);
+  const int start = static_cast<int>(word_start(w));
+  const int tid = threadIdx.x, pair = tid & 63, row0 = 4 * (tid >> 6);
+  const size_t sb = (static_cast<size_t>(src) * Hkv + h) * (kBlock * kPD);
+  const size_t db = (static_cast<size_t>(dst) * Hkv + h) * (kBlock * kPD);
+  const uint32_t* ks = reinterpret_cast<const uint32_t*>(kpool + sb) + pair;
+  uint32_t* kd = reinterpret_cast<uint32_t*>(dk + db) + pair;
+  float2 ph = unit_phase(start + row0, rope.rev[pair]);
+  const float2 step = unit_phase(1, rope.rev[pair]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = row0 + k;
+    kd[row * (kPD / 2)] = rotate_pair(ks[row * (kPD / 2)], ph);
+    ph = cmul(ph, step);
+  }
+  reinterpret_cast<uint4*>(dv + db)[tid] = reinterpret_cast<const uint4*>(vpool + sb)[tid];
+}
+
+// One work-group per (query row of a request, request): lane l rotates
+// channel pair l of every head of that token by R(p).
+__global__ __launch_bounds__(64) void rotate_queries_kernel(const uint16_t* q, const int32_t* cu_q,
+                                                            const int32_t* ctx, int Hq, uint16_t* q_out,
+                                                            RopeRev rope) {
+  const int j = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
+  const int q0 = cu_q[r], q_len = cu_q[r + 1] - q0;
+  if (j >= q_len) return;
+  const int pos = ctx[r] - q_len + j;
+  const float2 ph = unit_phase(pos, rope.rev[lane]);
+  const size_t base = static_cast<size_t>(q0 + j) * Hq * kPD;
+  for (int hh = 0; hh < Hq; ++hh) {
+    const uint32_t x = reinterpret_cast<const uint32_t*>(q + base + static_cast<size_t>(hh) * kPD)[lane];
+    reinterpret_cast<uint32_t*>(q_out + base + static_cast<size_t>(hh) * kPD)[lane] = rotate_pair(x, ph);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 attention on the vector ALU, for the float32 dtype.  One wave per
 // (query row, head); lane i owns channel pair i; keys are visited one by one
 // with an online softmax.  Used for small fp32 cases (correctness path).
@@ -1209,6 +1259,43 @@ lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, voi
                        static_cast<float*>(v_pool), static_cast<const float*>(k_new),
                        static_cast<const float*>(v_new), slots, cfg->num_kv_heads, cfg->head_dim);
   }
+  return launched();
+}
+
+lazyattn_status lazyattn_materialize_kv(const lazyattn_config* cfg, const void* k_pool, const void* v_pool,
+                                        int64_t num_blocks, const lazyattn_batch* batch,
+                                        const uint64_t* dst_tables, void* dst_k_pool, void* dst_v_pool,
+                                        int64_t dst_num_blocks, hipStream_t stream) {
+  lazyattn_status st = check_config(cfg);
+  if (st != LAZYATTN_OK) return st;
+  if ((st = check_batch(batch)) != LAZYATTN_OK) return st;
+  if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE) return LAZYATTN_EUNSUPPORTED;
+  if (batch->num_reqs == 0 || batch->max_entries == 0) return LAZYATTN_OK;
+  if (!k_pool || !v_pool || !dst_tables || !dst_k_pool || !dst_v_pool || num_blocks < 1 || dst_num_blocks < 1)
+    return LAZYATTN_EINVAL;
+  if (batch->num_reqs > 65535 || cfg->num_kv_heads > 65535) return LAZYATTN_EUNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(batch->max_entries), batch->num_reqs, cfg->num_kv_heads);
+  hipLaunchKernelGGL(materialize_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(k_pool),
+                     static_cast<const uint16_t*>(v_pool), batch->block_tables, dst_tables, batch->num_entries,
+                     batch->max_entries, cfg->num_kv_heads, static_cast<uint16_t*>(dst_k_pool),
+                     static_cast<uint16_t*>(dst_v_pool), make_rope_rev(cfg));
+  return launched();
+}
+
+lazyattn_status lazyattn_rotate_queries(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
+                                        int32_t total_q, int32_t max_q_len, const lazyattn_batch* batch,
+                                        void* q_out, hipStream_t stream) {
+  lazyattn_status st = check_config(cfg);
+  if (st != LAZYATTN_OK) return st;
+  if ((st = check_batch(batch)) != LAZYATTN_OK) return st;
+  if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE) return LAZYATTN_EUNSUPPORTED;
+  if (total_q < 0 || max_q_len < 0) return LAZYATTN_EINVAL;
+  if (batch->num_reqs == 0 || total_q == 0 || max_q_len == 0) return LAZYATTN_OK;
+  if (!q || !cu_q_lens || !q_out) return LAZYATTN_EINVAL;
+  if (batch->num_reqs > 65535) return LAZYATTN_EUNSUPPORTED;
+  hipLaunchKernelGGL(rotate_queries_kernel, dim3(max_q_len, batch->num_reqs), dim3(64), 0, stream,
+                     static_cast<const uint16_t*>(q), cu_q_lens, batch->ctx_lens, cfg->num_q_heads,
+                     static_cast<uint16_t*>(q_out), make_rope_rev(cfg));
   return launched();
 }
 

@@ -137,3 +137,52 @@ class DecodeCall:
 
     def merge(self, stream=None):
         _abi.merge_splits(self.cfg, self.q.shape[0], self.splits, self.workspace, self.out, stream)
+
+
+class MaterializedPrefill:
+    """The materialise-then-attend baseline for one prefill call: private copies
+    of every request's blocks (K rotated at absolute positions), queries rotated
+    at theirs, and the rotation-free prefill over the copy."""
+
+    def __init__(self, spec, inputs: dict, device="cuda", num_splits: int = 0):
+        self.cfg_rope = config_for(spec)
+        self.cfg_none = config_for(spec, pe="none")
+        n_ent = np.asarray(inputs["num_entries"], dtype=np.int64)
+        starts = inputs["table_starts"]
+        R, E = inputs["table_blocks"].shape
+        dst_blocks = np.zeros((R, E), dtype=np.uint32)
+        off = 0
+        for r in range(R):
+            dst_blocks[r, :n_ent[r]] = np.arange(off, off + n_ent[r], dtype=np.uint32)
+            off += int(n_ent[r])
+        self.dst_num_blocks = max(off, 1)
+        dt = torch_dtype(spec.dtype)
+        self.k = torch.empty((self.dst_num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim), dtype=dt,
+                             device=device)
+        self.v = torch.empty((self.dst_num_blocks, spec.num_kv_heads, spec.head_dim, spec.block_size), dtype=dt,
+                             device=device)
+        self.src = DeviceTables.from_inputs(inputs, device)
+        self.dst = DeviceTables(dst_blocks, starts, inputs["num_entries"], inputs["ctx_lens"], device)
+        self.call = PrefillCall(self.cfg_none, spec, inputs, device, num_splits)
+        self.call.tables = self.dst
+        self.q_rot = torch.empty_like(self.call.q)
+        self.bytes_copied = 2 * self.k.numel() * self.k.element_size()
+
+    def materialize(self, pools: DevicePools, stream=None):
+        _abi.materialize_kv(self.cfg_rope, pools.k, pools.v, pools.num_blocks, self.src.batch, self.dst.tables,
+                            self.k, self.v, self.dst_num_blocks, stream)
+
+    def rotate_queries(self, stream=None):
+        c = self.call
+        _abi.rotate_queries(self.cfg_rope, c.q, c.cu_q, c.total_q, c.max_q_len, self.src.batch, self.q_rot, stream)
+
+    def attend(self, stream=None):
+        c = self.call
+        _abi.prefill(self.cfg_none, self.q_rot, c.cu_q, c.total_q, c.max_q_len, self.k, self.v, self.dst_num_blocks,
+                     self.dst.batch, c.out, c.workspace, c.num_splits, stream)
+        return c.out
+
+    def run(self, pools: DevicePools, stream=None):
+        self.materialize(pools, stream)
+        self.rotate_queries(stream)
+        return self.attend(stream)

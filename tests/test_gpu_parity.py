@@ -370,6 +370,31 @@ def test_prefill_redo_when_scores_outgrow_the_first_tile():
 
 
 # ---------------------------------------------------------------------------
+# the materialise-then-attend baseline computes the same attention
+# ---------------------------------------------------------------------------
+def test_materialized_baseline_matches_oracle_and_leaves_the_pool():
+    say("8B prefill through the materialise-then-attend baseline")
+    wl = W.build_workload(W.spec(2, requests=[3]))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb = wl.prefill_batch()
+    pools = staging.DevicePools(wl, DEV)
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    k_before = pools.k.clone()
+    mat = staging.MaterializedPrefill(s, pb, DEV)
+    got = gpu_f64(mat.run(pools))
+    sync()
+    assert torch.equal(pools.k.view(torch.int16), k_before.view(torch.int16))
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="materialised baseline")
+    _, lazy, _ = run_prefill(wl, pools=pools, pb=pb)
+    mx, mn = diff_stats(lazy, got)
+    say(f"deferred vs materialised: max {mx:.2e} mean {mn:.2e}")
+    assert mx <= 1e-2 and mn <= 1e-3
+
+
+# ---------------------------------------------------------------------------
 # negative controls: planted mistakes in the oracle must fail the bar
 # ---------------------------------------------------------------------------
 def test_negative_controls_fail_the_tolerance():
