@@ -171,6 +171,10 @@ def bench_prefill(torch, args, W, staging, _abi):
     call = staging.PrefillCall(cfg, s, pb, "cuda")
     cfg_none = staging.config_for(s, pe="none")
     call_none = staging.PrefillCall(cfg_none, s, pb, "cuda")
+    # the same batch over a pool in document-local frames
+    fpools = staging.FramedPools(wl, cfg, "cuda")
+    staging.append_tokens(cfg, fpools, pb, s.dtype, "cuda")
+    call_framed = staging.PrefillCall(cfg, s, pb, "cuda", framed=True)
     torch.cuda.synchronize()
     timer = Timer(torch)
     for _ in range(args.warmup):
@@ -181,11 +185,14 @@ def bench_prefill(torch, args, W, staging, _abi):
     # back-to-back between two events
     ms = timer.span(lambda: call.run(pools), args.steps)
     # the attention kernel alone and its rotation-free control, three interleaved rounds (medians)
-    att, att_none, step_none = [], [], []
+    att, att_none, step_none, att_framed = [], [], [], []
+    call_framed.run(fpools)
     for _ in range(3):
         att.append(timer.span(lambda: call.attend(pools), args.steps))
         att_none.append(timer.span(lambda: call_none.attend(pools), args.steps))
         step_none.append(timer.span(lambda: call_none.run(pools), args.steps))
+        att_framed.append(timer.span(lambda: call_framed.attend(fpools), args.steps))
+    del fpools
     # cold: the last-level cache flushed by a 512 MB write before each single launch
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     cold, cold_none = [], []
@@ -206,11 +213,11 @@ def bench_prefill(torch, args, W, staging, _abi):
     del mat
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
     return dict(wl=wl, pb=pb, ms=ms, ms_attend=med(att), ms_none=med(step_none), ms_none_attend=med(att_none),
-                att=att, att_none=att_none, cold=med(cold), cold_none=med(cold_none), flops=flops, base=base,
+                att=att, att_none=att_none, att_framed=att_framed, ms_framed_attend=med(att_framed), cold=med(cold), cold_none=med(cold_none), flops=flops, base=base,
                 splits=call.splits, pools=pools)
 
 
-def bench_decode(torch, args, W, staging, _abi, n_steps: int):
+def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = True):
     """Decode steps 0..n_steps-1 of the 8B decode shape.  Each step's new token is appended
     untimed; then 3 back-to-back launches of its attention kernel are timed (they re-read the same
     step's pool, as the step itself would), with and without the merge, and rotation-free."""
@@ -220,29 +227,41 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int):
     cfg_none = staging.config_for(s, pe="none")
     pools = staging.DevicePools(wl, "cuda")
     staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, "cuda")
+    fpools = staging.FramedPools(wl, cfg, "cuda") if framed else None
+    if framed:
+        staging.append_tokens(cfg, fpools, wl.tokens_before_step(0), s.dtype, "cuda")
     t = torch
     tot_ms, tot_merge_ms, tot_ms_none, tot_bytes, tot_unique, tokens = 0.0, 0.0, 0.0, 0, 0, 0
+    tot_ms_framed = 0.0
     for step in range(-2, n_steps):          # two untimed warm-up launches on step 0's inputs
         d = wl.decode_step(max(step, 0))
         if step >= 0:
             staging.append_tokens(cfg, pools, d, s.dtype, "cuda")
+            if framed:
+                staging.append_tokens(cfg, fpools, d, s.dtype, "cuda")
         call = staging.DecodeCall(cfg, s, d, "cuda")
         call_none = staging.DecodeCall(cfg_none, s, d, "cuda")
         timer = Timer(t)
         ms_att = timer.span(lambda: call.attend(pools), 3)
         ms_step = timer.span(lambda: call.run(pools), 3)
         ms_none = timer.span(lambda: call_none.attend(pools), 3)
+        ms_framed = 0.0
+        if framed:
+            call_framed = staging.DecodeCall(cfg, s, d, "cuda", framed=True)
+            ms_framed = timer.span(lambda: call_framed.attend(fpools), 3)
         if step < 0:
             continue
         tot_ms += ms_att
         tot_merge_ms += max(ms_step - ms_att, 0.0)
         tot_ms_none += ms_none
+        tot_ms_framed += ms_framed
         by = decode_bytes(d, wl)
         tot_bytes += by["logical"]
         tot_unique += by["unique"]
         tokens += len(d["ctx_lens"])
     n = max(n_steps, 1)
-    return dict(ms=tot_ms / n, merge_ms=tot_merge_ms / n, ms_none=tot_ms_none / n, bytes=tot_bytes / n,
+    return dict(ms=tot_ms / n, merge_ms=tot_merge_ms / n, ms_none=tot_ms_none / n, ms_framed=tot_ms_framed / n,
+                bytes=tot_bytes / n,
                 unique=tot_unique / n,
                 tokens=tokens, splits=_abi.decode_splits(cfg, len(wl.requests), wl.table_arrays(wl.requests)[0].shape[1]))
 
@@ -321,7 +340,7 @@ def main() -> int:
     _abi.lib()
 
     if args.decode_only:
-        dec = bench_decode(torch, args, W, staging, _abi, args.decode_steps)
+        dec = bench_decode(torch, args, W, staging, _abi, args.decode_steps, framed=False)
         print(json.dumps({"decode_ms_per_step": dec["ms"], "decode_GBps": dec["bytes"] / dec["ms"] / 1e6}),
               flush=True)
         return 0
@@ -369,6 +388,13 @@ def main() -> int:
             "copied_bytes": int(pre["base"]["copied_bytes"]),
             "deferred_step_us": round(pre["ms"] * 1e3, 2),
             "deferred_speedup": round(pre["base"]["total"] / pre["ms"], 3)},
+        "document_frames": {
+            "what": "the same attention over a pool whose keys carry their index inside their document "
+                    "(stored R(j) k): prefill turns each key entry once by R(F - p0), decode turns the query "
+                    "once per document",
+            "prefill_attention_us": round(pre["ms_framed_attend"] * 1e3, 2),
+            "prefill_rounds_us": [round(x * 1e3, 2) for x in pre["att_framed"]],
+            "prefill_overhead_vs_norotation": round(pre["ms_framed_attend"] / pre["ms_none_attend"] - 1.0, 4)},
     }
     if not args.prefill_only:
         del pre["pools"]
@@ -389,6 +415,8 @@ def main() -> int:
             "norotation_us_per_step": round(dec["ms_none"] * 1e3, 2),
             "rope_overhead": round(dec["ms"] / dec["ms_none"] - 1.0, 4),
         }
+        out["document_frames"]["decode_attention_us"] = round(dec["ms_framed"] * 1e3, 2)
+        out["document_frames"]["decode_overhead_vs_norotation"] = round(dec["ms_framed"] / dec["ms_none"] - 1.0, 4)
         print(f"# decode done: {dec['ms'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre, W)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LAZYATTN_ABI_VERSION 2
+#define LAZYATTN_ABI_VERSION 3
 
 typedef enum {
   LAZYATTN_OK = 0,
@@ -94,12 +94,24 @@ typedef struct {
   const float* alibi_slopes;  /* device [Hq], or NULL => 2^(-8(h+1)/Hq) */
 } lazyattn_config;
 
+/* Key frames.  With frame_starts == NULL the pool holds content-only keys
+ * (gist.science, Technical Summary > Methodology: purely content-based cache)
+ * and the kernels rotate every key row by R(t - p).  With frame_starts set,
+ * the pool holds keys in document-local frames: the key of entry e's row at
+ * logical position t is stored as R(t - F) k with F = frame_starts[r][e]
+ * (a document's first position; LAZYATTN_FLAG_* unchanged), written with
+ * lazyattn_append_kv_framed.  A block stays reusable at any offset, and the
+ * kernels need one rotation R(F - p) per (query, frame) instead of one per key
+ * (gist.science, Technical Implementation > Decoding: the query is rotated
+ * only when the offset changes; > Prefilling: one relative rotation per key
+ * tile).  pe ROPE, bf16 only. */
 typedef struct {
   int32_t num_reqs;                /* R >= 0 */
   int32_t max_entries;             /* row stride of block_tables, >= every num_entries[r] */
   const uint64_t* block_tables;    /* device [R][max_entries] packed words */
   const int32_t* num_entries;      /* device [R] entries in use */
   const int32_t* ctx_lens;         /* device [R] context length L_r, this call's new tokens included */
+  const int32_t* frame_starts;     /* device [R][max_entries] or NULL (content-only pool) */
 } lazyattn_batch;
 
 /* ---- host-only helpers (no GPU needed) ---------------------------------- */
@@ -247,6 +259,15 @@ lazyattn_status lazyattn_materialize_kv(const lazyattn_config* cfg, const void* 
 lazyattn_status lazyattn_rotate_queries(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
                                         int32_t total_q, int32_t max_q_len, const lazyattn_batch* batch,
                                         void* q_out, hipStream_t stream);
+
+/* lazyattn_append_kv for a pool in document-local frames: token i's key is
+ * stored as R(frame_index[i]) k_new[i] (frame_index = its logical position
+ * minus its frame's start), its value unchanged.  frame_index device [n]
+ * int32.  pe ROPE, bf16 only. */
+lazyattn_status lazyattn_append_kv_framed(const lazyattn_config* cfg, void* k_pool, void* v_pool,
+                                          int64_t num_blocks, const void* k_new, const void* v_new,
+                                          const int64_t* slots, const int32_t* frame_index, int32_t n,
+                                          hipStream_t stream);
 
 /* Decode every table entry on the device exactly as the attention kernels do
  * and write (block id, logical start, valid length) as int32 triples to

@@ -65,6 +65,8 @@ __all__ = [
     "bf16_to_f64", "to_f64", "rope_inv_freq", "rope_rotate", "alibi_slopes",
     "gather_context", "attend", "prefill", "decode", "append_kv",
     "brute_force_attention", "rotation_flop_fraction", "tile_flop_counts",
+    "rotate_into_frames", "append_kv_framed", "token_frames", "attend_framed", "prefill_framed",
+    "decode_framed",
 ]
 
 
@@ -144,6 +146,8 @@ def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
         return bf16_to_f64(x)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(dtype)
 
 
@@ -336,7 +340,104 @@ def append_kv(k_pool, v_pool, k_new, v_new, slots, block_size: int):
 
 
 # ---------------------------------------------------------------------------
-# 7. brute force: explicit loops, math.cos/math.sin, tiny inputs only
+# 6b. the document-local-frame pool variant
+#     [gist:Technical Implementation / Decoding]: the query is rotated only
+#     when the offset changes, i.e. when attention moves on to another
+#     document; [gist:Technical Implementation / Prefilling]: one relative
+#     rotation per key tile.  Both only save work if the cached keys already
+#     carry their positions inside their own document.  Reading: a document
+#     block stores R(j) k for the key's index j inside its document (its
+#     "frame"); entry e of a request carries the frame start F_e (the
+#     document's first logical position there).  Since R(a)^T R(b) = R(b - a)
+#     [gist:Mathematical Equivalence], with t = F + j
+#         q^T R(t - p) k = (R(p - F) q)^T (R(t - F) k),
+#     so the framed scores equal the content-only ones.
+# ---------------------------------------------------------------------------
+def rotate_into_frames(k_new: np.ndarray, frame_index, inv_freq: np.ndarray) -> np.ndarray:
+    """Keys [n][Hkv][D] as a framed pool stores them: token i turned by R(frame_index[i])."""
+    return rope_rotate(k_new, np.asarray(frame_index, dtype=np.float64)[:, None], inv_freq)
+
+
+def append_kv_framed(k_pool, v_pool, k_new, v_new, slots, frame_index, block_size: int, inv_freq,
+                     dtype: str):
+    """append_kv of the framed keys into float64 pools; k_new, v_new in ``dtype``."""
+    append_kv(k_pool, v_pool, rotate_into_frames(to_f64(k_new, dtype), frame_index, inv_freq),
+              to_f64(v_new, dtype), slots, block_size)
+
+
+def token_frames(words, n_entries, ctx_len, frame_starts, block_size, num_blocks) -> np.ndarray:
+    """Frame start of each logical token 0..L-1: that of the entry holding it."""
+    _, starts, lens = decode_table(words, n_entries, ctx_len, block_size, num_blocks)
+    f = np.empty(ctx_len, dtype=np.int64)
+    for e in range(starts.size):
+        f[int(starts[e]):int(starts[e]) + int(lens[e])] = int(frame_starts[e])
+    return f
+
+
+def attend_framed(q, q_pos, K, V, k_pos, k_frame, *, rope_theta: float, softmax_scale=None, heads=None):
+    """Causal attention over framed keys: z_t = scale * <R(p - F_t) q_p, K_t>.
+
+    q [M][Hq][D] unrotated; K [L][Hkv][D] holds R(t - F_t) k_t; V content.
+    The query is turned separately for every key's frame (no grouping by
+    document: the plain definition).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    M, Hq, D = q.shape
+    G = Hq // K.shape[1]
+    scale = 1.0 / math.sqrt(D) if not softmax_scale else float(softmax_scale)
+    heads = list(range(Hq)) if heads is None else list(heads)
+    inv_freq = rope_inv_freq(D, rope_theta)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    k_pos = np.asarray(k_pos, dtype=np.int64)
+    k_frame = np.asarray(k_frame, dtype=np.int64)
+    out = np.zeros((M, len(heads), D), dtype=np.float64)
+    for j, h in enumerate(heads):
+        kvh = h // G
+        for m in range(M):
+            qt = rope_rotate(np.broadcast_to(q[m, h], (K.shape[0], D)), q_pos[m] - k_frame, inv_freq)
+            z = scale * np.sum(qt * K[:, kvh, :], axis=1)
+            vis = k_pos <= q_pos[m]
+            z = np.where(vis, z, -np.inf)
+            e = np.where(vis, np.exp(z - z.max()), 0.0)
+            out[m, j] = (e / e.sum()) @ V[:, kvh, :]
+    return out
+
+
+def prefill_framed(*, q, cu_q_lens, ctx_lens, num_entries, table_words, frame_starts, k_pool, v_pool,
+                   block_size: int, dtype: str, rope_theta: float, softmax_scale=None,
+                   requests=None, heads=None, token_subset=None) -> dict:
+    """prefill over a framed pool (k_pool, v_pool float64; q in ``dtype``); results as prefill's."""
+    qf = to_f64(q, dtype)
+    reqs = range(len(ctx_lens)) if requests is None else requests
+    res = {}
+    for r in reqs:
+        words, n_ent, L = _request_args(table_words, num_entries, ctx_lens, r)
+        K, V, kp = gather_context(words, n_ent, L, k_pool, v_pool, block_size, "f64")
+        fr = token_frames(words, n_ent, L, frame_starts[r], block_size, k_pool.shape[0])
+        a, b = int(cu_q_lens[r]), int(cu_q_lens[r + 1])
+        M = b - a
+        local = np.arange(M) if token_subset is None or r not in token_subset \
+            else np.asarray(token_subset[r], dtype=np.int64)
+        res[r] = attend_framed(qf[a + local], L - M + local, K, V, kp, fr, rope_theta=rope_theta,
+                               softmax_scale=softmax_scale, heads=heads)
+    return res
+
+
+def decode_framed(*, q, ctx_lens, num_entries, table_words, frame_starts, k_pool, v_pool,
+                  block_size: int, dtype: str, rope_theta: float, softmax_scale=None,
+                  requests=None, heads=None) -> dict:
+    """One decode step over a framed pool (float64 pools); results as decode's."""
+    qf = to_f64(q, dtype)
+    reqs = range(len(ctx_lens)) if requests is None else requests
+    res = {}
+    for r in reqs:
+        words, n_ent, L = _request_args(table_words, num_entries, ctx_lens, r)
+        K, V, kp = gather_context(words, n_ent, L, k_pool, v_pool, block_size, "f64")
+        fr = token_frames(words, n_ent, L, frame_starts[r], block_size, k_pool.shape[0])
+        res[r] = attend_framed(qf[r][None], np.array([L - 1]), K, V, kp, fr, rope_theta=rope_theta,
+                               softmax_scale=softmax_scale, heads=heads)[0]
+    return res
+
 # ---------------------------------------------------------------------------
 def brute_force_attention(q_rows, q_positions, words, n_entries, ctx_len, k_pool, v_pool,
                           block_size, num_q_heads, num_kv_heads, theta, pe="rope", scale=None):

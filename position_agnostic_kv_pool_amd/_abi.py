@@ -52,6 +52,7 @@ class Batch(ctypes.Structure):
         ("block_tables", ctypes.c_void_p),
         ("num_entries", ctypes.c_void_p),
         ("ctx_lens", ctypes.c_void_p),
+        ("frame_starts", ctypes.c_void_p),
     ]
 
 
@@ -87,6 +88,7 @@ def lib() -> ctypes.CDLL:
             "lazyattn_decode_attend": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_merge_splits": (I32, [CP, I32, I32, P, SZ, P, P]),
             "lazyattn_append_kv": (I32, [CP, P, P, I64, P, P, P, I32, P]),
+            "lazyattn_append_kv_framed": (I32, [CP, P, P, I64, P, P, P, P, I32, P]),
             "lazyattn_debug_decode_tables": (I32, [BP, P, P]),
             "lazyattn_materialize_kv": (I32, [CP, P, P, I64, BP, P, P, P, I64, P]),
             "lazyattn_rotate_queries": (I32, [CP, P, P, I32, I32, BP, P, P]),
@@ -186,15 +188,17 @@ def _stream(stream) -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_batch(tables, num_entries, ctx_lens) -> Batch:
-    """Batch over device tensors: tables int64/uint64 [R][E] words, num_entries/ctx_lens int32 [R]."""
+def make_batch(tables, num_entries, ctx_lens, frame_starts=None) -> Batch:
+    """Batch over device tensors: tables int64/uint64 [R][E] words, num_entries/ctx_lens int32 [R],
+    optional frame_starts int32 [R][E] (keys stored in document-local frames)."""
     b = Batch()
     b.num_reqs = int(num_entries.shape[0])
     b.max_entries = int(tables.shape[1]) if tables.dim() == 2 else 0
     b.block_tables = _ptr(tables)
     b.num_entries = _ptr(num_entries)
     b.ctx_lens = _ptr(ctx_lens)
-    b._keep = (tables, num_entries, ctx_lens)
+    b.frame_starts = _ptr(frame_starts) if frame_starts is not None else None
+    b._keep = (tables, num_entries, ctx_lens, frame_starts)
     return b
 
 
@@ -260,6 +264,14 @@ def rotate_queries(cfg: Config, q, cu_q_lens, total_q: int, max_q_len: int, batc
     st = lib().lazyattn_rotate_queries(ctypes.byref(cfg), _ptr(q), _ptr(cu_q_lens), int(total_q), int(max_q_len),
                                        ctypes.byref(batch), _ptr(q_out), _stream(stream))
     _check(st, "lazyattn_rotate_queries")
+
+
+def append_kv_framed(cfg: Config, k_pool, v_pool, num_blocks: int, k_new, v_new, slots, frame_index,
+                     stream=None) -> None:
+    st = lib().lazyattn_append_kv_framed(ctypes.byref(cfg), _ptr(k_pool), _ptr(v_pool), int(num_blocks),
+                                         _ptr(k_new), _ptr(v_new), _ptr(slots), _ptr(frame_index),
+                                         int(slots.shape[0]), _stream(stream))
+    _check(st, "lazyattn_append_kv_framed")
 
 
 def debug_decode_tables(batch: Batch, out, stream=None) -> None:

@@ -160,6 +160,7 @@ struct PrefillArgs {
   const uint64_t* tables;
   const int32_t* n_ent;
   const int32_t* ctx;
+  const int32_t* frames;         // [R][max_entries] frame starts (document-local frames) or NULL
   const float* alibi;
   uint16_t* out;
   float* o_part;
@@ -171,6 +172,9 @@ struct PrefillArgs {
 };
 
 constexpr int kPD = 128;                 // head dim of the bf16 kernels
+// Kernel instantiation for RoPE over a pool in document-local frames: a key
+// row at logical position t is stored as R(t - F) k, F its entry's frame start
+constexpr int kPeFramed = 3;
 constexpr int kPrefillThreads = 512;    // threads per prefill work-group
 constexpr int kKS = kPD + 8;             // K~ row stride in bf16 (272 B: conflict-free 16 B reads)
 constexpr int kVE = kPD * kBlock;        // one entry of V, channel-major [D][16], in bf16
@@ -272,6 +276,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     ln = valid ? s1 - s0 : 0;
   };
 
+  // frame starts (framed pool): lanes x = 0..3 (mod 8) hold entry e0 + x of a tile
+  const int32_t* frow = A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0);
+  auto load_frames = [&](int j) -> int {
+    const int x = lane & 7;
+    const int e = e_begin + 4 * j + x;
+    return (PE == kPeFramed && x < 4 && e < ne) ? frow[e] : 0;
+  };
+
   // ---- staging: wave w handles rows 8 part .. 8 part + 7 of entry E = w / 2 --------
   // K: lane l holds channel pair l of the 8 key rows (4 B each); V: lane l holds
   // keys 8 (l % 2) .. + 7 of channels 64 part + 32 cc + l / 2, cc = 0, 1
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
-        if (PE == LAZYATTN_PE_ROPE) {
+        if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) {
           const float2 ph = unit_phase_turns(p_row[nt] - p0, A.rope.rev[8 * kk + 4 * h + jj]);
           const float y0 = x0 * ph.x - x1 * ph.y;
           const float y1 = x0 * ph.y + x1 * ph.x;
@@ -352,9 +364,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   float mx[NT] = {kNegInf};
   auto pass = [&](const bool maxpass, const bool fresh) __attribute__((always_inline)) {
     uint64_t wv0 = load_words(0), wv1 = load_words(1), wv2 = load_words(2);
+    int fv1 = 0, fv2 = 0;
     {
       int blk, st, ln;
       entry_of(wv0, 0, E_own, blk, st, ln);
+      int fv0 = 0;
+      if (PE == kPeFramed) {
+        fv0 = load_frames(0);
+        fv1 = load_frames(1);
+        fv2 = load_frames(2);
+      }
       load_kv(blk);
       if (PE == LAZYATTN_PE_ROPE) {
         float2 ph = unit_phase_turns(st - p0 + 8 * part, A.rope.rev[lane]);
@@ -363,6 +382,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
           kr[k] = rotate_pair(kr[k], ph);
           ph = cmul(ph, r1);
         }
+      }
+      if (PE == kPeFramed) {
+        // every row of the entry turns by the same R(F - p0)
+        const float2 ph = unit_phase_turns(__builtin_amdgcn_readlane(fv0, E_own) - p0, A.rope.rev[lane]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) kr[k] = rotate_pair(kr[k], ph);
       }
       mask_v(ln);
       stage_write(0);
@@ -384,6 +409,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         for (int nt = 0; nt < NT; ++nt) S[tau][nt] = negm[nt];
       float2 ph = make_float2(1.f, 0.f);
       if (PE == LAZYATTN_PE_ROPE) ph = unit_phase_turns(nst - p0 + 8 * part, A.rope.rev[lane]);
+      if (PE == kPeFramed) ph = unit_phase_turns(__builtin_amdgcn_readlane(fv1, E_own) - p0, A.rope.rev[lane]);
       // K~ operands are read one k-step ahead of their products
       bf16x8 ak[2][2];
 #pragma unroll
@@ -404,6 +430,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
           kr[kk] = rotate_pair(kr[kk], ph);
           ph = cmul(ph, r1);
         }
+        if (PE == kPeFramed) kr[kk] = rotate_pair(kr[kk], ph);
         if (kk == 3) mask_v(nln);
       }
       stage_write((i + 1) & 1);
@@ -412,6 +439,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       entry_of(wv2, i + 2, E_own, lblk, lst, lln);
       load_kv(lblk);
       const uint64_t wv3 = load_words(i + 3);
+      const int fv3 = load_frames(i + 3);
 
       int st[4], ln[4];
 #pragma unroll
@@ -507,6 +535,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       wv0 = wv1;
       wv1 = wv2;
       wv2 = wv3;
+      fv1 = fv2;
+      fv2 = fv3;
       __syncthreads();
     }
   };
@@ -635,6 +665,7 @@ struct DecodeArgs {
   const uint64_t* tables;
   const int32_t* n_ent;
   const int32_t* ctx;
+  const int32_t* frames;         // [R][max_entries] frame starts (document-local frames) or NULL
   const float* alibi;
   uint16_t* out;
   float* o_part;
@@ -667,7 +698,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
 
   // query fragments: lane (g, n) holds head column nt*16+n, channels 32g + 8s + 0..7,
   // scaled by scale*log2(e) and rounded to bf16
+  // (framed pool: the raw fragments are kept, and qb is formed per frame)
   bf16x8 qb[NT][4];
+  uint4 qraw[NT][4];
   float slope[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -679,6 +712,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
     for (int s = 0; s < 4; ++s) {
       uint4 raw = make_uint4(0, 0, 0, 0);
       if (ok) raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(r) * Hq + h) * kPD + 32 * g + 8 * s);
+      qraw[nt][s] = raw;
       uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
@@ -692,8 +726,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
   if (PE == LAZYATTN_PE_ROPE) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) rt[i] = unit_phase(n, A.rope.rev[16 * g + i]);
-    my_rev = A.rope.rev[lane];
   }
+  if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) my_rev = A.rope.rev[lane];
+  // framed pool: frame starts of this request's entries, and the frame the
+  // query fragments qb are currently turned to (none yet)
+  const int32_t* frow = A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0);
+  int q_frame = 0, q_turns = 0;
+  bool q_set = false;
 
   f32x4 O[8][NT];
 #pragma unroll
@@ -727,15 +766,48 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
   };
 
   int e = e_begin + wave;
-  if (e < e_end) load_block(e, cur, kr, vr);
+  int fr_next = 0;
+  if (e < e_end) {
+    load_block(e, cur, kr, vr);
+    if (PE == kPeFramed) fr_next = __builtin_amdgcn_readfirstlane(frow[e]);
+  }
   for (int it = 0; e < e_end; ++it) {
     const EntryInfo inf = cur;
+    const int fr = fr_next;
     uint4 k[4] = {kr[0], kr[1], kr[2], kr[3]};
     uint2 v[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) v[dt] = vr[dt];
     const int e_next = e + 4;
-    if (e_next < e_end) load_block(e_next, cur, kr, vr);
+    if (e_next < e_end) {
+      load_block(e_next, cur, kr, vr);
+      if (PE == kPeFramed) fr_next = __builtin_amdgcn_readfirstlane(frow[e_next]);
+    }
+
+    // ---- framed pool: turn the query to this entry's frame, R(p - F) q ----------
+    if (PE == kPeFramed && (!q_set || fr != q_frame)) {
+      float2* bw = bsh + (wave * 2 + (q_turns & 1)) * 64;
+      bw[lane] = unit_phase_turns(p - fr, my_rev);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint32_t w4[4] = {qraw[nt][s].x, qraw[nt][s].y, qraw[nt][s].z, qraw[nt][s].w};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float2 ph = bw[16 * g + 4 * s + jj];     // pair 16g + 4s + jj
+            const float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
+            w4[jj] = pack_bf16x2((x0 * ph.x - x1 * ph.y) * A.scale_log2, (x0 * ph.y + x1 * ph.x) * A.scale_log2);
+          }
+          qb[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        }
+      q_frame = fr;
+      q_set = true;
+      ++q_turns;
+    }
 
     // ---- rotate the key rows: R(S - p + n) = R(S - p) R(n) ------------------
     bf16x8 ka[4];
@@ -1012,6 +1084,25 @@ __global__ void append_kv_kernel(T* kpool, T* vpool, const T* knew, const T* vne
   }
 }
 
+// KV append into a pool in document-local frames: the key is turned by
+// R(frame_index) (its position within its frame) before it is stored; one
+// thread per channel pair, the angle reduced in double as everywhere else.
+__global__ void append_kv_framed_kernel(uint16_t* kpool, uint16_t* vpool, const uint16_t* knew, const uint16_t* vnew,
+                                        const int64_t* slots, const int32_t* frame_index, int Hkv, int D,
+                                        const RopeRev rope) {
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int64_t slot = slots[i];
+  const int64_t blk = slot / kBlock;
+  const int row = static_cast<int>(slot - blk * kBlock);
+  const int j = frame_index[i];
+  const size_t src = (static_cast<size_t>(i) * Hkv + h) * D;
+  const uint32_t* k2 = reinterpret_cast<const uint32_t*>(knew + src);
+  uint32_t* kdst = reinterpret_cast<uint32_t*>(kpool + ((static_cast<size_t>(blk) * Hkv + h) * kBlock + row) * D);
+  for (int pr = threadIdx.x; pr < D / 2; pr += blockDim.x) kdst[pr] = rotate_pair(k2[pr], unit_phase(j, rope.rev[pr]));
+  for (int d = threadIdx.x; d < D; d += blockDim.x)
+    vpool[((static_cast<size_t>(blk) * Hkv + h) * D + d) * kBlock + row] = vnew[src + d];
+}
+
 // ---------------------------------------------------------------------------
 // Table decode, exactly as the attention kernels see it.
 // ---------------------------------------------------------------------------
@@ -1080,6 +1171,8 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   const RopeRev rope = make_rope_rev(cfg);
   const float scale = softmax_scale_of(cfg);
 
+  const bool framed = batch->frame_starts != nullptr;
+  if (framed && (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE)) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32) {
     if (max_q_len > 0x7fffffff || R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), cu_q_lens, static_cast<const float*>(k_pool),
@@ -1102,11 +1195,12 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   float* ml_part = splits > 1 ? o_part + static_cast<size_t>(splits) * total_q * Hq * kPD : nullptr;
   PrefillArgs a{static_cast<const uint16_t*>(q), cu_q_lens, static_cast<const uint16_t*>(k_pool),
                 static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
-                cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, Hq, Hkv, G, batch->max_entries,
+                batch->frame_starts, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, Hq, Hkv, G, batch->max_entries,
                 total_q, m_q, prefill_entries_per_split(batch->max_entries, splits), splits,
                 (cfg->flags & LAZYATTN_FLAG_EXACT_MAX) ? 1 : 0, scale * kLog2e, rope};
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(gz));
-  switch (cfg->pe) {
+  switch (framed ? kPeFramed : cfg->pe) {
+    case kPeFramed: hipLaunchKernelGGL(prefill_bf16_kernel<kPeFramed>, grid, dim3(kPrefillThreads), 0, stream, a); break;
     case LAZYATTN_PE_ROPE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ROPE>, grid, dim3(kPrefillThreads), 0, stream, a); break;
     case LAZYATTN_PE_NONE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_NONE>, grid, dim3(kPrefillThreads), 0, stream, a); break;
     default: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ALIBI>, grid, dim3(kPrefillThreads), 0, stream, a); break;
@@ -1130,6 +1224,8 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   const RopeRev rope = make_rope_rev(cfg);
   const float scale = softmax_scale_of(cfg);
 
+  const bool framed = batch->frame_starts != nullptr;
+  if (framed && (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE)) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32) {
     if (R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), nullptr, static_cast<const float*>(k_pool),
@@ -1149,7 +1245,7 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   float* ml_part = splits > 1 ? o_part + static_cast<size_t>(splits) * R * Hq * kPD : nullptr;
   DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
-               cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, R, Hq, Hkv, G,
+               batch->frame_starts, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, R, Hq, Hkv, G,
                batch->max_entries, decode_entries_per_split(batch->max_entries, splits), splits, scale * kLog2e,
                rope};
   const dim3 grid(splits, Hkv, R);
@@ -1163,13 +1259,15 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
     hipLaunchKernelGGL((decode_bf16_kernel<PEV, NTV>), grid, dim3(256), lds, stream, a);            \
   } while (0)
   if (nt == 1) {
-    switch (cfg->pe) {
+    switch (framed ? kPeFramed : cfg->pe) {
+      case kPeFramed: LAZYATTN_DECODE(kPeFramed, 1); break;
       case LAZYATTN_PE_ROPE: LAZYATTN_DECODE(LAZYATTN_PE_ROPE, 1); break;
       case LAZYATTN_PE_NONE: LAZYATTN_DECODE(LAZYATTN_PE_NONE, 1); break;
       default: LAZYATTN_DECODE(LAZYATTN_PE_ALIBI, 1); break;
     }
   } else {
-    switch (cfg->pe) {
+    switch (framed ? kPeFramed : cfg->pe) {
+      case kPeFramed: LAZYATTN_DECODE(kPeFramed, 2); break;
       case LAZYATTN_PE_ROPE: LAZYATTN_DECODE(LAZYATTN_PE_ROPE, 2); break;
       case LAZYATTN_PE_NONE: LAZYATTN_DECODE(LAZYATTN_PE_NONE, 2); break;
       default: LAZYATTN_DECODE(LAZYATTN_PE_ALIBI, 2); break;
@@ -1262,6 +1360,23 @@ lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, voi
   return launched();
 }
 
+lazyattn_status lazyattn_append_kv_framed(const lazyattn_config* cfg, void* k_pool, void* v_pool, int64_t num_blocks,
+                                          const void* k_new, const void* v_new, const int64_t* slots,
+                                          const int32_t* frame_index, int32_t n, hipStream_t stream) {
+  lazyattn_status st = check_config(cfg);
+  if (st != LAZYATTN_OK) return st;
+  if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE) return LAZYATTN_EUNSUPPORTED;
+  if (n < 0 || num_blocks < 0) return LAZYATTN_EINVAL;
+  if (n == 0) return LAZYATTN_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slots || !frame_index || num_blocks < 1) return LAZYATTN_EINVAL;
+  if (cfg->num_kv_heads > 65535) return LAZYATTN_EUNSUPPORTED;
+  hipLaunchKernelGGL(append_kv_framed_kernel, dim3(n, cfg->num_kv_heads), dim3(64), 0, stream,
+                     static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slots, frame_index,
+                     cfg->num_kv_heads, cfg->head_dim, make_rope_rev(cfg));
+  return launched();
+}
+
 lazyattn_status lazyattn_materialize_kv(const lazyattn_config* cfg, const void* k_pool, const void* v_pool,
                                         int64_t num_blocks, const lazyattn_batch* batch,
                                         const uint64_t* dst_tables, void* dst_k_pool, void* dst_v_pool,
@@ -1270,6 +1385,7 @@ lazyattn_status lazyattn_materialize_kv(const lazyattn_config* cfg, const void* 
   if (st != LAZYATTN_OK) return st;
   if ((st = check_batch(batch)) != LAZYATTN_OK) return st;
   if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE) return LAZYATTN_EUNSUPPORTED;
+  if (batch->frame_starts) return LAZYATTN_EUNSUPPORTED;     // copies are made from a content-only pool
   if (batch->num_reqs == 0 || batch->max_entries == 0) return LAZYATTN_OK;
   if (!k_pool || !v_pool || !dst_tables || !dst_k_pool || !dst_v_pool || num_blocks < 1 || dst_num_blocks < 1)
     return LAZYATTN_EINVAL;

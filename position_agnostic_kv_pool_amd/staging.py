@@ -48,23 +48,60 @@ class DevicePools:
         self.v[idx] = to_device(vp.data, s.dtype, device)
 
 
+class FramedPools:
+    """K/V pools holding keys in document-local frames (key stored as R(j) k, j
+    its index inside its document), same layouts as DevicePools.  Every
+    referenced document is written through lazyattn_append_kv_framed."""
+
+    def __init__(self, wl, cfg, device="cuda"):
+        s = wl.spec
+        if s.dtype != "bf16":
+            raise ValueError("document-local frames are bf16 only")
+        dt = torch_dtype(s.dtype)
+        nb = wl.num_blocks
+        self.num_blocks = nb
+        self.dtype = s.dtype
+        self.k = torch.full((nb, s.num_kv_heads, s.block_size, s.head_dim), float("nan"), dtype=dt, device=device)
+        self.v = torch.full((nb, s.num_kv_heads, s.head_dim, s.block_size), float("nan"), dtype=dt, device=device)
+        ks, vs, sl, fi = [], [], [], []
+        for d in wl.referenced_docs:
+            k, v = wl.doc_kv(int(d))
+            slots, j = wl.doc_frame_tokens(int(d))
+            ks.append(k)
+            vs.append(v)
+            sl.append(slots)
+            fi.append(j)
+        if ks:
+            chunk = 1 << 16                       # tokens per append call
+            k, v = np.concatenate(ks), np.concatenate(vs)
+            sl, fi = np.concatenate(sl).astype(np.int64), np.concatenate(fi).astype(np.int32)
+            for a in range(0, sl.size, chunk):
+                b = min(sl.size, a + chunk)
+                _abi.append_kv_framed(cfg, self.k, self.v, nb, to_device(k[a:b], s.dtype, device),
+                                      to_device(v[a:b], s.dtype, device), torch.from_numpy(sl[a:b]).to(device),
+                                      torch.from_numpy(fi[a:b]).to(device))
+
+
 class DeviceTables:
-    """Packed block tables plus per-request counts for one call."""
+    """Packed block tables plus per-request counts (and frame starts) for one call."""
 
     def __init__(self, table_blocks: np.ndarray, table_starts: np.ndarray, num_entries: np.ndarray,
-                 ctx_lens: np.ndarray, device="cuda", block_permutation: np.ndarray = None):
+                 ctx_lens: np.ndarray, device="cuda", block_permutation: np.ndarray = None,
+                 frame_starts: np.ndarray = None):
         blocks = table_blocks if block_permutation is None else \
             block_permutation[table_blocks.astype(np.int64)].astype(np.uint32)
         self.words_host = _abi.pack_entries(blocks, table_starts)
         self.tables = torch.from_numpy(self.words_host.view(np.int64)).to(device)
         self.num_entries = torch.from_numpy(np.ascontiguousarray(num_entries, dtype=np.int32)).to(device)
         self.ctx_lens = torch.from_numpy(np.ascontiguousarray(ctx_lens, dtype=np.int32)).to(device)
-        self.batch = _abi.make_batch(self.tables, self.num_entries, self.ctx_lens)
+        self.frame_starts = None if frame_starts is None else \
+            torch.from_numpy(np.ascontiguousarray(frame_starts, dtype=np.int32)).to(device)
+        self.batch = _abi.make_batch(self.tables, self.num_entries, self.ctx_lens, self.frame_starts)
 
     @classmethod
-    def from_inputs(cls, inputs: dict, device="cuda", block_permutation=None):
+    def from_inputs(cls, inputs: dict, device="cuda", block_permutation=None, framed=False):
         return cls(inputs["table_blocks"], inputs["table_starts"], inputs["num_entries"], inputs["ctx_lens"],
-                   device, block_permutation)
+                   device, block_permutation, inputs["frame_starts"] if framed else None)
 
 
 def append_tokens(cfg, pools: DevicePools, inputs: dict, dtype: str, device="cuda", block_permutation=None):
@@ -77,15 +114,20 @@ def append_tokens(cfg, pools: DevicePools, inputs: dict, dtype: str, device="cud
     k = to_device(inputs["k_new"], dtype, device)
     v = to_device(inputs["v_new"], dtype, device)
     sl = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(device)
-    _abi.append_kv(cfg, pools.k, pools.v, pools.num_blocks, k, v, sl)
+    if isinstance(pools, FramedPools):
+        fi = torch.from_numpy(np.ascontiguousarray(inputs["frame_index"], dtype=np.int32)).to(device)
+        _abi.append_kv_framed(cfg, pools.k, pools.v, pools.num_blocks, k, v, sl, fi)
+    else:
+        _abi.append_kv(cfg, pools.k, pools.v, pools.num_blocks, k, v, sl)
 
 
 class PrefillCall:
     """Device inputs and output/workspace buffers of one prefill call."""
 
-    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None):
+    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None,
+                 framed: bool = False):
         self.cfg = cfg
-        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation)
+        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation, framed)
         self.q = to_device(inputs["q"], spec.dtype, device)
         self.cu_q = torch.from_numpy(inputs["cu_q_lens"].astype(np.int32)).to(device)
         self.total_q = int(inputs["total_q"])
@@ -115,9 +157,10 @@ class PrefillCall:
 class DecodeCall:
     """Device inputs and output/workspace buffers of one decode step."""
 
-    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None):
+    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None,
+                 framed: bool = False):
         self.cfg = cfg
-        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation)
+        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation, framed)
         self.q = to_device(inputs["q"], spec.dtype, device)
         self.out = torch.empty_like(self.q)
         self.num_splits = num_splits

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _abi.lib().lazyattn_abi_version() == 2
+    assert _abi.lib().lazyattn_abi_version() == 3
     for s in range(5):
         assert len(_abi.status_string(s)) > 0
     assert _abi.status_string(99) == "unknown status"
@@ -191,6 +191,20 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch():
     assert lib.lazyattn_merge_splits(ctypes.byref(c), 4, 2, P, 4 * 4 * 2 * 130 * 4 - 1, P, None) == _abi.EWORKSPACE
     assert lib.lazyattn_merge_splits(ctypes.byref(c), 4, 1, None, 0, None, None) == _abi.OK
     assert lib.lazyattn_merge_splits(ctypes.byref(c), 0, 3, None, 0, None, None) == _abi.OK
+    # document-local frames: RoPE and bf16 only; the framed append needs its indices
+    bf = _abi.Batch()
+    bf.num_reqs, bf.max_entries = 2, 4
+    bf.block_tables = bf.num_entries = bf.ctx_lens = bf.frame_starts = 16
+    c32 = _cfg(dtype="f32", head_dim=64)
+    assert lib.lazyattn_prefill(ctypes.byref(c32), P, P, 1, 1, P, P, 1, ctypes.byref(bf), 0, P, None, 0, None) == _abi.EUNSUPPORTED
+    assert lib.lazyattn_decode(ctypes.byref(_cfg(pe="alibi")), P, P, P, 1, ctypes.byref(bf), 0, P, None, 0, None) == _abi.EUNSUPPORTED
+    assert lib.lazyattn_decode(ctypes.byref(_cfg(pe="none")), P, P, P, 1, ctypes.byref(bf), 0, P, None, 0, None) == _abi.EUNSUPPORTED
+    assert lib.lazyattn_materialize_kv(ctypes.byref(c), P, P, 1, ctypes.byref(bf), P, P, P, 1, None) == _abi.EUNSUPPORTED
+    assert lib.lazyattn_append_kv_framed(ctypes.byref(c), P, P, 1, P, P, P, None, 3, None) == _abi.EINVAL
+    assert lib.lazyattn_append_kv_framed(ctypes.byref(c), P, P, 1, P, P, P, P, -1, None) == _abi.EINVAL
+    assert lib.lazyattn_append_kv_framed(ctypes.byref(_cfg(pe="none")), P, P, 1, P, P, P, P, 3, None) == _abi.EUNSUPPORTED
+    assert lib.lazyattn_append_kv_framed(ctypes.byref(c32), P, P, 1, P, P, P, P, 3, None) == _abi.EUNSUPPORTED
+    assert lib.lazyattn_append_kv_framed(ctypes.byref(c), None, None, 0, None, None, None, None, 0, None) == _abi.OK
     # malformed batch
     b2 = _abi.Batch()
     b2.num_reqs, b2.max_entries = 1, 0

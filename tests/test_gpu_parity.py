@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 import oracle as O  # noqa: E402
 import workloads as W  # noqa: E402
 from position_agnostic_kv_pool_amd import _abi, staging  # noqa: E402
-from _helpers import OracleState, assert_parity, diff_stats, gpu_f64, within  # noqa: E402
+from _helpers import OracleState, assert_parity, diff_stats, gpu_f64, half_ulp, within  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -392,6 +392,140 @@ def test_materialized_baseline_matches_oracle_and_leaves_the_pool():
     mx, mn = diff_stats(lazy, got)
     say(f"deferred vs materialised: max {mx:.2e} mean {mn:.2e}")
     assert mx <= 1e-2 and mn <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# document-local frames: keys stored as R(j) k, j the index inside their
+# document; the results must be those of the content-only definition
+# ---------------------------------------------------------------------------
+def test_append_kv_framed_rounds_the_exact_rotation():
+    say("framed append: 8B documents written as R(j) k")
+    wl = W.build_workload(W.spec(2, requests=[2]))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.FramedPools(wl, cfg, DEV)
+    sync()
+    inv = O.rope_inv_freq(s.head_dim, s.rope_theta)
+    agree, total = 0, 0
+    for d in wl.referenced_docs[:4]:
+        k, v = wl.doc_kv(int(d))
+        slots, j = wl.doc_frame_tokens(int(d))
+        exact = O.rotate_into_frames(O.bf16_to_f64(k), j, inv)             # [L][Hkv][D]
+        bi = torch.from_numpy(slots // 16).to(DEV)
+        ri = torch.from_numpy(slots % 16).to(DEV)
+        got = gpu_f64(pools.k[bi, :, ri])                                    # [L][Hkv][D]
+        # within half a bf16 ulp of the exact value, plus the float32 rotation
+        # error, which scales with the magnitude of the channel pair
+        kf = O.bf16_to_f64(k)
+        pair = np.sqrt(kf[..., 0::2] ** 2 + kf[..., 1::2] ** 2).repeat(2, axis=-1)
+        excess = np.abs(got - exact) - half_ulp(exact, "bf16") - 1e-6 * pair
+        say(f"framed append doc {int(d)}: worst excess over the bar {excess.max():.3e}")
+        assert excess.max() <= 0
+        rounded = O.bf16_to_f64(W.f32_to_bf16_bits(exact.astype(np.float32)))
+        agree += int(np.sum(got == rounded))
+        total += got.size
+        # values are stored unchanged, bit for bit
+        gv = pools.v[bi, :, :, ri].cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(gv, v)
+        # the rows past the document's end stay poisoned
+        L = k.shape[0]
+        if L % 16:
+            tail = pools.k[int(slots[-1] // 16), :, L % 16:]
+            assert torch.isnan(tail.float()).all()
+    say(f"framed append: {agree}/{total} values equal the rounded exact rotation")
+    assert agree >= 0.999 * total
+
+
+def _framed_prefill(wl, num_splits=0, exact_max=False):
+    s = wl.spec
+    cfg = staging.config_for(s, exact_max=exact_max)
+    pools = staging.FramedPools(wl, cfg, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    out = staging.PrefillCall(cfg, s, pb, DEV, num_splits, framed=True).run(pools)
+    sync()
+    return pb, gpu_f64(out), pools
+
+
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_framed_prefill_llama8b_full(num_splits):
+    say("framed 8B prefill full, splits", num_splits)
+    wl = W.build_workload(W.spec(2))
+    pb, got, _ = _framed_prefill(wl, num_splits)
+    orc = OracleState(wl)
+    orc.append(pb)
+    rng = np.random.default_rng(3)
+    subset = None if num_splits == 0 else \
+        {r: sample_tokens(int(pb["cu_q_lens"][r + 1] - pb["cu_q_lens"][r]), 24, rng) for r in range(len(pb["ctx_lens"]))}
+    compare_prefill(wl, pb, got, orc, token_subset=subset, label=f"framed 8B prefill splits={num_splits}")
+    _, content, _ = run_prefill(wl, num_splits=num_splits, pb=pb)
+    mx, mn = diff_stats(got, content)
+    say(f"framed vs content-only kernel: max {mx:.2e} mean {mn:.2e}")
+
+
+def test_framed_prefill_exact_maximum_route():
+    say("framed 8B prefill, exact-maximum route")
+    wl = W.build_workload(W.spec(2, requests=[3]))
+    pb, got, _ = _framed_prefill(wl, exact_max=True)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="framed 8B prefill exact max")
+
+
+def test_framed_decode_llama8b():
+    say("framed 8B decode: 16 requests, suffix prefill then steps 0, 1, 15, 16, 40")
+    wl = W.build_workload(W.spec(3, requests=[16], n_decode=41))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb, got, pools = _framed_prefill(wl)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="framed 8B suffix prefill")
+    for step in range(41):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+        if step in (0, 1, 15, 16, 40):
+            out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, framed=True).run(pools))
+            ref = orc.decode(d)
+            mx, mn = assert_parity(out, np.stack([ref[r] for r in range(len(ref))]), "bf16",
+                                   f"framed 8B decode {step}")
+            say(f"framed 8B decode step {step}: max {mx:.2e} mean {mn:.2e}")
+
+
+def test_framed_decode_long_context_splits_and_mqa():
+    say("framed decode: 70B 32k step 0 at splits 0, 1, 7, 64; MQA (G = 32) step 0")
+    wl = W.build_workload(W.spec(4, requests=[1], n_decode=1))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.FramedPools(wl, cfg, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    d = wl.decode_step(0)
+    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+    orc = OracleState(wl)
+    orc.append(pb)
+    orc.append(d)
+    ref = orc.decode(d)
+    for splits in (0, 1, 7, 64):
+        out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, num_splits=splits, framed=True).run(pools))
+        mx, mn = assert_parity(out, ref[0][None], "bf16", f"framed 70B decode splits={splits}")
+        say(f"framed 70B decode splits={splits}: max {mx:.2e} mean {mn:.2e}")
+    wl = W.build_workload(W.spec(5, requests=[2, 24], skew=1.2))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.FramedPools(wl, cfg, DEV)
+    staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, DEV)
+    d = wl.decode_step(0)
+    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+    orc = OracleState(wl)
+    orc.append(wl.tokens_before_step(0))
+    orc.append(d)
+    out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, framed=True).run(pools))
+    reqs = list(range(0, len(d["ctx_lens"]), 3))
+    ref = orc.decode(d, requests=reqs)
+    mx, mn = assert_parity(out[reqs], np.stack([ref[r] for r in reqs]), "bf16", "framed MQA decode")
+    say(f"framed MQA decode: max {mx:.2e} mean {mn:.2e}")
 
 
 # ---------------------------------------------------------------------------

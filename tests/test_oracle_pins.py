@@ -382,3 +382,100 @@ def test_plausible_mistakes_exceed_bf16_tolerance_at_long_context():
     swapped = O.attend(q[..., half], qp, K[..., half], V, kp, pe="rope", rope_theta=500000.0)
     for bad in (off_by_one, no_rot, swapped):
         assert np.max(np.abs(bad - ref)) > 1e-2 or np.mean(np.abs(bad - ref)) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# document-local frames: the framed pool gives the content-only results
+# ---------------------------------------------------------------------------
+def _framed_pools(wl, inv_freq, extra=None):
+    """fp64 framed pools of a workload: every referenced document written with
+    its in-document indices, then ``extra`` new tokens with their frame_index."""
+    kp, vp = wl.pools()
+    k64 = np.full(kp.shape, np.nan)
+    v64 = np.full(vp.shape, np.nan)
+    for d in wl.referenced_docs:
+        k, v = wl.doc_kv(int(d))
+        slots, j = wl.doc_frame_tokens(int(d))
+        O.append_kv_framed(k64, v64, k, v, slots, j, wl.B, inv_freq, wl.spec.dtype)
+    if extra is not None:
+        O.append_kv_framed(k64, v64, extra["k_new"], extra["v_new"], extra["slots"], extra["frame_index"],
+                           wl.B, inv_freq, wl.spec.dtype)
+    return k64, v64
+
+
+def test_framed_pool_equals_content_pool_tiny():
+    import workloads as W
+    wl = W.build_workload(W.spec(1))
+    s = wl.spec
+    inv_freq = O.rope_inv_freq(s.head_dim, s.rope_theta)
+    pb = wl.prefill_batch()
+    kc, vc = wl.pools()
+    kc, vc = kc.dense(), vc.dense()
+    O.append_kv(kc, vc, pb["k_new"], pb["v_new"], pb["slots"], wl.B)
+    kf, vf = _framed_pools(wl, inv_freq, pb)
+    words = O.pack_table(pb["table_blocks"], pb["table_starts"])
+    common = dict(q=pb["q"], cu_q_lens=pb["cu_q_lens"], ctx_lens=pb["ctx_lens"],
+                  num_entries=pb["num_entries"], table_words=words, block_size=wl.B, dtype=s.dtype,
+                  rope_theta=s.rope_theta)
+    ref = O.prefill(k_pool=kc, v_pool=vc, num_kv_heads=s.num_kv_heads, pe="rope", **common)
+    got = O.prefill_framed(k_pool=kf, v_pool=vf, frame_starts=pb["frame_starts"], **common)
+    for r in ref:
+        np.testing.assert_allclose(got[r], ref[r], rtol=0, atol=1e-12)
+    # the frames differ from 0 and from the positions: the check is not vacuous
+    fs = pb["frame_starts"][0, :int(pb["num_entries"][0])]
+    assert len(set(fs.tolist())) > 2 and fs[0] == 0
+    # one decode step (its token appended with frame index q_len)
+    ds = wl.decode_step(0)
+    O.append_kv(kc, vc, ds["k_new"], ds["v_new"], ds["slots"], wl.B)
+    O.append_kv_framed(kf, vf, ds["k_new"], ds["v_new"], ds["slots"], ds["frame_index"], wl.B, inv_freq, s.dtype)
+    words = O.pack_table(ds["table_blocks"], ds["table_starts"])
+    common = dict(q=ds["q"], ctx_lens=ds["ctx_lens"], num_entries=ds["num_entries"], table_words=words,
+                  block_size=wl.B, dtype=s.dtype, rope_theta=s.rope_theta)
+    ref = O.decode(k_pool=kc, v_pool=vc, num_kv_heads=s.num_kv_heads, pe="rope", **common)
+    got = O.decode_framed(k_pool=kf, v_pool=vf, frame_starts=ds["frame_starts"], **common)
+    for r in ref:
+        np.testing.assert_allclose(got[r], ref[r], rtol=0, atol=1e-12)
+
+
+def test_framed_planted_frame_mistakes_are_seen():
+    # a frame start off by one for one document, or the frames ignored (every
+    # key read as if stored at its absolute position), moves the output far
+    # beyond the bf16 tolerance
+    import workloads as W
+    wl = W.build_workload(W.spec(1))
+    s = wl.spec
+    inv_freq = O.rope_inv_freq(s.head_dim, s.rope_theta)
+    pb = wl.prefill_batch()
+    kf, vf = _framed_pools(wl, inv_freq, pb)
+    words = O.pack_table(pb["table_blocks"], pb["table_starts"])
+    common = dict(q=pb["q"], cu_q_lens=pb["cu_q_lens"], ctx_lens=pb["ctx_lens"],
+                  num_entries=pb["num_entries"], table_words=words, k_pool=kf, v_pool=vf,
+                  block_size=wl.B, dtype=s.dtype, rope_theta=s.rope_theta, requests=[0])
+    good = O.prefill_framed(frame_starts=pb["frame_starts"], **common)[0]
+    fs = pb["frame_starts"].copy()
+    fs[0, 2:4] += 1                          # the second document's two entries
+    bad = O.prefill_framed(frame_starts=fs, **common)[0]
+    assert np.max(np.abs(bad - good)) > 2e-2
+    ignored = O.prefill_framed(frame_starts=np.zeros_like(pb["frame_starts"]), **common)[0]
+    assert np.max(np.abs(ignored - good)) > 2e-2
+
+
+def test_framed_two_channel_closed_form():
+    # D = 2, inv_freq = 1: a key stored at frame index j = t - F and a query at
+    # p give the score cos/sin of (t - p) exactly as the unframed rotation does
+    q = np.array([[[0.7, -0.2]]])                      # [M=1][H=1][D=2]
+    k = np.array([[[1.0, 0.5]], [[-0.3, 0.8]]])       # two keys
+    v = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    t = np.array([3, 9])
+    F = np.array([1, 6])                               # two different frames
+    kf = O.rotate_into_frames(k, t - F, np.array([1.0]))
+    out = O.attend_framed(q, np.array([9]), kf, v, t, F, rope_theta=1.0, softmax_scale=1.0)
+    # hand: score_t = q . R(t - p) k with R(a) = [[cos a, -sin a], [sin a, cos a]]
+    z = []
+    for tt, kk in zip(t, k[:, 0]):
+        a = float(tt - 9)
+        rk = np.array([math.cos(a) * kk[0] - math.sin(a) * kk[1], math.sin(a) * kk[0] + math.cos(a) * kk[1]])
+        z.append(float(q[0, 0] @ rk))
+    w = np.exp(np.array(z) - max(z))
+    w /= w.sum()
+    np.testing.assert_allclose(out[0, 0], w, rtol=0, atol=1e-15)

@@ -420,12 +420,36 @@ class Workload:
             starts[i, :q.entry_starts.size] = q.entry_starts
         return blocks, starts
 
+    def frame_arrays(self, reqs: Sequence[RequestLayout]) -> np.ndarray:
+        """Frame start of every table entry, int32 [R][E_max], for a pool in
+        document-local frames: a document's entries carry the document's first
+        logical position in that request, the request's private entries carry
+        the first position after its documents (ctx_docs).  Padding: 0."""
+        e_max = max(int(q.entry_blocks.size) for q in reqs)
+        out = np.zeros((len(reqs), e_max), dtype=np.int32)
+        for i, q in enumerate(reqs):
+            col, pos = 0, 0
+            for L in q.doc_lens:
+                nb = (int(L) + self.B - 1) // self.B
+                out[i, col:col + nb] = pos
+                col += nb
+                pos += int(L)
+            out[i, col:q.entry_blocks.size] = q.ctx_docs
+        return out
+
+    def doc_frame_tokens(self, d: int):
+        """(slots, frame_index) of document d's tokens: pool slot block * B + row, and
+        the token's index within the document."""
+        L = int(self.doc_lens[d])
+        j = np.arange(L, dtype=np.int64)
+        return self.doc_blocks(int(d))[j // self.B] * self.B + j % self.B, j.astype(np.int32)
+
     def prefill_batch(self) -> dict:
         """Inputs of one prefill call over every request with a query suffix."""
         reqs = [q for q in self.requests if q.q_len > 0]
         if not reqs:
             return None
-        qs, ks, vs, slots = [], [], [], []
+        qs, ks, vs, slots, fidx = [], [], [], [], []
         for q in reqs:
             rq = self._phase_rng(4, q.index, 0)
             qs.append(self._values(rq, (q.q_len, self.Hq, self.D)))
@@ -435,16 +459,17 @@ class Workload:
             for i in range(q.q_len):
                 b, row = self.new_token_slot(q, i)
                 slots.append(b * self.B + row)
+                fidx.append(i)
         q_lens = np.array([q.q_len for q in reqs], dtype=np.int32)
         blocks, starts = self.table_arrays(reqs)
         return dict(
             requests=reqs,
             q=np.concatenate(qs), k_new=np.concatenate(ks), v_new=np.concatenate(vs),
-            slots=np.asarray(slots, dtype=np.int64),
+            slots=np.asarray(slots, dtype=np.int64), frame_index=np.asarray(fidx, dtype=np.int32),
             cu_q_lens=np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32),
             ctx_lens=np.array([q.ctx_docs + q.q_len for q in reqs], dtype=np.int32),
             num_entries=np.array([q.num_entries_after(q.q_len) for q in reqs], dtype=np.int32),
-            table_blocks=blocks, table_starts=starts,
+            table_blocks=blocks, table_starts=starts, frame_starts=self.frame_arrays(reqs),
             max_q_len=int(q_lens.max()), total_q=int(q_lens.sum()),
         )
 
@@ -452,7 +477,7 @@ class Workload:
         """Every new token of the decode requests written before decode step ``step``:
         their prefill suffix and decode steps 0..step-1, as one batch of (k, v, slots)."""
         reqs = self.decode_requests(step)
-        ks, vs, slots = [], [], []
+        ks, vs, slots, fidx = [], [], [], []
         for q in reqs:
             if q.q_len > 0:
                 rk = self._phase_rng(5, q.index, 0)
@@ -461,16 +486,18 @@ class Workload:
                 for i in range(q.q_len):
                     b, row = self.new_token_slot(q, i)
                     slots.append(b * self.B + row)
+                    fidx.append(i)
             for s in range(step):
                 rk = self._phase_rng(5, q.index, 1 + s)
                 ks.append(self._values(rk, (1, self.Hkv, self.D)))
                 vs.append(self._values(rk, (1, self.Hkv, self.D)))
                 b, row = self.new_token_slot(q, q.q_len + s)
                 slots.append(b * self.B + row)
+                fidx.append(q.q_len + s)
         if not slots:
             return None
         return dict(k_new=np.concatenate(ks), v_new=np.concatenate(vs),
-                    slots=np.asarray(slots, dtype=np.int64))
+                    slots=np.asarray(slots, dtype=np.int64), frame_index=np.asarray(fidx, dtype=np.int32))
 
     def decode_requests(self, step: int) -> list:
         return [q for q in self.requests if q.n_decode > step]
@@ -495,9 +522,10 @@ class Workload:
             requests=reqs,
             q=np.stack(qs), k_new=np.stack(ks), v_new=np.stack(vs),
             slots=np.asarray(slots, dtype=np.int64),
+            frame_index=np.array([q.q_len + step for q in reqs], dtype=np.int32),
             ctx_lens=np.array([q.ctx_docs + n for q, n in zip(reqs, n_new)], dtype=np.int32),
             num_entries=np.array([q.num_entries_after(n) for q, n in zip(reqs, n_new)], dtype=np.int32),
-            table_blocks=blocks, table_starts=starts,
+            table_blocks=blocks, table_starts=starts, frame_starts=self.frame_arrays(reqs),
         )
 
 
