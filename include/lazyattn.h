@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LAZYATTN_ABI_VERSION 3
+#define LAZYATTN_ABI_VERSION 4
 
 typedef enum {
   LAZYATTN_OK = 0,
@@ -92,6 +92,11 @@ typedef struct {
   float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
   int32_t flags;          /* LAZYATTN_FLAG_* bits; other bits must be 0 */
   const float* alibi_slopes;  /* device [Hq], or NULL => 2^(-8(h+1)/Hq) */
+  const double* rope_inv_freq; /* host [head_dim/2]: angular frequency (radians per position) of
+                                * channel pair i, or NULL => rope_theta^(-2i/head_dim).  Each value
+                                * finite and >= 0; a 0 leaves its pair unrotated (partial rotary).
+                                * Read during the call only; rope_theta is then not used.  RoPE
+                                * variants: gist.science, Key Contributions > Generalizability. */
 } lazyattn_config;
 
 /* Key frames.  With frame_starts == NULL the pool holds content-only keys
@@ -118,6 +123,25 @@ typedef struct {
 
 /* Interface version; equals LAZYATTN_ABI_VERSION of the built library. */
 int32_t lazyattn_abi_version(void);
+
+/* RoPE frequency tables for lazyattn_config.rope_inv_freq (host, out [head_dim/2]).
+ *
+ * lazyattn_rope_inv_freq: partial rotary.  Pair i < rotary_dim/2 gets
+ * theta^(-2i/rotary_dim), the remaining pairs 0 (unrotated).  rotary_dim even,
+ * 2 <= rotary_dim <= head_dim; rotary_dim == head_dim is plain RoPE.
+ *
+ * lazyattn_rope_inv_freq_llama31: the frequency rescaling published with the
+ * Llama 3.1 models.  Base frequency f_i = theta^(-2i/head_dim) with wavelength
+ * w = 2 pi / f_i: kept if w < original_max_position / high_freq_factor,
+ * divided by factor if w > original_max_position / low_freq_factor, and in
+ * between blended linearly in s = (original_max_position / w - low) /
+ * (high - low) from f_i / factor (s = 0) to f_i (s = 1).  Requires factor >= 1,
+ * 0 < low_freq_factor < high_freq_factor, original_max_position >= 1.
+ *
+ * Both return LAZYATTN_EINVAL on a null out or out-of-range argument. */
+lazyattn_status lazyattn_rope_inv_freq(int32_t head_dim, int32_t rotary_dim, double theta, double* out);
+lazyattn_status lazyattn_rope_inv_freq_llama31(int32_t head_dim, double theta, double factor, double low_freq_factor,
+                                               double high_freq_factor, int32_t original_max_position, double* out);
 
 /* Static string naming a status; never NULL. */
 const char* lazyattn_status_string(lazyattn_status s);

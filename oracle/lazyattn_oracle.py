@@ -66,7 +66,7 @@ __all__ = [
     "gather_context", "attend", "prefill", "decode", "append_kv",
     "brute_force_attention", "rotation_flop_fraction", "tile_flop_counts",
     "rotate_into_frames", "append_kv_framed", "token_frames", "attend_framed", "prefill_framed",
-    "decode_framed",
+    "decode_framed", "rope_inv_freq_partial", "rope_inv_freq_llama31",
 ]
 
 
@@ -160,6 +160,40 @@ def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
     return np.power(float(theta), -2.0 * i / head_dim)
 
 
+def rope_inv_freq_partial(head_dim: int, rotary_dim: int, theta: float) -> np.ndarray:
+    """Partial rotary: the first rotary_dim/2 pairs use theta^(-2i/rotary_dim), the rest do not turn.
+
+    ([gist:Key Contributions] names RoPE variants as compatible.)  rotary_dim == head_dim is plain RoPE.
+    """
+    f = np.zeros(head_dim // 2, dtype=np.float64)
+    i = np.arange(rotary_dim // 2, dtype=np.float64)
+    f[:rotary_dim // 2] = np.power(float(theta), -2.0 * i / rotary_dim)
+    return f
+
+
+def rope_inv_freq_llama31(head_dim: int, theta: float, factor: float, low_freq_factor: float,
+                          high_freq_factor: float, original_max_position: int) -> np.ndarray:
+    """The frequency rescaling published with the Llama 3.1 models, written per pair from its definition.
+
+    A base frequency f (wavelength 2 pi / f) is kept when its wavelength is shorter than
+    original_max_position / high_freq_factor, divided by ``factor`` when longer than
+    original_max_position / low_freq_factor, and otherwise blended linearly between f / factor and f
+    with weight s = (original_max_position / wavelength - low_freq_factor) / (high_freq_factor - low_freq_factor).
+    """
+    base = rope_inv_freq(head_dim, theta)
+    out = np.empty_like(base)
+    for i, f in enumerate(base):
+        wavelength = 2.0 * math.pi / f
+        if wavelength < original_max_position / high_freq_factor:
+            out[i] = f
+        elif wavelength > original_max_position / low_freq_factor:
+            out[i] = f / factor
+        else:
+            s = (original_max_position / wavelength - low_freq_factor) / (high_freq_factor - low_freq_factor)
+            out[i] = (1.0 - s) * f / factor + s * f
+    return out
+
+
 def rope_rotate(x: np.ndarray, pos, inv_freq: np.ndarray) -> np.ndarray:
     """Rotate each interleaved channel pair (2i, 2i+1) of x[..., D] by pos * inv_freq_i.
 
@@ -221,11 +255,13 @@ def gather_context(words, n_entries, ctx_len, k_pool, v_pool, block_size, dtype)
 def attend(q: np.ndarray, q_pos: np.ndarray, K: np.ndarray, V: np.ndarray, k_pos: np.ndarray, *,
            pe: str, rope_theta: float = 10000.0, softmax_scale: Optional[float] = None,
            slopes: Optional[np.ndarray] = None, formulation: str = "materialized",
-           heads: Optional[Sequence[int]] = None, return_weights: bool = False):
+           heads: Optional[Sequence[int]] = None, return_weights: bool = False,
+           inv_freq: Optional[np.ndarray] = None):
     """Causal attention of queries q [M][Hq][D] at positions q_pos over keys K, V [L][Hkv][D].
 
     Returns out [M][Hq][D] (only ``heads`` if given, in that order along
-    axis 1) and, if asked, the weights [M][H][L].
+    axis 1) and, if asked, the weights [M][H][L].  ``inv_freq`` [D/2]
+    replaces the theta^(-2i/D) table (RoPE variants).
     """
     q = np.asarray(q, dtype=np.float64)
     M, Hq, D = q.shape
@@ -233,7 +269,7 @@ def attend(q: np.ndarray, q_pos: np.ndarray, K: np.ndarray, V: np.ndarray, k_pos
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(D) if not softmax_scale else float(softmax_scale)
     heads = list(range(Hq)) if heads is None else list(heads)
-    inv_freq = rope_inv_freq(D, rope_theta)
+    inv_freq = rope_inv_freq(D, rope_theta) if inv_freq is None else np.asarray(inv_freq, dtype=np.float64)
     if pe == "alibi" and slopes is None:
         slopes = alibi_slopes(Hq)
     q_pos = np.asarray(q_pos, dtype=np.int64)
@@ -283,7 +319,7 @@ def prefill(*, q, cu_q_lens, ctx_lens, num_entries, table_words, k_pool, v_pool,
             num_kv_heads: int, block_size: int, dtype: str, pe: str, rope_theta: float,
             softmax_scale: Optional[float] = None, slopes=None, formulation: str = "materialized",
             requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
-            token_subset: Optional[dict] = None) -> dict:
+            token_subset: Optional[dict] = None, inv_freq: Optional[np.ndarray] = None) -> dict:
     """Causal prefill of each request's new tokens over its whole context.
 
     q [total_q][Hq][D]; request r owns rows cu_q_lens[r]..cu_q_lens[r+1]-1,
@@ -305,14 +341,15 @@ def prefill(*, q, cu_q_lens, ctx_lens, num_entries, table_words, k_pool, v_pool,
         qpos = L - M + local
         res[r] = attend(qf[a + local], qpos, K, V, kp, pe=pe, rope_theta=rope_theta,
                         softmax_scale=softmax_scale, slopes=slopes,
-                        formulation=formulation, heads=heads)
+                        formulation=formulation, heads=heads, inv_freq=inv_freq)
     return res
 
 
 def decode(*, q, ctx_lens, num_entries, table_words, k_pool, v_pool,
            num_kv_heads: int, block_size: int, dtype: str, pe: str, rope_theta: float,
            softmax_scale: Optional[float] = None, slopes=None, formulation: str = "materialized",
-           requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None) -> dict:
+           requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
+           inv_freq: Optional[np.ndarray] = None) -> dict:
     """One decode step: request r's single query q[r] [Hq][D] sits at position ctx_lens[r]-1."""
     qf = to_f64(q, dtype)
     reqs = range(len(ctx_lens)) if requests is None else requests
@@ -322,7 +359,7 @@ def decode(*, q, ctx_lens, num_entries, table_words, k_pool, v_pool,
         K, V, kp = gather_context(words, n_ent, L, k_pool, v_pool, block_size, dtype)
         res[r] = attend(qf[r][None], np.array([L - 1]), K, V, kp, pe=pe, rope_theta=rope_theta,
                         softmax_scale=softmax_scale, slopes=slopes,
-                        formulation=formulation, heads=heads)[0]
+                        formulation=formulation, heads=heads, inv_freq=inv_freq)[0]
     return res
 
 

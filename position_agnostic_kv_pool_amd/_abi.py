@@ -42,6 +42,7 @@ class Config(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("flags", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
+        ("rope_inv_freq", ctypes.c_void_p),
     ]
 
 
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
             "lazyattn_debug_decode_tables": (I32, [BP, P, P]),
             "lazyattn_materialize_kv": (I32, [CP, P, P, I64, BP, P, P, P, I64, P]),
             "lazyattn_rotate_queries": (I32, [CP, P, P, I32, I32, BP, P, P]),
+            "lazyattn_rope_inv_freq": (I32, [I32, I32, ctypes.c_double, P]),
+            "lazyattn_rope_inv_freq_llama31": (I32, [I32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                                     ctypes.c_double, I32, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -115,7 +119,8 @@ def _check(status: int, where: str):
 # ---------------------------------------------------------------------------
 def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str = "bf16", pe: str = "rope",
                 rope_theta: float = 10000.0, softmax_scale: float = 0.0, alibi_slopes=None,
-                block_size: int = 16, exact_max: bool = False) -> Config:
+                block_size: int = 16, exact_max: bool = False, inv_freq: np.ndarray = None) -> Config:
+    """inv_freq: optional host float64 [head_dim/2] RoPE frequency table (kept alive by the config)."""
     c = Config()
     c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size = num_q_heads, num_kv_heads, head_dim, block_size
     c.dtype = _DT[dtype] if isinstance(dtype, str) else int(dtype)
@@ -124,8 +129,32 @@ def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str =
     c.softmax_scale = float(softmax_scale)
     c.flags = FLAG_EXACT_MAX if exact_max else 0
     c.alibi_slopes = _ptr(alibi_slopes) if alibi_slopes is not None else None
-    c._keep = alibi_slopes
+    f = None
+    if inv_freq is not None:
+        f = np.ascontiguousarray(inv_freq, dtype=np.float64)
+        if f.shape != (head_dim // 2,):
+            raise ValueError(f"inv_freq must hold head_dim/2 = {head_dim // 2} values")
+    c.rope_inv_freq = f.ctypes.data if f is not None else None
+    c._keep = (alibi_slopes, f)
     return c
+
+
+def rope_inv_freq(head_dim: int, rotary_dim: int, theta: float) -> np.ndarray:
+    """Partial-rotary frequency table from the library (pairs past rotary_dim/2 are 0)."""
+    out = np.empty(head_dim // 2, dtype=np.float64)
+    _check(lib().lazyattn_rope_inv_freq(int(head_dim), int(rotary_dim), float(theta), out.ctypes.data),
+           "rope_inv_freq")
+    return out
+
+
+def rope_inv_freq_llama31(head_dim: int, theta: float, factor: float, low_freq_factor: float,
+                          high_freq_factor: float, original_max_position: int) -> np.ndarray:
+    """Llama 3.1 rescaled frequency table from the library."""
+    out = np.empty(head_dim // 2, dtype=np.float64)
+    _check(lib().lazyattn_rope_inv_freq_llama31(int(head_dim), float(theta), float(factor), float(low_freq_factor),
+                                                float(high_freq_factor), int(original_max_position),
+                                                out.ctypes.data), "rope_inv_freq_llama31")
+    return out
 
 
 def pack_entries(blocks: np.ndarray, starts: np.ndarray) -> np.ndarray:

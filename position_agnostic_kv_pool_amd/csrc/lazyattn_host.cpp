@@ -19,13 +19,19 @@ lazyattn_status check_config(const lazyattn_config* cfg) {
   if (cfg->dtype != LAZYATTN_F32 && cfg->dtype != LAZYATTN_BF16) return LAZYATTN_EINVAL;
   if (cfg->pe != LAZYATTN_PE_ROPE && cfg->pe != LAZYATTN_PE_NONE && cfg->pe != LAZYATTN_PE_ALIBI)
     return LAZYATTN_EINVAL;
-  if (cfg->pe == LAZYATTN_PE_ROPE && !(cfg->rope_theta > 0.0)) return LAZYATTN_EINVAL;
+  if (cfg->pe == LAZYATTN_PE_ROPE && !cfg->rope_inv_freq && !(cfg->rope_theta > 0.0)) return LAZYATTN_EINVAL;
   if (!(cfg->softmax_scale >= 0.0f) || isinf(cfg->softmax_scale)) return LAZYATTN_EINVAL;
   if (cfg->head_dim < 1 || cfg->block_size < 1) return LAZYATTN_EINVAL;
   if (cfg->block_size != kBlock) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_BF16 && cfg->head_dim != 128) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32 && cfg->head_dim != 64 && cfg->head_dim != 128)
     return LAZYATTN_EUNSUPPORTED;
+  if (cfg->rope_inv_freq) {
+    for (int i = 0; i < cfg->head_dim / 2; ++i) {
+      const double f = cfg->rope_inv_freq[i];
+      if (!(f >= 0.0) || isinf(f)) return LAZYATTN_EINVAL;
+    }
+  }
   return LAZYATTN_OK;
 }
 
@@ -34,8 +40,10 @@ RopeRev make_rope_rev(const lazyattn_config* cfg) {
   const int pairs = cfg->head_dim / 2;
   const double two_pi = 6.283185307179586476925286766559;
   for (int i = 0; i < pairs && i < kMaxPairs; ++i) {
-    double inv_freq = pow(cfg->rope_theta > 0.0 ? cfg->rope_theta : 1.0,
-                          -2.0 * static_cast<double>(i) / static_cast<double>(cfg->head_dim));
+    const double inv_freq = cfg->rope_inv_freq
+                                ? cfg->rope_inv_freq[i]
+                                : pow(cfg->rope_theta > 0.0 ? cfg->rope_theta : 1.0,
+                                      -2.0 * static_cast<double>(i) / static_cast<double>(cfg->head_dim));
     r.rev[i] = inv_freq / two_pi;
   }
   return r;
@@ -93,6 +101,38 @@ using namespace lazyattn;
 extern "C" {
 
 int32_t lazyattn_abi_version(void) { return LAZYATTN_ABI_VERSION; }
+
+lazyattn_status lazyattn_rope_inv_freq(int32_t head_dim, int32_t rotary_dim, double theta, double* out) {
+  if (!out || head_dim < 2 || head_dim % 2 != 0 || rotary_dim < 2 || rotary_dim % 2 != 0 || rotary_dim > head_dim ||
+      !(theta > 0.0) || isinf(theta))
+    return LAZYATTN_EINVAL;
+  for (int i = 0; i < head_dim / 2; ++i)
+    out[i] = (2 * i < rotary_dim) ? pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(rotary_dim)) : 0.0;
+  return LAZYATTN_OK;
+}
+
+lazyattn_status lazyattn_rope_inv_freq_llama31(int32_t head_dim, double theta, double factor, double low_freq_factor,
+                                               double high_freq_factor, int32_t original_max_position, double* out) {
+  if (!out || head_dim < 2 || head_dim % 2 != 0 || !(theta > 0.0) || isinf(theta) || !(factor >= 1.0) ||
+      isinf(factor) || !(low_freq_factor > 0.0) || !(high_freq_factor > low_freq_factor) ||
+      isinf(high_freq_factor) || original_max_position < 1)
+    return LAZYATTN_EINVAL;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double ctx = static_cast<double>(original_max_position);
+  for (int i = 0; i < head_dim / 2; ++i) {
+    const double f = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(head_dim));
+    const double wavelength = two_pi / f;
+    if (wavelength < ctx / high_freq_factor) {
+      out[i] = f;                                  // short wavelengths: unchanged
+    } else if (wavelength > ctx / low_freq_factor) {
+      out[i] = f / factor;                         // long wavelengths: stretched by the factor
+    } else {
+      const double s = (ctx / wavelength - low_freq_factor) / (high_freq_factor - low_freq_factor);
+      out[i] = (1.0 - s) * (f / factor) + s * f;
+    }
+  }
+  return LAZYATTN_OK;
+}
 
 const char* lazyattn_status_string(lazyattn_status s) {
   switch (s) {

@@ -24,10 +24,11 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
 
 
-def config_for(spec, pe: str = None, softmax_scale: float = 0.0, exact_max: bool = False) -> _abi.Config:
+def config_for(spec, pe: str = None, softmax_scale: float = 0.0, exact_max: bool = False,
+               inv_freq: np.ndarray = None) -> _abi.Config:
     return _abi.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype,
                             pe or spec.pe, spec.rope_theta, softmax_scale, block_size=spec.block_size,
-                            exact_max=exact_max)
+                            exact_max=exact_max, inv_freq=inv_freq)
 
 
 class DevicePools:

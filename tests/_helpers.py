@@ -64,7 +64,7 @@ class OracleState:
         return O.pack_table(inputs["table_blocks"], inputs["table_starts"])
 
     def prefill(self, inputs, token_subset=None, requests=None, pe=None, heads=None, q_shift=0,
-                pair_perm=None):
+                pair_perm=None, inv_freq=None):
         """Oracle prefill outputs {r: [tokens][heads][D]}; q_shift / pair_perm plant mistakes (controls)."""
         s = self.wl.spec
         words = self.words(inputs)
@@ -78,7 +78,7 @@ class OracleState:
         return O.prefill(q=q, cu_q_lens=inputs["cu_q_lens"], ctx_lens=ctx, num_entries=inputs["num_entries"],
                          table_words=words, k_pool=kp, v_pool=vp, num_kv_heads=s.num_kv_heads,
                          block_size=s.block_size, dtype=s.dtype, pe=pe or s.pe, rope_theta=s.rope_theta,
-                         requests=requests, heads=heads, token_subset=token_subset)
+                         requests=requests, heads=heads, token_subset=token_subset, inv_freq=inv_freq)
 
     def _contexts(self, inputs, r):
         s = self.wl.spec
@@ -114,12 +114,12 @@ class OracleState:
                               rope_theta=s.rope_theta, heads=heads)
         return res
 
-    def decode(self, inputs, requests=None, pe=None):
+    def decode(self, inputs, requests=None, pe=None, inv_freq=None):
         s = self.wl.spec
         return O.decode(q=inputs["q"], ctx_lens=inputs["ctx_lens"], num_entries=inputs["num_entries"],
                         table_words=self.words(inputs), k_pool=self.k, v_pool=self.v,
                         num_kv_heads=s.num_kv_heads, block_size=s.block_size, dtype=s.dtype, pe=pe or s.pe,
-                        rope_theta=s.rope_theta, requests=requests)
+                        rope_theta=s.rope_theta, requests=requests, inv_freq=inv_freq)
 
 
 def gpu_f64(t) -> np.ndarray:

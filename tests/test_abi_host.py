@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _abi.lib().lazyattn_abi_version() == 3
+    assert _abi.lib().lazyattn_abi_version() == 4
     for s in range(5):
         assert len(_abi.status_string(s)) > 0
     assert _abi.status_string(99) == "unknown status"
@@ -215,3 +215,31 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch():
     assert lib.lazyattn_decode(ctypes.byref(c), None, None, None, 0, ctypes.byref(b0), 0, None, None, 0, None) == _abi.OK
     assert lib.lazyattn_prefill(ctypes.byref(c), None, None, 0, 0, None, None, 0, ctypes.byref(b), 0, None, None, 0, None) == _abi.OK
     assert lib.lazyattn_append_kv(ctypes.byref(c), None, None, 0, None, None, None, 0, None) == _abi.OK
+
+
+def test_rope_frequency_tables_match_the_oracle():
+    import oracle as O
+    for D, rd, th in ((128, 128, 5e5), (128, 64, 1e4), (64, 32, 1e4), (128, 2, 10.0)):
+        np.testing.assert_allclose(_abi.rope_inv_freq(D, rd, th), O.rope_inv_freq_partial(D, rd, th), rtol=1e-14)
+    for args in ((128, 5e5, 8.0, 1.0, 4.0, 8192), (128, 5e5, 1.0, 1.0, 4.0, 8192), (64, 1e4, 4.0, 2.0, 8.0, 2048)):
+        np.testing.assert_allclose(_abi.rope_inv_freq_llama31(*args), O.rope_inv_freq_llama31(*args), rtol=1e-14)
+    lib = _abi.lib()
+    out = np.empty(64)
+    bad = [(128, 0, 1e4), (128, 3, 1e4), (128, 130, 1e4), (128, 64, 0.0), (127, 64, 1e4)]
+    for D, rd, th in bad:
+        assert lib.lazyattn_rope_inv_freq(D, rd, th, out.ctypes.data) == _abi.EINVAL
+    assert lib.lazyattn_rope_inv_freq(128, 64, 1e4, None) == _abi.EINVAL
+    assert lib.lazyattn_rope_inv_freq_llama31(128, 5e5, 0.5, 1.0, 4.0, 8192, out.ctypes.data) == _abi.EINVAL
+    assert lib.lazyattn_rope_inv_freq_llama31(128, 5e5, 8.0, 4.0, 4.0, 8192, out.ctypes.data) == _abi.EINVAL
+    assert lib.lazyattn_rope_inv_freq_llama31(128, 5e5, 8.0, 1.0, 4.0, 0, out.ctypes.data) == _abi.EINVAL
+
+
+def test_config_frequency_table_checks():
+    lib = _abi.lib()
+    check = lambda c: lib.lazyattn_prefill_splits(ctypes.byref(c), 1, 1, 1) > 0
+    good = _cfg(rope_theta=0.0, inv_freq=np.linspace(1.0, 0.0, 64))     # theta unused with a table
+    assert check(good)
+    assert not check(_cfg(rope_theta=0.0))
+    assert not check(_cfg(inv_freq=np.full(64, -1.0)))
+    assert not check(_cfg(inv_freq=np.full(64, np.inf)))
+    assert not check(_cfg(inv_freq=np.full(64, np.nan)))

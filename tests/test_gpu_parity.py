@@ -529,6 +529,66 @@ def test_framed_decode_long_context_splits_and_mqa():
 
 
 # ---------------------------------------------------------------------------
+# RoPE variants: a caller-supplied frequency table (Llama 3.1 rescaling,
+# partial rotary), content-only and framed pools
+# ---------------------------------------------------------------------------
+_VARIANTS = {
+    "llama31": lambda s: O.rope_inv_freq_llama31(s.head_dim, s.rope_theta, 8.0, 1.0, 4.0, 8192),
+    "partial64": lambda s: O.rope_inv_freq_partial(s.head_dim, 64, s.rope_theta),
+}
+
+
+@pytest.mark.parametrize("variant", sorted(_VARIANTS))
+def test_rope_variants_prefill_and_decode(variant):
+    say(f"RoPE variant {variant}: 8B prefill (3 requests), decode steps 0 and 5 (8 requests), framed decode")
+    wl = W.build_workload(W.spec(2, requests=[3]))
+    s = wl.spec
+    table = _VARIANTS[variant](s)
+    # the library's own table generator gives the same frequencies
+    lib_table = _abi.rope_inv_freq_llama31(s.head_dim, s.rope_theta, 8.0, 1.0, 4.0, 8192) \
+        if variant == "llama31" else _abi.rope_inv_freq(s.head_dim, 64, s.rope_theta)
+    np.testing.assert_allclose(lib_table, table, rtol=1e-14)
+    cfg = staging.config_for(s, inv_freq=lib_table)
+    pb = wl.prefill_batch()
+    pools = staging.DevicePools(wl, DEV)
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    got = gpu_f64(staging.PrefillCall(cfg, s, pb, DEV).run(pools))
+    orc = OracleState(wl)
+    orc.append(pb)
+    ref = orc.prefill(pb, inv_freq=table)
+    cu = pb["cu_q_lens"]
+    mx, mn = assert_parity(np.concatenate([got[cu[r]:cu[r + 1]] for r in ref]),
+                           np.concatenate([ref[r] for r in ref]), "bf16", f"{variant} prefill")
+    say(f"{variant} prefill: max {mx:.2e} mean {mn:.2e}")
+    # the variant matters: plain RoPE is far from it
+    plain = orc.prefill(pb, requests=[0])[0]
+    assert np.max(np.abs(plain - ref[0])) > 5e-2
+
+    wl = W.build_workload(W.spec(3, requests=[8], n_decode=6))
+    s = wl.spec
+    pools = staging.DevicePools(wl, DEV)
+    fpools = staging.FramedPools(wl, cfg, DEV)
+    orc = OracleState(wl)
+    for inp in (wl.tokens_before_step(0),):
+        staging.append_tokens(cfg, pools, inp, s.dtype, DEV)
+        staging.append_tokens(cfg, fpools, inp, s.dtype, DEV)
+        orc.append(inp)
+    for step in range(6):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        staging.append_tokens(cfg, fpools, d, s.dtype, DEV)
+        orc.append(d)
+        if step in (0, 5):
+            ref = orc.decode(d, inv_freq=table)
+            ref = np.stack([ref[r] for r in range(len(ref))])
+            out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+            mx, mn = assert_parity(out, ref, "bf16", f"{variant} decode {step}")
+            fout = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, framed=True).run(fpools))
+            fmx, fmn = assert_parity(fout, ref, "bf16", f"{variant} framed decode {step}")
+            say(f"{variant} decode step {step}: max {mx:.2e} mean {mn:.2e}; framed max {fmx:.2e} mean {fmn:.2e}")
+
+
+# ---------------------------------------------------------------------------
 # negative controls: planted mistakes in the oracle must fail the bar
 # ---------------------------------------------------------------------------
 def test_negative_controls_fail_the_tolerance():

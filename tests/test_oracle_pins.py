@@ -479,3 +479,50 @@ def test_framed_two_channel_closed_form():
     w = np.exp(np.array(z) - max(z))
     w /= w.sum()
     np.testing.assert_allclose(out[0, 0], w, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# RoPE variants: partial rotary and the Llama 3.1 frequency rescaling
+# ---------------------------------------------------------------------------
+def test_partial_rotary_table_and_identity_pairs():
+    full = O.rope_inv_freq(128, 5e5)
+    np.testing.assert_array_equal(O.rope_inv_freq_partial(128, 128, 5e5), full)
+    part = O.rope_inv_freq_partial(128, 64, 1e4)
+    assert np.all(part[32:] == 0.0)
+    np.testing.assert_allclose(part[:32], O.rope_inv_freq(64, 1e4), rtol=1e-15)
+    # zero-frequency pairs are left exactly as they are
+    x = np.random.default_rng(12).standard_normal((5, 128))
+    y = O.rope_rotate(x, np.arange(5) * 1000 + 3, part)
+    np.testing.assert_array_equal(y[:, 64:], x[:, 64:])
+    assert np.max(np.abs(y[:, :64] - x[:, :64])) > 0.1
+
+
+def test_all_zero_frequencies_equal_no_positional_encoding():
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((4, 4, 8))
+    K = rng.standard_normal((9, 2, 8))
+    V = rng.standard_normal((9, 2, 8))
+    a = O.attend(q, np.arange(5, 9), K, V, np.arange(9), pe="rope", inv_freq=np.zeros(4))
+    b = O.attend(q, np.arange(5, 9), K, V, np.arange(9), pe="none")
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-15)
+
+
+def test_llama31_rescaling_structure():
+    D, theta, L = 128, 5e5, 8192
+    base = O.rope_inv_freq(D, theta)
+    # factor 1 changes nothing
+    np.testing.assert_allclose(O.rope_inv_freq_llama31(D, theta, 1.0, 1.0, 4.0, L), base, rtol=1e-15)
+    f = O.rope_inv_freq_llama31(D, theta, 8.0, 1.0, 4.0, L)
+    wl = 2 * np.pi / base
+    short, long_ = wl < L / 4.0, wl > L / 1.0
+    assert short.sum() > 0 and long_.sum() > 0 and (~short & ~long_).sum() > 0
+    np.testing.assert_array_equal(f[short], base[short])
+    np.testing.assert_allclose(f[long_], base[long_] / 8.0, rtol=1e-15)
+    mid = ~short & ~long_
+    assert np.all(f[mid] < base[mid]) and np.all(f[mid] > base[mid] / 8.0)
+    assert np.all(np.diff(f) < 0)                    # still strictly decreasing with the pair index
+    # continuity across both region boundaries: with pairs dense in frequency, neighbours stay close
+    # (a blend running the wrong way, or swapped regions, jumps by up to the factor there)
+    fd = O.rope_inv_freq_llama31(1 << 16, theta, 8.0, 1.0, 4.0, L)
+    bd = O.rope_inv_freq(1 << 16, theta)
+    assert np.max(np.abs(np.diff(np.log(fd)) - np.diff(np.log(bd)))) < 1e-3
