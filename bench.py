@@ -266,6 +266,38 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = Tru
                 tokens=tokens, splits=_abi.decode_splits(cfg, len(wl.requests), wl.table_arrays(wl.requests)[0].shape[1]))
 
 
+def hit_ratio_study(W, _abi) -> dict:
+    """Document cache hit ratios of the native pool manager under three cache keys (host only).
+
+    Trace: 4000 requests x 8 distinct documents of 512 tokens, Zipf over a pool of 2000 documents.
+    Budgets are KV bytes of a whole Llama-3.1-8B model (32 layers x 8 KV heads x 128 x K,V x bf16
+    = 128 KiB per token): 1 GiB (8192 tokens) and 8 GiB.
+    """
+    per_token = 32 * 8 * 128 * 2 * 2
+    out = {"trace": "4000 requests x 8 Zipf documents x 512 tokens, pool of 2000 documents",
+           "kv_bytes_per_token": per_token, "token_hit_ratio": {}}
+    t_run, n_admits = 0.0, 0
+    for skew in (0.8, 1.2):
+        ids, lens, offs = W.cache_trace(2000, 4000, (8, 8), skew, seed=11)
+        for gib in (1, 8):
+            blocks = (gib << 30) // (per_token * 16)
+            row = {}
+            for pol in ("agnostic", "aware", "prefix"):
+                pool = _abi.Pool(blocks, pol)
+                t0 = time.perf_counter()
+                pool.run_trace(ids, lens, offs)
+                t_run += time.perf_counter() - t0
+                n_admits += offs.size - 1
+                st = pool.stats()
+                row[pol] = round(st["token_hits"] / st["token_accesses"], 5)
+                pool.close()
+            row["agnostic_over_aware"] = round(row["agnostic"] / max(row["aware"], 1e-12), 2)
+            row["agnostic_over_prefix"] = round(row["agnostic"] / max(row["prefix"], 1e-12), 2)
+            out["token_hit_ratio"][f"zipf{skew}_{gib}GiB"] = row
+    out["requests_per_s"] = round(n_admits / t_run, 1)
+    return out
+
+
 def cpu_baseline(pre, W):
     """The fp64 oracle on the same prefill batch (all 16 requests), host cores."""
     import numpy as np  # noqa: F401
@@ -418,6 +450,7 @@ def main() -> int:
         out["document_frames"]["decode_attention_us"] = round(dec["ms_framed"] * 1e3, 2)
         out["document_frames"]["decode_overhead_vs_norotation"] = round(dec["ms_framed"] / dec["ms_none"] - 1.0, 4)
         print(f"# decode done: {dec['ms'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    out["pool_hit_ratio"] = hit_ratio_study(W, _abi)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre, W)
     print(json.dumps(out), flush=True)

@@ -299,6 +299,83 @@ lazyattn_status lazyattn_append_kv_framed(const lazyattn_config* cfg, void* k_po
 lazyattn_status lazyattn_debug_decode_tables(const lazyattn_batch* batch, int32_t* out,
                                              hipStream_t stream);
 
+/* ---- block pool manager (host only) ----------------------------------------
+ *
+ * Which physical blocks hold which cached document, under a fixed block
+ * budget with least-recently-used eviction.  The cache key is the policy's:
+ *   POSITION_AGNOSTIC  the document alone: one copy serves every offset (the
+ *                      content-only pool the kernels above read);
+ *   POSITION_AWARE     (document, logical start): a document cached at one
+ *                      offset is a miss at any other, and each offset keeps its
+ *                      own copy;
+ *   PREFIX             the chain of documents up to and including this one: a
+ *                      document hits only if every earlier document of the
+ *                      request hit and the whole chain was cached before.
+ * (gist.science, Technical Summary > Problem Statement: position-aware caches
+ * hold several variants of one document and prefix reuse needs identical
+ * prefixes, which lowers the hit ratio under skewed access; > Key
+ * Contributions and > Experimental Results report the hit ratios.)
+ *
+ * A request is admitted whole: its documents in context order, document k at
+ * logical start sum(len[0..k-1]).  A miss allocates ceil(len / 16) blocks,
+ * evicting unpinned entries from the least recently used end while blocks are
+ * short; if they stay short, the document is bypassed (not cached, no blocks).
+ * Every cached document of an admitted request stays pinned (never evicted)
+ * until the request is released; on release its documents become the most
+ * recently used, in context order.  A PREFIX-policy document found cached
+ * after an earlier miss of the same request counts as a miss (its keys would
+ * be recomputed) and reuses its entry.  Not thread-safe: one caller per pool. */
+typedef enum {
+  LAZYATTN_CACHE_POSITION_AGNOSTIC = 0,
+  LAZYATTN_CACHE_POSITION_AWARE = 1,
+  LAZYATTN_CACHE_PREFIX = 2
+} lazyattn_cache_policy;
+
+typedef struct lazyattn_pool lazyattn_pool;   /* opaque */
+
+typedef struct {
+  int64_t num_blocks;       /* the budget */
+  int64_t blocks_in_use;    /* held by cached documents */
+  int64_t doc_accesses, doc_hits;
+  int64_t token_accesses, token_hits;
+  int64_t inserts, evictions, bypasses;
+  int64_t open_requests;    /* admitted, not yet released */
+} lazyattn_pool_stats;
+
+/* Document admission outcome (doc_status of lazyattn_pool_admit). */
+#define LAZYATTN_DOC_MISS 0    /* blocks newly assigned: the caller writes the document's K/V into them */
+#define LAZYATTN_DOC_HIT 1     /* the cached copy is used as is */
+#define LAZYATTN_DOC_BYPASS 2  /* no blocks: the budget is held by pinned documents */
+
+/* Create a pool of num_blocks >= 0 blocks (ids 0..num_blocks-1) with the
+ * given policy; *out receives the handle (freed by lazyattn_pool_destroy).
+ * EINVAL on a bad policy or size. */
+lazyattn_status lazyattn_pool_create(int64_t num_blocks, int32_t policy, lazyattn_pool** out);
+void lazyattn_pool_destroy(lazyattn_pool* pool);
+
+/* Admit one request of n_docs documents (doc_ids [n_docs] >= 0, doc_lens
+ * [n_docs] >= 1, host arrays).  Writes doc_status [n_docs] and, for every
+ * document that is not bypassed, its table entries in context order:
+ * blocks [*num_entries] and starts [*num_entries] (logical start of each
+ * block, as lazyattn_pack_entries takes them), at most max_entries of them.
+ * *ticket identifies the request for lazyattn_pool_release.  EINVAL on bad
+ * arguments; EWORKSPACE if the entries do not fit max_entries (the pool is
+ * then unchanged). */
+lazyattn_status lazyattn_pool_admit(lazyattn_pool* pool, const int64_t* doc_ids, const int32_t* doc_lens,
+                                    int32_t n_docs, uint32_t* blocks, uint32_t* starts, int32_t max_entries,
+                                    int32_t* num_entries, uint8_t* doc_status, int64_t* ticket);
+
+/* Unpin the documents of an admitted request.  EINVAL on an unknown ticket. */
+lazyattn_status lazyattn_pool_release(lazyattn_pool* pool, int64_t ticket);
+
+lazyattn_status lazyattn_pool_get_stats(const lazyattn_pool* pool, lazyattn_pool_stats* out);
+
+/* Admit and release n_requests requests in order: request i holds documents
+ * req_offsets[i] .. req_offsets[i+1]-1 of doc_ids / doc_lens (host arrays).
+ * The statistics accumulate in the pool.  EINVAL on bad arguments. */
+lazyattn_status lazyattn_pool_run_trace(lazyattn_pool* pool, const int64_t* doc_ids, const int32_t* doc_lens,
+                                        const int64_t* req_offsets, int64_t n_requests);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,7 +66,7 @@ __all__ = [
     "gather_context", "attend", "prefill", "decode", "append_kv",
     "brute_force_attention", "rotation_flop_fraction", "tile_flop_counts",
     "rotate_into_frames", "append_kv_framed", "token_frames", "attend_framed", "prefill_framed",
-    "decode_framed", "rope_inv_freq_partial", "rope_inv_freq_llama31",
+    "decode_framed", "rope_inv_freq_partial", "rope_inv_freq_llama31", "BlockCache",
 ]
 
 
@@ -555,3 +555,115 @@ def rotation_flop_fraction(M: int, N: int = 64, D: int = 128) -> float:
     """Rotation FLOPs as a fraction of the tile's matmul FLOPs."""
     c = tile_flop_counts(M, N, D)
     return c["rotation"] / (c["qk"] + c["pv"])
+
+
+# ---------------------------------------------------------------------------
+# 9. which documents a block budget keeps: three cache keys under LRU
+#    [gist:Problem Statement]: a position-aware cache can reuse a document
+#    only at the position it was cached at, so it stores several variants of
+#    one document; prefix reuse needs an identical prefix; under a limited
+#    HBM budget and skewed (Zipf) access this lowers the hit ratio.
+#    [gist:Key Contributions], [gist:Experimental Results] report the ratios.
+#    Readings (the pages leave the mechanics open): documents are cached
+#    whole, ceil(len/16) blocks each; least-recently-used eviction of entries
+#    no admitted request is using; a document that cannot get blocks is
+#    served uncached ("bypass"); a request's documents become most recently
+#    used when it finishes, in context order; under the prefix key a
+#    document counts as a hit only if all earlier documents of the request
+#    hit.  Blocks are handed out lowest id first and come back on eviction so
+#    that they are handed out again in their old order.
+# ---------------------------------------------------------------------------
+class BlockCache:
+    """Plain Python model of a document cache over ``num_blocks`` blocks.
+
+    policy "agnostic": key = document; "aware": key = (document, logical start);
+    "prefix": key = the tuple of documents up to and including this one.
+    """
+
+    MISS, HIT, BYPASS = 0, 1, 2
+
+    def __init__(self, num_blocks: int, policy: str):
+        from collections import OrderedDict
+        if policy not in ("agnostic", "aware", "prefix"):
+            raise ValueError(policy)
+        self.policy = policy
+        self.num_blocks = int(num_blocks)
+        self.free = list(range(self.num_blocks))      # free[0] is handed out next
+        self.entries = {}                             # key -> [blocks, pins]
+        self.lru = OrderedDict()                      # unpinned keys, oldest first
+        self.open = {}
+        self.next_ticket = 1
+        self.stats = dict(doc_accesses=0, doc_hits=0, token_accesses=0, token_hits=0, inserts=0,
+                          evictions=0, bypasses=0)
+
+    def _key(self, docs, k, start):
+        if self.policy == "agnostic":
+            return docs[k]
+        if self.policy == "aware":
+            return (docs[k], start)
+        return tuple(docs[:k + 1])
+
+    def admit(self, docs, lens):
+        docs = [int(d) for d in docs]
+        status, blocks, starts, used = [], [], [], []
+        start = 0
+        all_hit_so_far = True
+        for k, n in enumerate(int(x) for x in lens):
+            nb = -(-n // 16)
+            key = self._key(docs, k, start)
+            self.stats["doc_accesses"] += 1
+            self.stats["token_accesses"] += n
+            if key in self.entries:
+                ent = self.entries[key]
+                s = self.HIT if (self.policy != "prefix" or all_hit_so_far) else self.MISS
+                if ent[1] == 0:
+                    del self.lru[key]
+                ent[1] += 1
+            else:
+                while len(self.free) < nb and self.lru:
+                    old, _ = self.lru.popitem(last=False)
+                    self.free = self.entries.pop(old)[0] + self.free
+                    self.stats["evictions"] += 1
+                if len(self.free) >= nb:
+                    ent = [self.free[:nb], 1]
+                    self.free = self.free[nb:]
+                    self.entries[key] = ent
+                    self.stats["inserts"] += 1
+                    s = self.MISS
+                else:
+                    ent = None
+                    self.stats["bypasses"] += 1
+                    s = self.BYPASS
+            if s == self.HIT:
+                self.stats["doc_hits"] += 1
+                self.stats["token_hits"] += n
+            else:
+                all_hit_so_far = False
+            if ent is not None:
+                used.append(key)
+                for j, b in enumerate(ent[0]):
+                    blocks.append(b)
+                    starts.append(start + 16 * j)
+            status.append(s)
+            start += n
+        t = self.next_ticket
+        self.next_ticket += 1
+        self.open[t] = used
+        return status, blocks, starts, t
+
+    def release(self, ticket):
+        for key in self.open.pop(ticket):
+            ent = self.entries[key]
+            ent[1] -= 1
+            if ent[1] == 0:
+                self.lru[key] = None
+
+    def blocks_in_use(self):
+        return self.num_blocks - len(self.free)
+
+    def run(self, requests):
+        """requests: iterable of (docs, lens); each admitted and released in turn."""
+        for docs, lens in requests:
+            _, _, _, t = self.admit(docs, lens)
+            self.release(t)
+        return self.stats

@@ -46,6 +46,15 @@ class Config(ctypes.Structure):
     ]
 
 
+class PoolStats(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "num_blocks", "blocks_in_use", "doc_accesses", "doc_hits", "token_accesses", "token_hits",
+        "inserts", "evictions", "bypasses", "open_requests")]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
 class Batch(ctypes.Structure):
     _fields_ = [
         ("num_reqs", ctypes.c_int32),
@@ -94,6 +103,12 @@ def lib() -> ctypes.CDLL:
             "lazyattn_materialize_kv": (I32, [CP, P, P, I64, BP, P, P, P, I64, P]),
             "lazyattn_rotate_queries": (I32, [CP, P, P, I32, I32, BP, P, P]),
             "lazyattn_rope_inv_freq": (I32, [I32, I32, ctypes.c_double, P]),
+            "lazyattn_pool_create": (I32, [I64, I32, ctypes.POINTER(P)]),
+            "lazyattn_pool_destroy": (None, [P]),
+            "lazyattn_pool_admit": (I32, [P, P, P, I32, P, P, I32, P, P, P]),
+            "lazyattn_pool_release": (I32, [P, I64]),
+            "lazyattn_pool_get_stats": (I32, [P, ctypes.POINTER(PoolStats)]),
+            "lazyattn_pool_run_trace": (I32, [P, P, P, P, I64]),
             "lazyattn_rope_inv_freq_llama31": (I32, [I32, ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                                      ctypes.c_double, I32, P]),
         }
@@ -306,3 +321,59 @@ def append_kv_framed(cfg: Config, k_pool, v_pool, num_blocks: int, k_new, v_new,
 def debug_decode_tables(batch: Batch, out, stream=None) -> None:
     st = lib().lazyattn_debug_decode_tables(ctypes.byref(batch), _ptr(out), _stream(stream))
     _check(st, "lazyattn_debug_decode_tables")
+
+
+# ---------------------------------------------------------------------------
+# block pool manager (host only)
+# ---------------------------------------------------------------------------
+CACHE_POLICIES = {"agnostic": 0, "aware": 1, "prefix": 2}
+DOC_MISS, DOC_HIT, DOC_BYPASS = 0, 1, 2
+
+
+class Pool:
+    """A lazyattn_pool handle: documents -> physical blocks under a block budget (LRU eviction)."""
+
+    def __init__(self, num_blocks: int, policy: str = "agnostic"):
+        h = ctypes.c_void_p()
+        _check(lib().lazyattn_pool_create(int(num_blocks), CACHE_POLICIES[policy], ctypes.byref(h)), "pool_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().lazyattn_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def admit(self, doc_ids, doc_lens):
+        """(status uint8 [n], blocks uint32 [E], starts uint32 [E], ticket) for one request."""
+        ids = np.ascontiguousarray(doc_ids, dtype=np.int64)
+        lens = np.ascontiguousarray(doc_lens, dtype=np.int32)
+        cap = int(((lens.astype(np.int64) + 15) // 16).sum())
+        blocks = np.empty(max(cap, 1), dtype=np.uint32)
+        starts = np.empty(max(cap, 1), dtype=np.uint32)
+        status = np.empty(max(ids.size, 1), dtype=np.uint8)
+        ne, t = ctypes.c_int32(), ctypes.c_int64()
+        _check(lib().lazyattn_pool_admit(self._h, ids.ctypes.data, lens.ctypes.data, int(ids.size), blocks.ctypes.data,
+                                         starts.ctypes.data, cap, ctypes.byref(ne), status.ctypes.data,
+                                         ctypes.byref(t)), "pool_admit")
+        return status[:ids.size], blocks[:ne.value], starts[:ne.value], int(t.value)
+
+    def release(self, ticket: int):
+        _check(lib().lazyattn_pool_release(self._h, int(ticket)), "pool_release")
+
+    def stats(self) -> dict:
+        st = PoolStats()
+        _check(lib().lazyattn_pool_get_stats(self._h, ctypes.byref(st)), "pool_get_stats")
+        return st.as_dict()
+
+    def run_trace(self, doc_ids, doc_lens, req_offsets):
+        ids = np.ascontiguousarray(doc_ids, dtype=np.int64)
+        lens = np.ascontiguousarray(doc_lens, dtype=np.int32)
+        off = np.ascontiguousarray(req_offsets, dtype=np.int64)
+        _check(lib().lazyattn_pool_run_trace(self._h, ids.ctypes.data, lens.ctypes.data, off.ctypes.data,
+                                             int(off.size - 1)), "pool_run_trace")

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblazyattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["lazyattn_kernels.hip", "lazyattn_host.cpp"]
+SOURCES = ["lazyattn_kernels.hip", "lazyattn_host.cpp", "lazyattn_pool.cpp"]
 ARCH = "gfx950"
 
 

@@ -6,6 +6,7 @@ case in full; the other cases at their real shapes with requests or query
 tokens sampled where the oracle would take minutes.
 """
 import sys
+import types
 
 import numpy as np
 import pytest
@@ -526,6 +527,66 @@ def test_framed_decode_long_context_splits_and_mqa():
     ref = orc.decode(d, requests=reqs)
     mx, mn = assert_parity(out[reqs], np.stack([ref[r] for r in reqs]), "bf16", "framed MQA decode")
     say(f"framed MQA decode: max {mx:.2e} mean {mn:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# the pool manager places documents; the kernels read its tables
+# ---------------------------------------------------------------------------
+def test_pool_manager_tables_feed_the_prefill():
+    say("pool manager: 8B prefill, 6 requests, documents placed by lazyattn_pool_admit")
+    wl = W.build_workload(W.spec(2, requests=[6]))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb = wl.prefill_batch()
+    reqs = pb["requests"]
+    budget = int(sum(wl.doc_nblk[d] for d in wl.referenced_docs))        # room for every document
+    n_priv = sum(len(q.private_blocks) for q in reqs)
+    nb = budget + n_priv
+    dt = staging.torch_dtype(s.dtype)
+    kp = torch.full((nb, s.num_kv_heads, 16, s.head_dim), float("nan"), dtype=dt, device=DEV)
+    vp = torch.full((nb, s.num_kv_heads, s.head_dim, 16), float("nan"), dtype=dt, device=DEV)
+    pool = _abi.Pool(budget, "agnostic")
+    E = max(q.entry_blocks.size for q in reqs)
+    tb = np.zeros((len(reqs), E), np.uint32)
+    ts = np.full((len(reqs), E), 0x7FFFFFFF, np.uint32)
+    ne = np.zeros(len(reqs), np.int32)
+    priv_map, writes, hits, nxt = {}, 0, 0, budget
+    for r, q in enumerate(reqs):
+        st, bl, sta, _ = pool.admit(q.doc_ids, q.doc_lens)
+        assert np.all(st != _abi.DOC_BYPASS)
+        col = 0
+        for k, d in enumerate(q.doc_ids):
+            nblk = int(wl.doc_nblk[d])
+            if st[k] == _abi.DOC_MISS:          # the caller writes a missed document once
+                kk, vv = wl.doc_kv(int(d))
+                L = kk.shape[0]
+                j = np.arange(L)
+                slots = bl[col + j // 16].astype(np.int64) * 16 + j % 16
+                _abi.append_kv(cfg, kp, vp, nb, staging.to_device(kk, s.dtype, DEV), staging.to_device(vv, s.dtype, DEV),
+                               torch.from_numpy(slots).to(DEV))
+                writes += 1
+            else:
+                hits += 1
+            col += nblk
+        tb[r, :col], ts[r, :col] = bl, sta
+        for j, b in enumerate(q.private_blocks):
+            priv_map[int(b)] = nxt
+            tb[r, col + j] = nxt
+            ts[r, col + j] = q.ctx_docs + 16 * j
+            nxt += 1
+        ne[r] = q.num_entries_after(q.q_len)
+    assert writes == len(set(int(d) for q in reqs for d in q.doc_ids)) and hits > 0
+    remap = np.array([priv_map[int(b)] for b in pb["slots"] // 16], dtype=np.int64) * 16 + pb["slots"] % 16
+    _abi.append_kv(cfg, kp, vp, nb, staging.to_device(pb["k_new"], s.dtype, DEV),
+                   staging.to_device(pb["v_new"], s.dtype, DEV), torch.from_numpy(remap).to(DEV))
+    inp = dict(pb, table_blocks=tb, table_starts=ts, num_entries=ne)
+    placed = types.SimpleNamespace(k=kp, v=vp, num_blocks=nb)
+    got = gpu_f64(staging.PrefillCall(cfg, s, inp, DEV).run(placed))
+    sync()
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="prefill over pool-manager tables")
+    say(f"pool manager: {writes} documents written, {hits} document hits served from shared blocks")
 
 
 # ---------------------------------------------------------------------------

@@ -15,6 +15,7 @@ from .synth import (  # noqa: F401
     RequestLayout,
     SparsePool,
     build_workload,
+    cache_trace,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     spec,

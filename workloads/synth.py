@@ -531,3 +531,31 @@ class Workload:
 
 def build_workload(s: WorkloadSpec) -> Workload:
     return Workload(s)
+
+
+# ----------------------------------------------------------------------------
+# request traces for the block-pool hit-ratio simulation
+# ----------------------------------------------------------------------------
+def cache_trace(n_docs_pool: int, n_requests: int, docs_per_request: tuple, zipf_s: float, seed: int,
+                doc_len: int = 512, doc_len_lognormal: Optional[tuple] = None):
+    """A seeded stream of retrieval requests: (doc_ids int64 [N], doc_lens int32 [N], req_offsets int64 [R+1]).
+
+    Each request retrieves between docs_per_request[0] and [1] distinct documents, Zipf(zipf_s) over
+    the pool's popularity ranks (sequentially renormalised, without replacement), in random order.
+    Document lengths are fixed, or lognormal (median, sigma, lo, hi) per document.
+    """
+    rl = np.random.default_rng(np.random.SeedSequence([seed, 1]))
+    if doc_len_lognormal is None:
+        lens = np.full(n_docs_pool, doc_len, dtype=np.int32)
+    else:
+        med, sig, lo, hi = doc_len_lognormal
+        lens = np.clip(np.rint(np.exp(rl.normal(np.log(med), sig, size=n_docs_pool))), lo, hi).astype(np.int32)
+    rd = np.random.default_rng(np.random.SeedSequence([seed, 2]))
+    ids, offs = [], [0]
+    for _ in range(n_requests):
+        n = int(rd.integers(docs_per_request[0], docs_per_request[1] + 1))
+        d = _zipf_draw(rd, n_docs_pool, n, zipf_s)
+        ids.append(d)
+        offs.append(offs[-1] + n)
+    doc_ids = np.concatenate(ids).astype(np.int64) if ids else np.zeros(0, np.int64)
+    return doc_ids, lens[doc_ids].astype(np.int32), np.asarray(offs, dtype=np.int64)
