@@ -754,22 +754,31 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
   uint4 kr[4];
   uint2 vr[8];
   EntryInfo cur;
-  auto load_block = [&](int e, EntryInfo& inf, uint4 (&k)[4], uint2 (&v)[8]) {
-    inf = entry_info(trow, e, ne, L);
-    const uint16_t* kb = A.kpool + (static_cast<size_t>(inf.blk) * Hkv + kvh) * (kBlock * kPD);
+  auto load_kv = [&](uint32_t blk, uint4 (&k)[4], uint2 (&v)[8]) {
+    const uint16_t* kb = A.kpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kBlock * kPD);
     const uint4* kp = reinterpret_cast<const uint4*>(kb + n * kPD + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) k[s] = kp[s];
-    const uint16_t* vb = A.vpool + (static_cast<size_t>(inf.blk) * Hkv + kvh) * (kPD * kBlock);
+    const uint16_t* vb = A.vpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kPD * kBlock);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) v[dt] = *reinterpret_cast<const uint2*>(vb + (16 * dt + n) * kBlock + 4 * g);
   };
 
-  int e = e_begin + wave;
-  int fr_next = 0;
+  // The wave-uniform entry index makes the table words scalar loads.  An
+  // entry's words (and frame start) are fetched one iteration before its K/V
+  // loads are issued, so those loads never wait on them: entry e's K/V are in
+  // flight while entry e - 4 is processed, entry e + 4's words likewise.
+  int e = __builtin_amdgcn_readfirstlane(e_begin + wave);
+  EntryInfo nx{};
+  int fr_next = 0, fr_nx = 0;
   if (e < e_end) {
-    load_block(e, cur, kr, vr);
-    if (PE == kPeFramed) fr_next = __builtin_amdgcn_readfirstlane(frow[e]);
+    cur = entry_info(trow, e, ne, L);
+    load_kv(cur.blk, kr, vr);
+    if (PE == kPeFramed) fr_next = frow[e];
+    if (e + 4 < e_end) {
+      nx = entry_info(trow, e + 4, ne, L);
+      if (PE == kPeFramed) fr_nx = frow[e + 4];
+    }
   }
   for (int it = 0; e < e_end; ++it) {
     const EntryInfo inf = cur;
@@ -780,8 +789,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
     for (int dt = 0; dt < 8; ++dt) v[dt] = vr[dt];
     const int e_next = e + 4;
     if (e_next < e_end) {
-      load_block(e_next, cur, kr, vr);
-      if (PE == kPeFramed) fr_next = __builtin_amdgcn_readfirstlane(frow[e_next]);
+      load_kv(nx.blk, kr, vr);
+      cur = nx;
+      fr_next = fr_nx;
+      if (e_next + 4 < e_end) {
+        nx = entry_info(trow, e_next + 4, ne, L);
+        if (PE == kPeFramed) fr_nx = frow[e_next + 4];
+      }
     }
 
     // ---- framed pool: turn the query to this entry's frame, R(p - F) q ----------
@@ -1139,8 +1153,16 @@ static lazyattn_status check_batch(const lazyattn_batch* b) {
   return LAZYATTN_OK;
 }
 
+// Decode work-groups reserve at least this much LDS, so that at most two share
+// a CU (160 KiB each) whatever the positional encoding: with three, the
+// concurrent streams thrash the L2 that shared document blocks are reused from
+// (measured slower on the Llama-3.1-8B decode), and the rotation-free control
+// keeps the occupancy of the RoPE kernel it is compared with.
+constexpr size_t kDecodeLdsFloor = 56 * 1024;
+
 static size_t decode_lds_bytes(int nt, int group) {
-  return (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(group) * kOS) * sizeof(float);
+  const size_t need = (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(group) * kOS) * sizeof(float);
+  return need > kDecodeLdsFloor ? need : kDecodeLdsFloor;
 }
 
 // ---------------------------------------------------------------------------
