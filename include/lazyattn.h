@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LAZYATTN_ABI_VERSION 4
+#define LAZYATTN_ABI_VERSION 5
 
 typedef enum {
   LAZYATTN_OK = 0,
@@ -81,6 +81,24 @@ typedef enum { LAZYATTN_PE_ROPE = 0, LAZYATTN_PE_NONE = 1, LAZYATTN_PE_ALIBI = 2
  * rounding, for validation. */
 #define LAZYATTN_FLAG_EXACT_MAX 1
 
+/* Pool formats (lazyattn_config.kv_format).
+ *
+ * PLAIN: pools hold cfg->dtype values, K [num_blocks][Hkv][16][D] and
+ * V [num_blocks][Hkv][D][16].
+ *
+ * FP8_E4M3 (dtype bf16, D = 128 only): each (block, KV head) is one chunk of
+ * LAZYATTN_FP8_CHUNK_BYTES bytes in each pool, pools [num_blocks][Hkv][chunk]:
+ *   K chunk: codes [16 rows][128 channels], then int8 exponents [16], one per row;
+ *   V chunk: codes [128 channels][16 tokens], then int8 exponents [16], one per token.
+ * A value is its OCP e4m3 code (bias 7, largest 448) times 2^exponent.  Rows
+ * are quantised whole when appended (lazyattn_append_kv): exponent = the
+ * smallest e with max|x| <= 448 * 2^e (0 for an all-zero row), code = x * 2^-e
+ * rounded to nearest even, saturated at +-448.  Power-of-two scales make the
+ * bf16 values the kernels compute with exact.  (The pages do not describe a
+ * narrower pool; this one halves the bytes a decode step streams.) */
+typedef enum { LAZYATTN_KV_PLAIN = 0, LAZYATTN_KV_FP8_E4M3 = 1 } lazyattn_kv_format;
+#define LAZYATTN_FP8_CHUNK_BYTES 2064
+
 typedef struct {
   int32_t num_q_heads;    /* Hq >= 1 */
   int32_t num_kv_heads;   /* Hkv >= 1, Hq % Hkv == 0 */
@@ -97,6 +115,7 @@ typedef struct {
                                 * finite and >= 0; a 0 leaves its pair unrotated (partial rotary).
                                 * Read during the call only; rope_theta is then not used.  RoPE
                                 * variants: gist.science, Key Contributions > Generalizability. */
+  int32_t kv_format;           /* lazyattn_kv_format */
 } lazyattn_config;
 
 /* Key frames.  With frame_starts == NULL the pool holds content-only keys

@@ -67,6 +67,8 @@ __all__ = [
     "brute_force_attention", "rotation_flop_fraction", "tile_flop_counts",
     "rotate_into_frames", "append_kv_framed", "token_frames", "attend_framed", "prefill_framed",
     "decode_framed", "rope_inv_freq_partial", "rope_inv_freq_llama31", "BlockCache",
+    "e4m3_value", "e4m3_encode", "fp8_row_exponent", "quantize_fp8_rows", "fp8_empty_pools",
+    "append_kv_fp8", "Fp8PoolView", "FP8_CHUNK",
 ]
 
 
@@ -319,7 +321,8 @@ def prefill(*, q, cu_q_lens, ctx_lens, num_entries, table_words, k_pool, v_pool,
             num_kv_heads: int, block_size: int, dtype: str, pe: str, rope_theta: float,
             softmax_scale: Optional[float] = None, slopes=None, formulation: str = "materialized",
             requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
-            token_subset: Optional[dict] = None, inv_freq: Optional[np.ndarray] = None) -> dict:
+            token_subset: Optional[dict] = None, inv_freq: Optional[np.ndarray] = None,
+            pool_dtype: Optional[str] = None) -> dict:
     """Causal prefill of each request's new tokens over its whole context.
 
     q [total_q][Hq][D]; request r owns rows cu_q_lens[r]..cu_q_lens[r+1]-1,
@@ -333,7 +336,7 @@ def prefill(*, q, cu_q_lens, ctx_lens, num_entries, table_words, k_pool, v_pool,
     res = {}
     for r in reqs:
         words, n_ent, L = _request_args(table_words, num_entries, ctx_lens, r)
-        K, V, kp = gather_context(words, n_ent, L, k_pool, v_pool, block_size, dtype)
+        K, V, kp = gather_context(words, n_ent, L, k_pool, v_pool, block_size, pool_dtype or dtype)
         a, b = int(cu_q_lens[r]), int(cu_q_lens[r + 1])
         M = b - a
         local = np.arange(M) if token_subset is None or r not in token_subset \
@@ -349,14 +352,14 @@ def decode(*, q, ctx_lens, num_entries, table_words, k_pool, v_pool,
            num_kv_heads: int, block_size: int, dtype: str, pe: str, rope_theta: float,
            softmax_scale: Optional[float] = None, slopes=None, formulation: str = "materialized",
            requests: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
-           inv_freq: Optional[np.ndarray] = None) -> dict:
+           inv_freq: Optional[np.ndarray] = None, pool_dtype: Optional[str] = None) -> dict:
     """One decode step: request r's single query q[r] [Hq][D] sits at position ctx_lens[r]-1."""
     qf = to_f64(q, dtype)
     reqs = range(len(ctx_lens)) if requests is None else requests
     res = {}
     for r in reqs:
         words, n_ent, L = _request_args(table_words, num_entries, ctx_lens, r)
-        K, V, kp = gather_context(words, n_ent, L, k_pool, v_pool, block_size, dtype)
+        K, V, kp = gather_context(words, n_ent, L, k_pool, v_pool, block_size, pool_dtype or dtype)
         res[r] = attend(qf[r][None], np.array([L - 1]), K, V, kp, pe=pe, rope_theta=rope_theta,
                         softmax_scale=softmax_scale, slopes=slopes,
                         formulation=formulation, heads=heads, inv_freq=inv_freq)[0]
@@ -667,3 +670,112 @@ class BlockCache:
             _, _, _, t = self.admit(docs, lens)
             self.release(t)
         return self.stats
+
+
+# ---------------------------------------------------------------------------
+# 10. an FP8 (e4m3) pool with per-row power-of-two scales
+#     Not described by the pages (their pool is bf16); a narrower format for
+#     the same content-only cache.  Readings: OCP e4m3 (1 sign, 4 exponent
+#     bits with bias 7, 3 mantissa bits; exponent 15 with mantissa 7 is NaN,
+#     largest finite 448, subnormals below 2^-6); each 128-value row (one
+#     token's K, or its V) gets the smallest exponent e >= -127 with
+#     max|x| <= 448 * 2^e (0 for an all-zero row) and codes = nearest e4m3
+#     value of x * 2^-e, ties to the even code, saturating at 448.
+#     Chunk per (block, KV head): K codes [16 rows][128], then 16 int8
+#     exponents (rows); V codes [128][16 tokens], then 16 int8 exponents.
+# ---------------------------------------------------------------------------
+FP8_CHUNK = 16 * 128 + 16
+
+
+def e4m3_value(code: int) -> float:
+    """The value of one e4m3 code, from the format's definition."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 15 and m == 7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_MAGNITUDES = np.array([e4m3_value(c) for c in range(127)])       # codes 0..126, increasing
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 code of each value (ties to the even code, saturating at 448; the sign of
+    zero kept), by search over the 127 non-negative finite magnitudes."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(_E4M3_MAGNITUDES, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = np.abs(a - _E4M3_MAGNITUDES[lo])
+    d_hi = np.abs(_E4M3_MAGNITUDES[hi] - a)
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= 448.0, 126, pick)
+    return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_row_exponent(amax: float) -> int:
+    """Smallest e >= -127 with amax <= 448 * 2^e (0 when amax is 0)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    e = max(-127, math.ceil(math.log2(amax / 448.0)))
+    while amax > 448.0 * 2.0 ** e:
+        e += 1
+    while e > -127 and amax <= 448.0 * 2.0 ** (e - 1):
+        e -= 1
+    return e
+
+
+def quantize_fp8_rows(x: np.ndarray):
+    """Rows x [..., D] (float32 values) -> (codes uint8 [..., D], exponents int8 [...])."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    exps = np.vectorize(fp8_row_exponent, otypes=[np.int64])(amax)
+    y = np.ldexp(x, -exps[..., None].astype(np.int32))              # float32, exact scaling
+    return e4m3_encode(y), exps.astype(np.int8)
+
+
+def fp8_empty_pools(num_blocks: int, num_kv_heads: int):
+    """Chunked K and V pools, every byte 0xFF (NaN codes) until written."""
+    shape = (num_blocks, num_kv_heads, FP8_CHUNK)
+    return np.full(shape, 0xFF, dtype=np.uint8), np.full(shape, 0xFF, dtype=np.uint8)
+
+
+def append_kv_fp8(k_chunks, v_chunks, k_new, v_new, slots, dtype: str, block_size: int = 16):
+    """Quantise new tokens' K/V [n][Hkv][D] (in ``dtype``) row by row into pool slots, in place."""
+    k = to_f64(k_new, dtype).astype(np.float32)
+    v = to_f64(v_new, dtype).astype(np.float32)
+    kc, ke = quantize_fp8_rows(k)
+    vc, ve = quantize_fp8_rows(v)
+    D = k.shape[-1]
+    for i, sl in enumerate(np.asarray(slots, dtype=np.int64)):
+        b, row = int(sl) // block_size, int(sl) % block_size
+        k_chunks[b, :, row * D:(row + 1) * D] = kc[i]
+        k_chunks[b, :, block_size * D + row] = ke[i].view(np.uint8)
+        v_chunks[b, :, row:block_size * D:block_size] = vc[i]
+        v_chunks[b, :, block_size * D + row] = ve[i].view(np.uint8)
+
+
+class Fp8PoolView:
+    """Dequantised float64 blocks of a chunked pool, in the plain layouts, on indexing:
+    kind "k" -> [n][Hkv][16][D], kind "v" -> [n][Hkv][D][16]."""
+
+    _table = np.array([e4m3_value(c) for c in range(256)])
+
+    def __init__(self, chunks: np.ndarray, kind: str, head_dim: int = 128, block_size: int = 16):
+        self.chunks, self.kind, self.D, self.B = chunks, kind, head_dim, block_size
+
+    @property
+    def shape(self):
+        nb, hkv = self.chunks.shape[:2]
+        return (nb, hkv, self.B, self.D) if self.kind == "k" else (nb, hkv, self.D, self.B)
+
+    def __getitem__(self, ids):
+        c = self.chunks[ids]
+        vals = self._table[c[..., :self.B * self.D]]
+        scale = np.ldexp(1.0, c[..., self.B * self.D:].view(np.int8).astype(np.int32))   # [n][Hkv][16]
+        if self.kind == "k":
+            return vals.reshape(c.shape[:2] + (self.B, self.D)) * scale[..., :, None]
+        return vals.reshape(c.shape[:2] + (self.D, self.B)) * scale[..., None, :]

@@ -30,6 +30,10 @@ class LazyAttnError(RuntimeError):
         self.status = status
 
 
+KV_FORMATS = {"plain": 0, "fp8": 1}
+FP8_CHUNK_BYTES = 2064
+
+
 class Config(ctypes.Structure):
     _fields_ = [
         ("num_q_heads", ctypes.c_int32),
@@ -43,6 +47,7 @@ class Config(ctypes.Structure):
         ("flags", ctypes.c_int32),
         ("alibi_slopes", ctypes.c_void_p),
         ("rope_inv_freq", ctypes.c_void_p),
+        ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -134,8 +139,10 @@ def _check(status: int, where: str):
 # ---------------------------------------------------------------------------
 def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str = "bf16", pe: str = "rope",
                 rope_theta: float = 10000.0, softmax_scale: float = 0.0, alibi_slopes=None,
-                block_size: int = 16, exact_max: bool = False, inv_freq: np.ndarray = None) -> Config:
-    """inv_freq: optional host float64 [head_dim/2] RoPE frequency table (kept alive by the config)."""
+                block_size: int = 16, exact_max: bool = False, inv_freq: np.ndarray = None,
+                kv_format: str = "plain") -> Config:
+    """inv_freq: optional host float64 [head_dim/2] RoPE frequency table (kept alive by the config);
+    kv_format "plain" or "fp8" (e4m3 chunks of FP8_CHUNK_BYTES per block and KV head)."""
     c = Config()
     c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size = num_q_heads, num_kv_heads, head_dim, block_size
     c.dtype = _DT[dtype] if isinstance(dtype, str) else int(dtype)
@@ -150,6 +157,7 @@ def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str =
         if f.shape != (head_dim // 2,):
             raise ValueError(f"inv_freq must hold head_dim/2 = {head_dim // 2} values")
     c.rope_inv_freq = f.ctypes.data if f is not None else None
+    c.kv_format = KV_FORMATS[kv_format]
     c._keep = (alibi_slopes, f)
     return c
 

@@ -26,6 +26,9 @@ lazyattn_status check_config(const lazyattn_config* cfg) {
   if (cfg->dtype == LAZYATTN_BF16 && cfg->head_dim != 128) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32 && cfg->head_dim != 64 && cfg->head_dim != 128)
     return LAZYATTN_EUNSUPPORTED;
+  if (cfg->kv_format != LAZYATTN_KV_PLAIN && cfg->kv_format != LAZYATTN_KV_FP8_E4M3) return LAZYATTN_EINVAL;
+  if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3 && (cfg->dtype != LAZYATTN_BF16 || cfg->head_dim != 128))
+    return LAZYATTN_EUNSUPPORTED;
   if (cfg->rope_inv_freq) {
     for (int i = 0; i < cfg->head_dim / 2; ++i) {
       const double f = cfg->rope_inv_freq[i];

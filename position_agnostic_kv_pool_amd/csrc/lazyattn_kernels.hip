@@ -69,6 +69,33 @@ __device__ __forceinline__ uint32_t rotate_pair(uint32_t u, float2 ph) {
   return pack_bf16x2(x0 * ph.x - x1 * ph.y, x0 * ph.y + x1 * ph.x);
 }
 
+// ---- FP8 (OCP e4m3) pool chunks: 2048 bytes of codes, then 16 int8 exponents ----
+constexpr int kChunk8 = LAZYATTN_FP8_CHUNK_BYTES;
+static_assert(kChunk8 == 16 * 128 + 16, "FP8 chunk = codes of 16 x 128 values + 16 exponents");
+
+// Two e4m3 codes (the low or high 16 bits of w) as floats; exact.  `hi` must
+// fold to a constant (the conversion's word select is an immediate).
+__device__ __forceinline__ float2 fp8x2_to_f32(uint32_t w, bool hi) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  const f2v r = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true)
+                   : __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  return make_float2(r.x, r.y);
+}
+// Two e4m3 codes as a bf16x2 word; exact (every e4m3 value is a bf16 value).
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi) {
+  return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, true))
+            : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(w), 1.0f, false));
+}
+// Rotate the channel pair of two e4m3 codes; rounds once, to bf16.
+__device__ __forceinline__ uint32_t rotate_fp8_pair(uint32_t w, bool hi, float2 ph) {
+  const float2 x = fp8x2_to_f32(w, hi);
+  return pack_bf16x2(x.x * ph.x - x.y * ph.y, x.x * ph.y + x.y * ph.x);
+}
+// 2^e for the int8 exponent in byte b of w.
+__device__ __forceinline__ float exp_scale(uint32_t w, int b) {
+  return __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(static_cast<int8_t>((w >> (8 * b)) & 0xffu)));
+}
+
 struct EntryInfo {
   uint32_t blk;
   int32_t start;
@@ -678,7 +705,7 @@ struct DecodeArgs {
 constexpr int kOS = kPD + 4;  // LDS row stride (floats) of the wave-merge buffer
 constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
-template <int PE, int NT>
+template <int PE, int NT, int KV8>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) float dsm[];
   float2* bsh = reinterpret_cast<float2*>(dsm);             // [4 waves][2][64]
@@ -754,14 +781,30 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
   uint4 kr[4];
   uint2 vr[8];
   EntryInfo cur;
+  // FP8 pool: lane (g, n) holds the 32 codes of key row n, channels 32g..32g+31
+  // (kr[0..1]), the codes of tokens 4g..4g+3 of channel rows 16dt+n (vr[dt].x)
+  // and the exponents of key rows / tokens 4g..4g+3 (kr[2].x, kr[2].y)
   auto load_kv = [&](uint32_t blk, uint4 (&k)[4], uint2 (&v)[8]) {
-    const uint16_t* kb = A.kpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kBlock * kPD);
-    const uint4* kp = reinterpret_cast<const uint4*>(kb + n * kPD + 32 * g);
+    if (KV8) {
+      const size_t chunk = (static_cast<size_t>(blk) * Hkv + kvh) * kChunk8;
+      const uint8_t* kc = reinterpret_cast<const uint8_t*>(A.kpool) + chunk;
+      const uint8_t* vc = reinterpret_cast<const uint8_t*>(A.vpool) + chunk;
+      const uint4* kp = reinterpret_cast<const uint4*>(kc + n * kPD + 32 * g);
+      k[0] = kp[0];
+      k[1] = kp[1];
+      k[2].x = *reinterpret_cast<const uint32_t*>(kc + 16 * kPD + 4 * g);
+      k[2].y = *reinterpret_cast<const uint32_t*>(vc + 16 * kPD + 4 * g);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) k[s] = kp[s];
-    const uint16_t* vb = A.vpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kPD * kBlock);
+      for (int dt = 0; dt < 8; ++dt) v[dt].x = *reinterpret_cast<const uint32_t*>(vc + (16 * dt + n) * kBlock + 4 * g);
+    } else {
+      const uint16_t* kb = A.kpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kBlock * kPD);
+      const uint4* kp = reinterpret_cast<const uint4*>(kb + n * kPD + 32 * g);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) v[dt] = *reinterpret_cast<const uint2*>(vb + (16 * dt + n) * kBlock + 4 * g);
+      for (int s = 0; s < 4; ++s) k[s] = kp[s];
+      const uint16_t* vb = A.vpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kPD * kBlock);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) v[dt] = *reinterpret_cast<const uint2*>(vb + (16 * dt + n) * kBlock + 4 * g);
+    }
   };
 
   // The wave-uniform entry index makes the table words scalar loads.  An
@@ -787,6 +830,20 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
     uint2 v[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) v[dt] = vr[dt];
+    const uint32_t kexp = k[2].x, vexp = k[2].y;
+    if (KV8) {
+      // FP8 codes to bf16 operands (exact); the exponents scale S and P below
+      const uint4 c0 = k[0], c1 = k[1];
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      if (PE != LAZYATTN_PE_ROPE) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          k[s] = make_uint4(fp8x2_to_bf16x2(cw[2 * s], false), fp8x2_to_bf16x2(cw[2 * s], true),
+                            fp8x2_to_bf16x2(cw[2 * s + 1], false), fp8x2_to_bf16x2(cw[2 * s + 1], true));
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) v[dt] = make_uint2(fp8x2_to_bf16x2(vr[dt].x, false), fp8x2_to_bf16x2(vr[dt].x, true));
+    }
     const int e_next = e + 4;
     if (e_next < e_end) {
       load_kv(nx.blk, kr, vr);
@@ -831,15 +888,31 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (KV8) {
+        // the lane's 32 codes are still in kr[0..1] of this iteration (k[0..1])
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        uint32_t w4[4] = {k[s].x, k[s].y, k[s].z, k[s].w};
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t c_lo = (s < 2) ? (s == 0 ? k[0].x : k[0].z) : (s == 2 ? k[1].x : k[1].z);
+          const uint32_t c_hi = (s < 2) ? (s == 0 ? k[0].y : k[0].w) : (s == 2 ? k[1].y : k[1].w);
+          uint32_t w4[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int i = 4 * s + jj;                      // pair 16g + i
-          w4[jj] = rotate_pair(w4[jj], cmul(bw[16 * g + i], rt[i]));
+          for (int jj = 0; jj < 4; ++jj) {
+            const int i = 4 * s + jj;                    // pair 16g + i
+            w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[16 * g + i], rt[i]));
+          }
+          ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
         }
-        ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint32_t w4[4] = {k[s].x, k[s].y, k[s].z, k[s].w};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int i = 4 * s + jj;                    // pair 16g + i
+            w4[jj] = rotate_pair(w4[jj], cmul(bw[16 * g + i], rt[i]));
+          }
+          ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        }
       }
     } else {
 #pragma unroll
@@ -859,10 +932,15 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      // scores relative to the reference: the chain starts from -m
-      f32x4 S = negm[nt];
+      // scores relative to the reference: the chain starts from -m (FP8: the
+      // row's scale multiplies the product first)
+      f32x4 S = KV8 ? f32x4{0.f, 0.f, 0.f, 0.f} : negm[nt];
 #pragma unroll
       for (int s = 0; s < 4; ++s) S = mfma16x16x32(ka[s], qb[nt][s], S);
+      if (KV8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[j] = fmaf(S[j], exp_scale(kexp, j), negm[nt][j]);
+      }
       float lm = kNegInf;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -898,7 +976,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
       const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
       // row sum of the bf16-rounded weights that enter P.V
       l_run[nt] += (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23));
-      const s16x4 pb = __builtin_bit_cast(s16x4, make_uint2(p01, p23));
+      s16x4 pb = __builtin_bit_cast(s16x4, make_uint2(p01, p23));
+      if (KV8) {
+        // each token's value scale goes on its weight (tokens past the entry's
+        // length have weight 0 and codes zeroed above)
+        pb = __builtin_bit_cast(s16x4, make_uint2(pack_bf16x2(pe[0] * exp_scale(vexp, 0), pe[1] * exp_scale(vexp, 1)),
+                                                  pack_bf16x2(pe[2] * exp_scale(vexp, 2), pe[3] * exp_scale(vexp, 3))));
+      }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt][nt] = mfma16x16x16(__builtin_bit_cast(s16x4, v[dt]), pb, O[dt][nt]);
     }
@@ -1117,6 +1201,67 @@ __global__ void append_kv_framed_kernel(uint16_t* kpool, uint16_t* vpool, const 
     vpool[((static_cast<size_t>(blk) * Hkv + h) * D + d) * kBlock + row] = vnew[src + d];
 }
 
+// FP8 append: each new K row and V row (128 values of one token and head) is
+// quantised whole.  Exponent e = the smallest with max|x| <= 448 * 2^e (at
+// least -127; 0 for an all-zero row); code = x * 2^-e rounded to the nearest
+// e4m3 value, ties to even, saturated at 448; the sign is kept (also of zero).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t code;
+  if (a >= 448.0f) {
+    code = 0x7eu;
+  } else if (a < 0.015625f) {                     // below 2^-6: steps of 2^-9 (8 = smallest normal)
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  } else {
+    const int E = __builtin_amdgcn_frexp_expf(a) - 1;                  // a in [2^E, 2^(E+1))
+    const int m = static_cast<int>(__builtin_rintf(__builtin_amdgcn_ldexpf(a, 3 - E)));   // 8..16
+    code = static_cast<uint32_t>((E + 7) * 8 + (m - 8));              // m = 16 carries into the exponent
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ int fp8_row_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const int Ea = __builtin_amdgcn_frexp_expf(amax) - 1;               // amax in [2^Ea, 2^(Ea+1))
+  if (Ea - 7 <= -127) return -127;
+  return (amax <= __builtin_amdgcn_ldexpf(1.75f, Ea)) ? Ea - 8 : Ea - 7;   // 448 = 1.75 * 2^8
+}
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// One wave per (token, KV head); lane l holds channels 2l, 2l+1.
+__global__ __launch_bounds__(64) void append_kv_fp8_kernel(uint8_t* kpool, uint8_t* vpool, const uint16_t* knew,
+                                                           const uint16_t* vnew, const int64_t* slots, int Hkv) {
+  const int i = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
+  const int64_t slot = slots[i];
+  const int64_t blk = slot / kBlock;
+  const int row = static_cast<int>(slot - blk * kBlock);
+  const size_t src = (static_cast<size_t>(i) * Hkv + h) * kPD;
+  const uint32_t kw = reinterpret_cast<const uint32_t*>(knew + src)[l];
+  const uint32_t vw = reinterpret_cast<const uint32_t*>(vnew + src)[l];
+  const float k0 = bf_lo(kw), k1 = bf_hi(kw);
+  const float v0 = bf_lo(vw), v1 = bf_hi(vw);
+  const int ek = fp8_row_exponent(wave_max64(fmaxf(fabsf(k0), fabsf(k1))));
+  const int ev = fp8_row_exponent(wave_max64(fmaxf(fabsf(v0), fabsf(v1))));
+  const size_t chunk = (static_cast<size_t>(blk) * Hkv + h) * kChunk8;
+  uint8_t* kc = kpool + chunk;
+  uint8_t* vc = vpool + chunk;
+  const uint32_t c0 = f32_to_e4m3(__builtin_amdgcn_ldexpf(k0, -ek));
+  const uint32_t c1 = f32_to_e4m3(__builtin_amdgcn_ldexpf(k1, -ek));
+  reinterpret_cast<uint16_t*>(kc + row * kPD)[l] = static_cast<uint16_t>(c0 | (c1 << 8));
+  vc[(2 * l) * kBlock + row] = static_cast<uint8_t>(f32_to_e4m3(__builtin_amdgcn_ldexpf(v0, -ev)));
+  vc[(2 * l + 1) * kBlock + row] = static_cast<uint8_t>(f32_to_e4m3(__builtin_amdgcn_ldexpf(v1, -ev)));
+  if (l == 0) {
+    kc[16 * kPD + row] = static_cast<uint8_t>(static_cast<int8_t>(ek));
+    vc[16 * kPD + row] = static_cast<uint8_t>(static_cast<int8_t>(ev));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Table decode, exactly as the attention kernels see it.
 // ---------------------------------------------------------------------------
@@ -1195,6 +1340,7 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
 
   const bool framed = batch->frame_starts != nullptr;
   if (framed && (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE)) return LAZYATTN_EUNSUPPORTED;
+  if (cfg->kv_format != LAZYATTN_KV_PLAIN) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32) {
     if (max_q_len > 0x7fffffff || R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), cu_q_lens, static_cast<const float*>(k_pool),
@@ -1231,6 +1377,33 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   return launched();
 }
 
+template <int PEV, int NTV, int KV8>
+static void launch_decode_one(dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
+  if (lds > 65536)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<PEV, NTV, KV8>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipLaunchKernelGGL((decode_bf16_kernel<PEV, NTV, KV8>), grid, dim3(256), lds, stream, a);
+}
+
+template <int KV8>
+static void launch_decode(int pe_sel, int nt, dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
+  if (nt == 1) {
+    switch (pe_sel) {
+      case kPeFramed: launch_decode_one<kPeFramed, 1, KV8>(grid, lds, stream, a); break;
+      case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 1, KV8>(grid, lds, stream, a); break;
+      case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 1, KV8>(grid, lds, stream, a); break;
+      default: launch_decode_one<LAZYATTN_PE_ALIBI, 1, KV8>(grid, lds, stream, a); break;
+    }
+  } else {
+    switch (pe_sel) {
+      case kPeFramed: launch_decode_one<kPeFramed, 2, KV8>(grid, lds, stream, a); break;
+      case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 2, KV8>(grid, lds, stream, a); break;
+      case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 2, KV8>(grid, lds, stream, a); break;
+      default: launch_decode_one<LAZYATTN_PE_ALIBI, 2, KV8>(grid, lds, stream, a); break;
+    }
+  }
+}
+
 static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, const void* k_pool,
                                      const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
                                      int32_t num_splits, void* out, void* workspace, size_t workspace_bytes,
@@ -1248,6 +1421,7 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
 
   const bool framed = batch->frame_starts != nullptr;
   if (framed && (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE)) return LAZYATTN_EUNSUPPORTED;
+  if (framed && cfg->kv_format != LAZYATTN_KV_PLAIN) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32) {
     if (R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), nullptr, static_cast<const float*>(k_pool),
@@ -1273,29 +1447,11 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   const dim3 grid(splits, Hkv, R);
   const int nt = G <= 16 ? 1 : 2;
   const size_t lds = decode_lds_bytes(nt, G);
-#define LAZYATTN_DECODE(PEV, NTV)                                                                     \
-  do {                                                                                              \
-    if (lds > 65536)                                                                                \
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<PEV, NTV>),       \
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)); \
-    hipLaunchKernelGGL((decode_bf16_kernel<PEV, NTV>), grid, dim3(256), lds, stream, a);            \
-  } while (0)
-  if (nt == 1) {
-    switch (framed ? kPeFramed : cfg->pe) {
-      case kPeFramed: LAZYATTN_DECODE(kPeFramed, 1); break;
-      case LAZYATTN_PE_ROPE: LAZYATTN_DECODE(LAZYATTN_PE_ROPE, 1); break;
-      case LAZYATTN_PE_NONE: LAZYATTN_DECODE(LAZYATTN_PE_NONE, 1); break;
-      default: LAZYATTN_DECODE(LAZYATTN_PE_ALIBI, 1); break;
-    }
-  } else {
-    switch (framed ? kPeFramed : cfg->pe) {
-      case kPeFramed: LAZYATTN_DECODE(kPeFramed, 2); break;
-      case LAZYATTN_PE_ROPE: LAZYATTN_DECODE(LAZYATTN_PE_ROPE, 2); break;
-      case LAZYATTN_PE_NONE: LAZYATTN_DECODE(LAZYATTN_PE_NONE, 2); break;
-      default: LAZYATTN_DECODE(LAZYATTN_PE_ALIBI, 2); break;
-    }
-  }
-#undef LAZYATTN_DECODE
+  const int pe_sel = framed ? kPeFramed : cfg->pe;
+  if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3)
+    launch_decode<1>(pe_sel, nt, grid, lds, stream, a);
+  else
+    launch_decode<0>(pe_sel, nt, grid, lds, stream, a);
   *splits_out = splits;
   return launched();
 }
@@ -1370,7 +1526,11 @@ lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, voi
   if (!k_pool || !v_pool || !k_new || !v_new || !slots || num_blocks < 1) return LAZYATTN_EINVAL;
   if (cfg->num_kv_heads > 65535) return LAZYATTN_EUNSUPPORTED;
   const dim3 grid(n, cfg->num_kv_heads);
-  if (cfg->dtype == LAZYATTN_BF16) {
+  if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3) {
+    hipLaunchKernelGGL(append_kv_fp8_kernel, grid, dim3(64), 0, stream, static_cast<uint8_t*>(k_pool),
+                       static_cast<uint8_t*>(v_pool), static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), slots, cfg->num_kv_heads);
+  } else if (cfg->dtype == LAZYATTN_BF16) {
     hipLaunchKernelGGL(append_kv_kernel<uint16_t>, grid, dim3(128), 0, stream, static_cast<uint16_t*>(k_pool),
                        static_cast<uint16_t*>(v_pool), static_cast<const uint16_t*>(k_new),
                        static_cast<const uint16_t*>(v_new), slots, cfg->num_kv_heads, cfg->head_dim);
@@ -1388,6 +1548,7 @@ lazyattn_status lazyattn_append_kv_framed(const lazyattn_config* cfg, void* k_po
   lazyattn_status st = check_config(cfg);
   if (st != LAZYATTN_OK) return st;
   if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE) return LAZYATTN_EUNSUPPORTED;
+  if (cfg->kv_format != LAZYATTN_KV_PLAIN) return LAZYATTN_EUNSUPPORTED;
   if (n < 0 || num_blocks < 0) return LAZYATTN_EINVAL;
   if (n == 0) return LAZYATTN_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slots || !frame_index || num_blocks < 1) return LAZYATTN_EINVAL;
@@ -1408,6 +1569,7 @@ lazyattn_status lazyattn_materialize_kv(const lazyattn_config* cfg, const void* 
   if ((st = check_batch(batch)) != LAZYATTN_OK) return st;
   if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE) return LAZYATTN_EUNSUPPORTED;
   if (batch->frame_starts) return LAZYATTN_EUNSUPPORTED;     // copies are made from a content-only pool
+  if (cfg->kv_format != LAZYATTN_KV_PLAIN) return LAZYATTN_EUNSUPPORTED;
   if (batch->num_reqs == 0 || batch->max_entries == 0) return LAZYATTN_OK;
   if (!k_pool || !v_pool || !dst_tables || !dst_k_pool || !dst_v_pool || num_blocks < 1 || dst_num_blocks < 1)
     return LAZYATTN_EINVAL;

@@ -25,10 +25,10 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 def config_for(spec, pe: str = None, softmax_scale: float = 0.0, exact_max: bool = False,
-               inv_freq: np.ndarray = None) -> _abi.Config:
+               inv_freq: np.ndarray = None, kv_format: str = "plain") -> _abi.Config:
     return _abi.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype,
                             pe or spec.pe, spec.rope_theta, softmax_scale, block_size=spec.block_size,
-                            exact_max=exact_max, inv_freq=inv_freq)
+                            exact_max=exact_max, inv_freq=inv_freq, kv_format=kv_format)
 
 
 class DevicePools:
@@ -49,21 +49,30 @@ class DevicePools:
         self.v[idx] = to_device(vp.data, s.dtype, device)
 
 
-class FramedPools:
-    """K/V pools holding keys in document-local frames (key stored as R(j) k, j
-    its index inside its document), same layouts as DevicePools.  Every
-    referenced document is written through lazyattn_append_kv_framed."""
+class WrittenPools:
+    """K/V pools whose documents are written by the library's own append:
+    lazyattn_append_kv (FP8 pools: quantised there), or with ``framed``
+    lazyattn_append_kv_framed (keys in document-local frames, R(j) k with j the
+    index inside the document).  Never-written slots hold NaN (FP8: code 0xFF)."""
+
+    framed = False
 
     def __init__(self, wl, cfg, device="cuda"):
         s = wl.spec
         if s.dtype != "bf16":
-            raise ValueError("document-local frames are bf16 only")
-        dt = torch_dtype(s.dtype)
+            raise ValueError("written pools are bf16 only")
         nb = wl.num_blocks
         self.num_blocks = nb
         self.dtype = s.dtype
-        self.k = torch.full((nb, s.num_kv_heads, s.block_size, s.head_dim), float("nan"), dtype=dt, device=device)
-        self.v = torch.full((nb, s.num_kv_heads, s.head_dim, s.block_size), float("nan"), dtype=dt, device=device)
+        self.fp8 = cfg.kv_format == _abi.KV_FORMATS["fp8"]
+        if self.fp8:
+            shape = (nb, s.num_kv_heads, _abi.FP8_CHUNK_BYTES)
+            self.k = torch.full(shape, 0xFF, dtype=torch.uint8, device=device)
+            self.v = torch.full(shape, 0xFF, dtype=torch.uint8, device=device)
+        else:
+            dt = torch_dtype(s.dtype)
+            self.k = torch.full((nb, s.num_kv_heads, s.block_size, s.head_dim), float("nan"), dtype=dt, device=device)
+            self.v = torch.full((nb, s.num_kv_heads, s.head_dim, s.block_size), float("nan"), dtype=dt, device=device)
         ks, vs, sl, fi = [], [], [], []
         for d in wl.referenced_docs:
             k, v = wl.doc_kv(int(d))
@@ -78,9 +87,18 @@ class FramedPools:
             sl, fi = np.concatenate(sl).astype(np.int64), np.concatenate(fi).astype(np.int32)
             for a in range(0, sl.size, chunk):
                 b = min(sl.size, a + chunk)
-                _abi.append_kv_framed(cfg, self.k, self.v, nb, to_device(k[a:b], s.dtype, device),
-                                      to_device(v[a:b], s.dtype, device), torch.from_numpy(sl[a:b]).to(device),
-                                      torch.from_numpy(fi[a:b]).to(device))
+                kd, vd = to_device(k[a:b], s.dtype, device), to_device(v[a:b], s.dtype, device)
+                sd = torch.from_numpy(sl[a:b]).to(device)
+                if self.framed:
+                    _abi.append_kv_framed(cfg, self.k, self.v, nb, kd, vd, sd, torch.from_numpy(fi[a:b]).to(device))
+                else:
+                    _abi.append_kv(cfg, self.k, self.v, nb, kd, vd, sd)
+
+
+class FramedPools(WrittenPools):
+    """Pools in document-local frames (see WrittenPools)."""
+
+    framed = True
 
 
 class DeviceTables:
@@ -115,7 +133,7 @@ def append_tokens(cfg, pools: DevicePools, inputs: dict, dtype: str, device="cud
     k = to_device(inputs["k_new"], dtype, device)
     v = to_device(inputs["v_new"], dtype, device)
     sl = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).to(device)
-    if isinstance(pools, FramedPools):
+    if getattr(pools, "framed", False):
         fi = torch.from_numpy(np.ascontiguousarray(inputs["frame_index"], dtype=np.int32)).to(device)
         _abi.append_kv_framed(cfg, pools.k, pools.v, pools.num_blocks, k, v, sl, fi)
     else:

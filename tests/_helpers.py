@@ -124,3 +124,36 @@ class OracleState:
 
 def gpu_f64(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
+
+
+class OracleFp8State:
+    """The oracle's own FP8 pools for a workload: every referenced document quantised by the
+    oracle, grown by its own quantising appends; attention over the dequantised values."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        s = wl.spec
+        self.kc, self.vc = O.fp8_empty_pools(wl.num_blocks, s.num_kv_heads)
+        for d in wl.referenced_docs:
+            k, v = wl.doc_kv(int(d))
+            slots, _ = wl.doc_frame_tokens(int(d))
+            O.append_kv_fp8(self.kc, self.vc, k, v, slots, s.dtype)
+
+    def append(self, inputs):
+        if inputs is not None:
+            O.append_kv_fp8(self.kc, self.vc, inputs["k_new"], inputs["v_new"], inputs["slots"], self.wl.spec.dtype)
+
+    def _common(self, inputs):
+        s = self.wl.spec
+        return dict(ctx_lens=inputs["ctx_lens"], num_entries=inputs["num_entries"],
+                    table_words=O.pack_table(inputs["table_blocks"], inputs["table_starts"]),
+                    k_pool=O.Fp8PoolView(self.kc, "k"), v_pool=O.Fp8PoolView(self.vc, "v"),
+                    num_kv_heads=s.num_kv_heads, block_size=s.block_size, dtype=s.dtype, pool_dtype="f64",
+                    rope_theta=s.rope_theta)
+
+    def prefill(self, inputs, token_subset=None, requests=None, pe=None):
+        return O.prefill(q=inputs["q"], cu_q_lens=inputs["cu_q_lens"], pe=pe or self.wl.spec.pe,
+                         token_subset=token_subset, requests=requests, **self._common(inputs))
+
+    def decode(self, inputs, requests=None, pe=None):
+        return O.decode(q=inputs["q"], pe=pe or self.wl.spec.pe, requests=requests, **self._common(inputs))

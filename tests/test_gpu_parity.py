@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 import oracle as O  # noqa: E402
 import workloads as W  # noqa: E402
 from position_agnostic_kv_pool_amd import _abi, staging  # noqa: E402
-from _helpers import OracleState, assert_parity, diff_stats, gpu_f64, half_ulp, within  # noqa: E402
+from _helpers import OracleFp8State, OracleState, assert_parity, diff_stats, gpu_f64, half_ulp, within  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -647,6 +647,86 @@ def test_rope_variants_prefill_and_decode(variant):
             fout = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, framed=True).run(fpools))
             fmx, fmn = assert_parity(fout, ref, "bf16", f"{variant} framed decode {step}")
             say(f"{variant} decode step {step}: max {mx:.2e} mean {mn:.2e}; framed max {fmx:.2e} mean {fmn:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# FP8 (e4m3) pools: bytes bit-exact with the oracle's quantiser, attention
+# against the oracle over the dequantised values
+# ---------------------------------------------------------------------------
+def test_fp8_append_bit_exact():
+    say("FP8 append: 8B documents and query tokens quantised by lazyattn_append_kv")
+    wl = W.build_workload(W.spec(2, requests=[2]))
+    s = wl.spec
+    cfg = staging.config_for(s, kv_format="fp8")
+    pools = staging.WrittenPools(wl, cfg, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    sync()
+    orc = OracleFp8State(wl)
+    orc.append(pb)
+    blocks = np.unique(np.concatenate([wl.doc_blocks(int(d)) for d in wl.referenced_docs] + [pb["slots"] // 16]))
+    bi = torch.from_numpy(blocks).to(DEV)
+    gk, gv = pools.k[bi].cpu().numpy(), pools.v[bi].cpu().numpy()
+    assert np.array_equal(gk, orc.kc[blocks]), f"K chunks differ in {int(np.sum(gk != orc.kc[blocks]))} bytes"
+    assert np.array_equal(gv, orc.vc[blocks]), f"V chunks differ in {int(np.sum(gv != orc.vc[blocks]))} bytes"
+    say(f"FP8 append: {blocks.size} blocks x {s.num_kv_heads} heads bit-exact")
+
+
+def test_fp8_decode_llama8b():
+    say("FP8 decode: 8B, 16 requests, steps 0 and 16 (RoPE), step 16 rotation-free and ALiBi")
+    wl = W.build_workload(W.spec(3, requests=[16], n_decode=17))
+    s = wl.spec
+    cfg = staging.config_for(s, kv_format="fp8")
+    pools = staging.WrittenPools(wl, cfg, DEV)
+    orc = OracleFp8State(wl)
+    hist = wl.tokens_before_step(0)
+    staging.append_tokens(cfg, pools, hist, s.dtype, DEV)
+    orc.append(hist)
+    for step in range(17):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+        if step in (0, 16):
+            pes = ("rope",) if step == 0 else ("rope", "none", "alibi")
+            for pe in pes:
+                c = staging.config_for(s, pe=pe, kv_format="fp8")
+                out = gpu_f64(staging.DecodeCall(c, s, d, DEV).run(pools))
+                ref = orc.decode(d, pe=pe)
+                mx, mn = assert_parity(out, np.stack([ref[r] for r in range(len(ref))]), "bf16",
+                                       f"FP8 8B decode {pe} step {step}")
+                say(f"FP8 8B decode {pe} step {step}: max {mx:.2e} mean {mn:.2e}")
+
+
+def test_fp8_decode_long_context_and_mqa():
+    say("FP8 decode: 70B 32k step 0 at splits 0 and 7; MQA (G = 32) step 0")
+    wl = W.build_workload(W.spec(4, requests=[1], n_decode=1))
+    s = wl.spec
+    cfg = staging.config_for(s, kv_format="fp8")
+    pools = staging.WrittenPools(wl, cfg, DEV)
+    orc = OracleFp8State(wl)
+    for inp in (wl.prefill_batch(), wl.decode_step(0)):
+        staging.append_tokens(cfg, pools, inp, s.dtype, DEV)
+        orc.append(inp)
+    d = wl.decode_step(0)
+    ref = orc.decode(d)
+    for splits in (0, 7):
+        out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, num_splits=splits).run(pools))
+        mx, mn = assert_parity(out, ref[0][None], "bf16", f"FP8 70B decode splits={splits}")
+        say(f"FP8 70B decode splits={splits}: max {mx:.2e} mean {mn:.2e}")
+    wl = W.build_workload(W.spec(5, requests=[2, 24], skew=1.2))
+    s = wl.spec
+    cfg = staging.config_for(s, kv_format="fp8")
+    pools = staging.WrittenPools(wl, cfg, DEV)
+    orc = OracleFp8State(wl)
+    for inp in (wl.tokens_before_step(0), wl.decode_step(0)):
+        staging.append_tokens(cfg, pools, inp, s.dtype, DEV)
+        orc.append(inp)
+    d = wl.decode_step(0)
+    out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+    reqs = list(range(0, len(d["ctx_lens"]), 3))
+    ref = orc.decode(d, requests=reqs)
+    mx, mn = assert_parity(out[reqs], np.stack([ref[r] for r in reqs]), "bf16", "FP8 MQA decode")
+    say(f"FP8 MQA decode: max {mx:.2e} mean {mn:.2e}")
 
 
 # ---------------------------------------------------------------------------

@@ -526,3 +526,73 @@ def test_llama31_rescaling_structure():
     fd = O.rope_inv_freq_llama31(1 << 16, theta, 8.0, 1.0, 4.0, L)
     bd = O.rope_inv_freq(1 << 16, theta)
     assert np.max(np.abs(np.diff(np.log(fd)) - np.diff(np.log(bd)))) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP e4m3) pool: the format's definition and the quantisation rule
+# ---------------------------------------------------------------------------
+def test_e4m3_values_from_the_format():
+    assert O.e4m3_value(0x38) == 1.0 and O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0xFE) == -448.0
+    assert O.e4m3_value(0x08) == 2.0 ** -6 and O.e4m3_value(0x01) == 2.0 ** -9 and O.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert O.e4m3_value(0x40) == 2.0 and O.e4m3_value(0x3F) == 1.875
+    assert math.isnan(O.e4m3_value(0x7F)) and math.isnan(O.e4m3_value(0xFF))
+    assert O.e4m3_value(0x80) == 0.0 and math.copysign(1.0, O.e4m3_value(0x80)) == -1.0
+    finite = [c for c in range(256) if not math.isnan(O.e4m3_value(c))]
+    assert len(finite) == 254
+    assert len({O.e4m3_value(c) for c in finite}) == 253           # +0 and -0 compare equal
+
+
+def test_e4m3_encode_round_trip_ties_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = np.array([O.e4m3_value(int(c)) for c in codes])
+    np.testing.assert_array_equal(O.e4m3_encode(vals), codes)
+    # midpoints round to the even code
+    assert O.e4m3_encode(np.array([1.0625]))[0] == 0x38             # between 1 (0x38) and 1.125 (0x39)
+    assert O.e4m3_encode(np.array([1.1875]))[0] == 0x3A             # between 1.125 and 1.25
+    assert O.e4m3_encode(np.array([-1.1875]))[0] == 0xBA
+    assert O.e4m3_encode(np.array([2.0 ** -10]))[0] == 0x00         # between 0 and the first subnormal
+    assert O.e4m3_encode(np.array([3 * 2.0 ** -10]))[0] == 0x02
+    assert O.e4m3_encode(np.array([1.0625 + 1e-6]))[0] == 0x39
+    # saturation instead of overflow to NaN
+    np.testing.assert_array_equal(O.e4m3_encode(np.array([448.0, 460.0, 1e6, -1e6])), [0x7E, 0x7E, 0x7E, 0xFE])
+
+
+def test_fp8_row_exponent_rule_and_quantisation_error():
+    assert O.fp8_row_exponent(0.0) == 0
+    assert O.fp8_row_exponent(448.0) == 0 and O.fp8_row_exponent(448.0 * (1 + 2 ** -20)) == 1
+    assert O.fp8_row_exponent(224.0) == -1 and O.fp8_row_exponent(1.0) == -8
+    assert O.fp8_row_exponent(1.75) == -8 and O.fp8_row_exponent(1.75 * (1 + 2 ** -20)) == -7
+    assert O.fp8_row_exponent(1e-45) == -127
+    rng = np.random.default_rng(14)
+    x = (rng.standard_normal((200, 128)) * np.exp(rng.uniform(-8, 8, (200, 1)))).astype(np.float32)
+    codes, exps = O.quantize_fp8_rows(x)
+    table = np.array([O.e4m3_value(c) for c in range(256)])
+    deq = table[codes] * np.ldexp(1.0, exps.astype(np.int32))[:, None]
+    amax = np.abs(x).max(axis=1)
+    assert np.all(amax <= 448.0 * np.ldexp(1.0, exps.astype(np.int32)))
+    assert np.all(amax > 224.0 * np.ldexp(1.0, exps.astype(np.int32)))       # the smallest such exponent
+    # relative error of a normal e4m3 value: at most 2^-4 (half of the 3-bit mantissa step)
+    big = np.abs(x) >= 2.0 ** -6 * np.ldexp(1.0, exps.astype(np.int32))[:, None]
+    rel = np.abs(deq - x) / np.abs(x)
+    assert rel[big].max() <= 2.0 ** -4 + 1e-12
+
+
+def test_fp8_pool_view_dequantises_the_chunk_layout():
+    rng = np.random.default_rng(15)
+    kc, vc = O.fp8_empty_pools(3, 2)
+    k = rng.standard_normal((5, 2, 128)).astype(np.float32)
+    v = rng.standard_normal((5, 2, 128)).astype(np.float32)
+    slots = np.array([16 * 2 + 3, 16 * 2 + 4, 16 * 0 + 15, 16 * 1 + 0, 16 * 2 + 5])
+    O.append_kv_fp8(kc, vc, k, v, slots, "f32")
+    K = O.Fp8PoolView(kc, "k")[np.array([0, 1, 2])]
+    V = O.Fp8PoolView(vc, "v")[np.array([0, 1, 2])]
+    # within half a mantissa step (2^-4 relative), or half a subnormal step (2^-10 x the row's
+    # scale) for the values that fall below the smallest normal
+    _, ke = O.quantize_fp8_rows(k)
+    _, ve = O.quantize_fp8_rows(v)
+    for i, sl in enumerate(slots):
+        b, r = divmod(int(sl), 16)
+        for got, want, e in ((K[b, :, r, :], k[i], ke[i]), (V[b, :, :, r], v[i], ve[i])):
+            bound = np.maximum(2.0 ** -4 * np.abs(want), np.ldexp(1.0, e.astype(np.int32) - 10)[:, None])
+            assert np.all(np.abs(got - want) <= bound)
+    assert np.isnan(K[0, :, 0, :]).all()                                # never written
