@@ -175,6 +175,11 @@ def bench_prefill(torch, args, W, staging, _abi):
     fpools = staging.FramedPools(wl, cfg, "cuda")
     staging.append_tokens(cfg, fpools, pb, s.dtype, "cuda")
     call_framed = staging.PrefillCall(cfg, s, pb, "cuda", framed=True)
+    # and over an FP8 pool
+    cfg8 = staging.config_for(s, kv_format="fp8")
+    pools8 = staging.WrittenPools(wl, cfg8, "cuda")
+    staging.append_tokens(cfg8, pools8, pb, s.dtype, "cuda")
+    call8 = staging.PrefillCall(cfg8, s, pb, "cuda")
     torch.cuda.synchronize()
     timer = Timer(torch)
     for _ in range(args.warmup):
@@ -185,14 +190,16 @@ def bench_prefill(torch, args, W, staging, _abi):
     # back-to-back between two events
     ms = timer.span(lambda: call.run(pools), args.steps)
     # the attention kernel alone and its rotation-free control, three interleaved rounds (medians)
-    att, att_none, step_none, att_framed = [], [], [], []
+    att, att_none, step_none, att_framed, att_fp8 = [], [], [], [], []
     call_framed.run(fpools)
+    call8.run(pools8)
     for _ in range(3):
         att.append(timer.span(lambda: call.attend(pools), args.steps))
         att_none.append(timer.span(lambda: call_none.attend(pools), args.steps))
         step_none.append(timer.span(lambda: call_none.run(pools), args.steps))
         att_framed.append(timer.span(lambda: call_framed.attend(fpools), args.steps))
-    del fpools
+        att_fp8.append(timer.span(lambda: call8.attend(pools8), args.steps))
+    del fpools, pools8
     # cold: the last-level cache flushed by a 512 MB write before each single launch
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     cold, cold_none = [], []
@@ -213,7 +220,8 @@ def bench_prefill(torch, args, W, staging, _abi):
     del mat
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
     return dict(wl=wl, pb=pb, ms=ms, ms_attend=med(att), ms_none=med(step_none), ms_none_attend=med(att_none),
-                att=att, att_none=att_none, att_framed=att_framed, ms_framed_attend=med(att_framed), cold=med(cold), cold_none=med(cold_none), flops=flops, base=base,
+                att=att, att_none=att_none, att_framed=att_framed, ms_framed_attend=med(att_framed),
+                ms_fp8_attend=med(att_fp8), cold=med(cold), cold_none=med(cold_none), flops=flops, base=base,
                 splits=call.splits, pools=pools)
 
 
@@ -431,6 +439,10 @@ def main() -> int:
             "copied_bytes": int(pre["base"]["copied_bytes"]),
             "deferred_step_us": round(pre["ms"] * 1e3, 2),
             "deferred_speedup": round(pre["base"]["total"] / pre["ms"], 3)},
+        "fp8_pool_prefill": {
+            "what": "the prefill over an e4m3 pool with per-row power-of-two scales, converted to bf16 in staging",
+            "attention_us": round(pre["ms_fp8_attend"] * 1e3, 2),
+            "vs_bf16_pool": round(pre["ms_attend"] / pre["ms_fp8_attend"], 3)},
         "document_frames": {
             "what": "the same attention over a pool whose keys carry their index inside their document "
                     "(stored R(j) k): prefill turns each key entry once by R(F - p0), decode turns the query "

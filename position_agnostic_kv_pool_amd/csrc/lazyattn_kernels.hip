@@ -212,7 +212,7 @@ __device__ __forceinline__ int krow_of(int E, int rho) {
   return 16 * E + 8 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3);
 }
 
-template <int PE>
+template <int PE, int KV8>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const PrefillArgs A) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][4 * kVE];
@@ -319,16 +319,59 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   if (PE == LAZYATTN_PE_ROPE) r1 = unit_phase(1, A.rope.rev[lane]);
   uint32_t kr[8];
   uint4 vr[2];
+  // FP8 pool: kr[k] holds the two codes of row 8 part + k (low 16 bits), vr[cc].xy
+  // the 8 codes, and kx / vx the exponents of the 8 key rows / 8 tokens
+  uint2 kx = make_uint2(0, 0), vx = make_uint2(0, 0);
   // entries past the split's end (length 0) read block 0: their keys are
   // masked out of the scores and their V rows zeroed when staged
   auto load_kv = [&](int blk) {
     const size_t base = static_cast<size_t>(static_cast<uint32_t>(blk)) * Hkv + kvh;
-    const uint32_t* kp = reinterpret_cast<const uint32_t*>(A.kpool + base * (kBlock * kPD) + 8 * part * kPD) + lane;
-    const uint16_t* vp = A.vpool + base * (kPD * kBlock) + (64 * part + (lane >> 1)) * kBlock + 8 * (lane & 1);
+    if (KV8) {
+      const uint8_t* kc = reinterpret_cast<const uint8_t*>(A.kpool) + base * kChunk8;
+      const uint8_t* vc = reinterpret_cast<const uint8_t*>(A.vpool) + base * kChunk8;
+      const uint16_t* kp = reinterpret_cast<const uint16_t*>(kc + 8 * part * kPD) + lane;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
+      for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
+      kx = *reinterpret_cast<const uint2*>(kc + 16 * kPD + 8 * part);
+      const uint8_t* vp = vc + (64 * part + (lane >> 1)) * kBlock + 8 * (lane & 1);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) vr[cc] = *reinterpret_cast<const uint4*>(vp + 32 * cc * kBlock);
+      for (int cc = 0; cc < 2; ++cc) {
+        const uint2 w = *reinterpret_cast<const uint2*>(vp + 32 * cc * kBlock);
+        vr[cc] = make_uint4(w.x, w.y, 0u, 0u);
+      }
+      vx = *reinterpret_cast<const uint2*>(vc + 16 * kPD + 8 * (lane & 1));
+    } else {
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(A.kpool + base * (kBlock * kPD) + 8 * part * kPD) + lane;
+      const uint16_t* vp = A.vpool + base * (kPD * kBlock) + (64 * part + (lane >> 1)) * kBlock + 8 * (lane & 1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) vr[cc] = *reinterpret_cast<const uint4*>(vp + 32 * cc * kBlock);
+    }
+  };
+  // FP8: the staged key row k (its codes, times 2^exponent) as bf16, turned by ph
+  // for RoPE; V codes times their tokens' 2^exponent as bf16.  Exact but for
+  // the rotation's rounding.
+  auto key_fp8 = [&](int k, float2 ph) -> uint32_t {
+    const float sc = exp_scale(k < 4 ? kx.x : kx.y, k & 3);
+    if (PE == LAZYATTN_PE_ROPE) {
+      const float2 x = fp8x2_to_f32(kr[k], false);
+      const float x0 = x.x * sc, x1 = x.y * sc;
+      return pack_bf16x2(x0 * ph.x - x1 * ph.y, x0 * ph.y + x1 * ph.x);
+    }
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(kr[k]), sc, false));
+  };
+  auto convert_v8 = [&]() {
+    float sc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sc[t] = exp_scale(t < 4 ? vx.x : vx.y, t & 3);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const float2 a = fp8x2_to_f32(vr[cc].x, false), b = fp8x2_to_f32(vr[cc].x, true);
+      const float2 c2 = fp8x2_to_f32(vr[cc].y, false), d = fp8x2_to_f32(vr[cc].y, true);
+      vr[cc] = make_uint4(pack_bf16x2(a.x * sc[0], a.y * sc[1]), pack_bf16x2(b.x * sc[2], b.y * sc[3]),
+                          pack_bf16x2(c2.x * sc[4], c2.y * sc[5]), pack_bf16x2(d.x * sc[6], d.y * sc[7]));
+    }
   };
   // zero V rows past the entry's length (their weights are 0, but the pool's
   // padding may hold anything)
@@ -406,10 +449,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         float2 ph = unit_phase_turns(st - p0 + 8 * part, A.rope.rev[lane]);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          kr[k] = rotate_pair(kr[k], ph);
+          kr[k] = KV8 ? key_fp8(k, ph) : rotate_pair(kr[k], ph);
           ph = cmul(ph, r1);
         }
+      } else if (KV8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) kr[k] = key_fp8(k, make_float2(1.f, 0.f));
       }
+      if (KV8) convert_v8();
       if (PE == kPeFramed) {
         // every row of the entry turns by the same R(F - p0)
         const float2 ph = unit_phase_turns(__builtin_amdgcn_readlane(fv0, E_own) - p0, A.rope.rev[lane]);
@@ -454,11 +501,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) S[tau][nt] = mfma32x32x16(ak[kk & 1][tau], qf[8 * nt + kk], S[tau][nt]);
         if (PE == LAZYATTN_PE_ROPE) {
-          kr[kk] = rotate_pair(kr[kk], ph);
+          kr[kk] = KV8 ? key_fp8(kk, ph) : rotate_pair(kr[kk], ph);
           ph = cmul(ph, r1);
+        } else if (KV8) {
+          kr[kk] = key_fp8(kk, ph);
         }
         if (PE == kPeFramed) kr[kk] = rotate_pair(kr[kk], ph);
-        if (kk == 3) mask_v(nln);
+        if (kk == 3) {
+          if (KV8) convert_v8();
+          mask_v(nln);
+        }
       }
       stage_write((i + 1) & 1);
       // loads of tile i + 2, words of tile i + 3
@@ -1339,8 +1391,9 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   const float scale = softmax_scale_of(cfg);
 
   const bool framed = batch->frame_starts != nullptr;
+  const bool fp8 = cfg->kv_format == LAZYATTN_KV_FP8_E4M3;
   if (framed && (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE)) return LAZYATTN_EUNSUPPORTED;
-  if (cfg->kv_format != LAZYATTN_KV_PLAIN) return LAZYATTN_EUNSUPPORTED;
+  if (framed && fp8) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32) {
     if (max_q_len > 0x7fffffff || R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), cu_q_lens, static_cast<const float*>(k_pool),
@@ -1367,11 +1420,20 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
                 total_q, m_q, prefill_entries_per_split(batch->max_entries, splits), splits,
                 (cfg->flags & LAZYATTN_FLAG_EXACT_MAX) ? 1 : 0, scale * kLog2e, rope};
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(gz));
-  switch (framed ? kPeFramed : cfg->pe) {
-    case kPeFramed: hipLaunchKernelGGL(prefill_bf16_kernel<kPeFramed>, grid, dim3(kPrefillThreads), 0, stream, a); break;
-    case LAZYATTN_PE_ROPE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ROPE>, grid, dim3(kPrefillThreads), 0, stream, a); break;
-    case LAZYATTN_PE_NONE: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_NONE>, grid, dim3(kPrefillThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL(prefill_bf16_kernel<LAZYATTN_PE_ALIBI>, grid, dim3(kPrefillThreads), 0, stream, a); break;
+  const dim3 block(kPrefillThreads);
+  if (fp8) {
+    switch (cfg->pe) {
+      case LAZYATTN_PE_ROPE: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_ROPE, 1>), grid, block, 0, stream, a); break;
+      case LAZYATTN_PE_NONE: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_NONE, 1>), grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_ALIBI, 1>), grid, block, 0, stream, a); break;
+    }
+  } else {
+    switch (framed ? kPeFramed : cfg->pe) {
+      case kPeFramed: hipLaunchKernelGGL((prefill_bf16_kernel<kPeFramed, 0>), grid, block, 0, stream, a); break;
+      case LAZYATTN_PE_ROPE: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_ROPE, 0>), grid, block, 0, stream, a); break;
+      case LAZYATTN_PE_NONE: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_NONE, 0>), grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_ALIBI, 0>), grid, block, 0, stream, a); break;
+    }
   }
   *splits_out = splits;
   return launched();

@@ -672,6 +672,46 @@ def test_fp8_append_bit_exact():
     say(f"FP8 append: {blocks.size} blocks x {s.num_kv_heads} heads bit-exact")
 
 
+@pytest.mark.parametrize("pe,num_splits,exact", [("rope", 0, False), ("rope", 1, False), ("rope", 0, True),
+                                                  ("none", 0, False), ("alibi", 0, False)])
+def test_fp8_prefill_llama8b(pe, num_splits, exact):
+    say(f"FP8 prefill: 8B, 4 requests, pe={pe} splits={num_splits} exact_max={exact}")
+    wl = W.build_workload(W.spec(2, requests=[4]))
+    s = wl.spec
+    cfg = staging.config_for(s, pe=pe, exact_max=exact, kv_format="fp8")
+    pools = staging.WrittenPools(wl, cfg, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    got = gpu_f64(staging.PrefillCall(cfg, s, pb, DEV, num_splits).run(pools))
+    orc = OracleFp8State(wl)
+    orc.append(pb)
+    ref = orc.prefill(pb, pe=pe)
+    cu = pb["cu_q_lens"]
+    mx, mn = assert_parity(np.concatenate([got[cu[r]:cu[r + 1]] for r in ref]), np.concatenate([ref[r] for r in ref]),
+                           "bf16", f"FP8 8B prefill {pe}")
+    say(f"FP8 8B prefill {pe} splits={num_splits} exact={exact}: max {mx:.2e} mean {mn:.2e}")
+
+
+def test_fp8_prefill_mqa_sampled():
+    say("FP8 prefill: MQA (G = 32), 8 requests, sampled rows")
+    wl = W.build_workload(W.spec(5, requests=[8, 0], skew=0.8))
+    s = wl.spec
+    cfg = staging.config_for(s, kv_format="fp8")
+    pools = staging.WrittenPools(wl, cfg, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    got = gpu_f64(staging.PrefillCall(cfg, s, pb, DEV).run(pools))
+    orc = OracleFp8State(wl)
+    orc.append(pb)
+    rng = np.random.default_rng(4)
+    subset = {r: sample_tokens(128, 12, rng) for r in range(len(pb["ctx_lens"]))}
+    ref = orc.prefill(pb, token_subset=subset)
+    cu = pb["cu_q_lens"]
+    g = np.concatenate([got[cu[r] + subset[r]] for r in ref])
+    mx, mn = assert_parity(g, np.concatenate([ref[r] for r in ref]), "bf16", "FP8 MQA prefill")
+    say(f"FP8 MQA prefill: max {mx:.2e} mean {mn:.2e}")
+
+
 def test_fp8_decode_llama8b():
     say("FP8 decode: 8B, 16 requests, steps 0 and 16 (RoPE), step 16 rotation-free and ALiBi")
     wl = W.build_workload(W.spec(3, requests=[16], n_decode=17))
