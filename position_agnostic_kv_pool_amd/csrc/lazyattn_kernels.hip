@@ -758,11 +758,12 @@ constexpr int kOS = kPD + 4;  // LDS row stride (floats) of the wave-merge buffe
 constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
 template <int PE, int NT, int KV8>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
+__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) float dsm[];
   float2* bsh = reinterpret_cast<float2*>(dsm);             // [4 waves][2][64]
   float* ml_s = dsm + 4 * 2 * 64 * 2;                         // [4][NT*16][2]
   float* o_s = ml_s + 4 * NT * 16 * 2;                        // [4][G][kOS]
+  float2* rtab = reinterpret_cast<float2*>(o_s + 4 * A.G * kOS);  // [16][64] R(n), RoPE only
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
@@ -799,12 +800,17 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
       qb[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
     }
   }
-  // R(n) for this lane's key row and pairs 16g..16g+15; this lane's pair for R(S - p)
-  float2 rt[16];
+  // R(n) of lane (g, n)'s key row n at pair 16g + i, as rtab[i][lane] (a lane's
+  // 16 reads of one entry are then 64 consecutive float2 each); this lane's
+  // pair for R(S - p)
   double my_rev = 0.0;
   if (PE == LAZYATTN_PE_ROPE) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) rt[i] = unit_phase(n, A.rope.rev[16 * g + i]);
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, i = idx >> 6, l = idx & 63;
+      rtab[idx] = unit_phase(l & 15, A.rope.rev[16 * (l >> 4) + i]);
+    }
+    __syncthreads();
   }
   if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) my_rev = A.rope.rev[lane];
   // framed pool: frame starts of this request's entries, and the frame the
@@ -830,9 +836,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
     negm[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  uint4 kr[4];
-  uint2 vr[8];
-  EntryInfo cur;
   // FP8 pool: lane (g, n) holds the 32 codes of key row n, channels 32g..32g+31
   // (kr[0..1]), the codes of tokens 4g..4g+3 of channel rows 16dt+n (vr[dt].x)
   // and the exponents of key rows / tokens 4g..4g+3 (kr[2].x, kr[2].y)
@@ -859,186 +862,213 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const DecodeArgs A) {
     }
   };
 
-  // The wave-uniform entry index makes the table words scalar loads.  An
-  // entry's words (and frame start) are fetched one iteration before its K/V
-  // loads are issued, so those loads never wait on them: entry e's K/V are in
-  // flight while entry e - 4 is processed, entry e + 4's words likewise.
-  int e = __builtin_amdgcn_readfirstlane(e_begin + wave);
+  // Entries are processed in the wave-uniform order e_begin + wave, + 4, ...;
+  // the table words make scalar loads.  While one entry is processed, the K/V
+  // of the next DEPTH are in flight (FP8: two; the bf16 registers allow one),
+  // and the words of the next entry to load are fetched an entry ahead of its
+  // K/V loads, so those loads never wait on them.
+  constexpr int DEPTH = KV8 ? 2 : 1;
+  uint4 krb[DEPTH][4];
+  uint2 vrb[DEPTH][8];
+  EntryInfo curb[DEPTH];
+  int frb[DEPTH];
   EntryInfo nx{};
-  int fr_next = 0, fr_nx = 0;
-  if (e < e_end) {
-    cur = entry_info(trow, e, ne, L);
-    load_kv(cur.blk, kr, vr);
-    if (PE == kPeFramed) fr_next = frow[e];
-    if (e + 4 < e_end) {
-      nx = entry_info(trow, e + 4, ne, L);
-      if (PE == kPeFramed) fr_nx = frow[e + 4];
+  int fr_nx = 0;
+  int e = __builtin_amdgcn_readfirstlane(e_begin + wave);
+#pragma unroll
+  for (int sl = 0; sl < DEPTH; ++sl) {
+    const int ee = e + 4 * sl;
+    frb[sl] = 0;
+    if (ee < e_end) {
+      curb[sl] = entry_info(trow, ee, ne, L);
+      load_kv(curb[sl].blk, krb[sl], vrb[sl]);
+      if (PE == kPeFramed) frb[sl] = frow[ee];
     }
   }
-  for (int it = 0; e < e_end; ++it) {
-    const EntryInfo inf = cur;
-    const int fr = fr_next;
-    uint4 k[4] = {kr[0], kr[1], kr[2], kr[3]};
-    uint2 v[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) v[dt] = vr[dt];
-    const uint32_t kexp = k[2].x, vexp = k[2].y;
-    if (KV8) {
-      // FP8 codes to bf16 operands (exact); the exponents scale S and P below
-      const uint4 c0 = k[0], c1 = k[1];
-      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      if (PE != LAZYATTN_PE_ROPE) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          k[s] = make_uint4(fp8x2_to_bf16x2(cw[2 * s], false), fp8x2_to_bf16x2(cw[2 * s], true),
-                            fp8x2_to_bf16x2(cw[2 * s + 1], false), fp8x2_to_bf16x2(cw[2 * s + 1], true));
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) v[dt] = make_uint2(fp8x2_to_bf16x2(vr[dt].x, false), fp8x2_to_bf16x2(vr[dt].x, true));
-    }
-    const int e_next = e + 4;
-    if (e_next < e_end) {
-      load_kv(nx.blk, kr, vr);
-      cur = nx;
-      fr_next = fr_nx;
-      if (e_next + 4 < e_end) {
-        nx = entry_info(trow, e_next + 4, ne, L);
-        if (PE == kPeFramed) fr_nx = frow[e_next + 4];
-      }
-    }
+  if (e + 4 * DEPTH < e_end) {
+    nx = entry_info(trow, e + 4 * DEPTH, ne, L);
+    if (PE == kPeFramed) fr_nx = frow[e + 4 * DEPTH];
+  }
 
-    // ---- framed pool: turn the query to this entry's frame, R(p - F) q ----------
-    if (PE == kPeFramed && (!q_set || fr != q_frame)) {
-      float2* bw = bsh + (wave * 2 + (q_turns & 1)) * 64;
-      bw[lane] = unit_phase_turns(p - fr, my_rev);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint32_t w4[4] = {qraw[nt][s].x, qraw[nt][s].y, qraw[nt][s].z, qraw[nt][s].w};
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float2 ph = bw[16 * g + 4 * s + jj];     // pair 16g + 4s + jj
-            const float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
-            w4[jj] = pack_bf16x2((x0 * ph.x - x1 * ph.y) * A.scale_log2, (x0 * ph.y + x1 * ph.x) * A.scale_log2);
-          }
-          qb[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-        }
-      q_frame = fr;
-      q_set = true;
-      ++q_turns;
-    }
-
-    // ---- rotate the key rows: R(S - p + n) = R(S - p) R(n) ------------------
-    bf16x8 ka[4];
-    if (PE == LAZYATTN_PE_ROPE) {
-      float2* bw = bsh + (wave * 2 + (it & 1)) * 64;
-      bw[lane] = unit_phase_turns(inf.start - p, my_rev);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // one entry: its K/V arrived in k, v
+  auto process = [&](const EntryInfo inf, const int fr, uint4 (&k)[4], uint2 (&v)[8], const int it)
+                     __attribute__((always_inline)) {
+      const uint32_t kexp = k[2].x, vexp = k[2].y;
       if (KV8) {
-        // the lane's 32 codes are still in kr[0..1] of this iteration (k[0..1])
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t c_lo = (s < 2) ? (s == 0 ? k[0].x : k[0].z) : (s == 2 ? k[1].x : k[1].z);
-          const uint32_t c_hi = (s < 2) ? (s == 0 ? k[0].y : k[0].w) : (s == 2 ? k[1].y : k[1].w);
-          uint32_t w4[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int i = 4 * s + jj;                    // pair 16g + i
-            w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[16 * g + i], rt[i]));
+        // FP8 codes to bf16 operands (exact); the exponents scale S and P below
+        const uint4 c0 = k[0], c1 = k[1];
+        const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        if (PE != LAZYATTN_PE_ROPE) {
+  #pragma unroll
+          for (int s = 0; s < 4; ++s)
+            k[s] = make_uint4(fp8x2_to_bf16x2(cw[2 * s], false), fp8x2_to_bf16x2(cw[2 * s], true),
+                              fp8x2_to_bf16x2(cw[2 * s + 1], false), fp8x2_to_bf16x2(cw[2 * s + 1], true));
+        }
+  #pragma unroll
+        for (int dt = 0; dt < 8; ++dt) v[dt] = make_uint2(fp8x2_to_bf16x2(v[dt].x, false), fp8x2_to_bf16x2(v[dt].x, true));
+      }
+
+      // ---- framed pool: turn the query to this entry's frame, R(p - F) q ----------
+      if (PE == kPeFramed && (!q_set || fr != q_frame)) {
+        float2* bw = bsh + (wave * 2 + (q_turns & 1)) * 64;
+        bw[lane] = unit_phase_turns(p - fr, my_rev);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  #pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            uint32_t w4[4] = {qraw[nt][s].x, qraw[nt][s].y, qraw[nt][s].z, qraw[nt][s].w};
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const float2 ph = bw[16 * g + 4 * s + jj];     // pair 16g + 4s + jj
+              const float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
+              w4[jj] = pack_bf16x2((x0 * ph.x - x1 * ph.y) * A.scale_log2, (x0 * ph.y + x1 * ph.x) * A.scale_log2);
+            }
+            qb[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
           }
-          ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        q_frame = fr;
+        q_set = true;
+        ++q_turns;
+      }
+
+      // ---- rotate the key rows: R(S - p + n) = R(S - p) R(n) ------------------
+      bf16x8 ka[4];
+      if (PE == LAZYATTN_PE_ROPE) {
+        float2* bw = bsh + (wave * 2 + (it & 1)) * 64;
+        bw[lane] = unit_phase_turns(inf.start - p, my_rev);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (KV8) {
+          // the lane's 32 codes are in k[0..1]
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t c_lo = (s < 2) ? (s == 0 ? k[0].x : k[0].z) : (s == 2 ? k[1].x : k[1].z);
+            const uint32_t c_hi = (s < 2) ? (s == 0 ? k[0].y : k[0].w) : (s == 2 ? k[1].y : k[1].w);
+            uint32_t w4[4];
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int i = 4 * s + jj;                    // pair 16g + i
+              w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[16 * g + i], rtab[i * 64 + lane]));
+            }
+            ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+          }
+        } else {
+  #pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            uint32_t w4[4] = {k[s].x, k[s].y, k[s].z, k[s].w};
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int i = 4 * s + jj;                    // pair 16g + i
+              w4[jj] = rotate_pair(w4[jj], cmul(bw[16 * g + i], rtab[i * 64 + lane]));
+            }
+            ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+          }
         }
       } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint32_t w4[4] = {k[s].x, k[s].y, k[s].z, k[s].w};
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int i = 4 * s + jj;                    // pair 16g + i
-            w4[jj] = rotate_pair(w4[jj], cmul(bw[16 * g + i], rt[i]));
-          }
-          ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) ka[s] = __builtin_bit_cast(bf16x8, k[s]);
+      }
+      if (inf.len < kBlock) {
+        // zero V rows past the entry's length (they may hold anything, even NaN)
+  #pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          uint32_t a = v[dt].x, b = v[dt].y;
+          const int k0 = 4 * g;
+          a = ((k0 + 0 < inf.len) ? (a & 0xffffu) : 0u) | ((k0 + 1 < inf.len) ? (a & 0xffff0000u) : 0u);
+          b = ((k0 + 2 < inf.len) ? (b & 0xffffu) : 0u) | ((k0 + 3 < inf.len) ? (b & 0xffff0000u) : 0u);
+          v[dt] = make_uint2(a, b);
         }
       }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ka[s] = __builtin_bit_cast(bf16x8, k[s]);
-    }
-    if (inf.len < kBlock) {
-      // zero V rows past the entry's length (they may hold anything, even NaN)
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        uint32_t a = v[dt].x, b = v[dt].y;
-        const int k0 = 4 * g;
-        a = ((k0 + 0 < inf.len) ? (a & 0xffffu) : 0u) | ((k0 + 1 < inf.len) ? (a & 0xffff0000u) : 0u);
-        b = ((k0 + 2 < inf.len) ? (b & 0xffffu) : 0u) | ((k0 + 3 < inf.len) ? (b & 0xffff0000u) : 0u);
-        v[dt] = make_uint2(a, b);
-      }
-    }
 
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      // scores relative to the reference: the chain starts from -m (FP8: the
-      // row's scale multiplies the product first)
-      f32x4 S = KV8 ? f32x4{0.f, 0.f, 0.f, 0.f} : negm[nt];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) S = mfma16x16x32(ka[s], qb[nt][s], S);
-      if (KV8) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[j] = fmaf(S[j], exp_scale(kexp, j), negm[nt][j]);
+  #pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        // scores relative to the reference: the chain starts from -m (FP8: the
+        // row's scale multiplies the product first)
+        f32x4 S = KV8 ? f32x4{0.f, 0.f, 0.f, 0.f} : negm[nt];
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) S = mfma16x16x32(ka[s], qb[nt][s], S);
+        if (KV8) {
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) S[j] = fmaf(S[j], exp_scale(kexp, j), negm[nt][j]);
+        }
+        float lm = kNegInf;
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int krow = 4 * g + j;
+          float x = S[j];
+          if (PE == LAZYATTN_PE_ALIBI) x -= slope[nt] * static_cast<float>(p - (inf.start + krow));
+          x = (krow < inf.len) ? x : kNegInf;
+          S[j] = x;
+          lm = fmaxf(lm, x);
+        }
+        // raise the reference only when a score outgrows it by 2^8 (exact:
+        // numerator and denominator share it); the test is one compare and a ballot
+        const bool want = (lm > kRescaleSlack) || (m_run[nt] == kNegInf && lm > kNegInf);
+        if (__builtin_amdgcn_ballot_w64(want)) {
+          float pm = fmaxf(lm, __shfl_xor(lm, 16));
+          pm = fmaxf(pm, __shfl_xor(pm, 32));
+          const bool raise = (pm > kRescaleSlack) || (m_run[nt] == kNegInf && pm > kNegInf);
+          const float m_new = raise ? m_use[nt] + pm : m_run[nt];
+          const float mu_new = (m_new == kNegInf) ? 0.f : m_new;
+          const float delta = mu_new - m_use[nt];
+          const float alpha = (m_new == m_run[nt]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+          S -= delta;
+  #pragma unroll
+          for (int dt = 0; dt < 8; ++dt) O[dt][nt] *= alpha;
+          l_run[nt] *= alpha;
+          m_run[nt] = m_new;
+          m_use[nt] = mu_new;
+          negm[nt] = f32x4{-mu_new, -mu_new, -mu_new, -mu_new};
+        }
+        float pe[4];
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) pe[j] = __builtin_amdgcn_exp2f(S[j]);
+        const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
+        // row sum of the bf16-rounded weights that enter P.V
+        l_run[nt] += (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23));
+        s16x4 pb = __builtin_bit_cast(s16x4, make_uint2(p01, p23));
+        if (KV8) {
+          // each token's value scale goes on its weight (tokens past the entry's
+          // length have weight 0 and codes zeroed above)
+          pb = __builtin_bit_cast(s16x4, make_uint2(pack_bf16x2(pe[0] * exp_scale(vexp, 0), pe[1] * exp_scale(vexp, 1)),
+                                                    pack_bf16x2(pe[2] * exp_scale(vexp, 2), pe[3] * exp_scale(vexp, 3))));
+        }
+  #pragma unroll
+        for (int dt = 0; dt < 8; ++dt) O[dt][nt] = mfma16x16x16(__builtin_bit_cast(s16x4, v[dt]), pb, O[dt][nt]);
       }
-      float lm = kNegInf;
+  };
+
+  int it = 0;
+  bool more = e < e_end;
+  while (more) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int krow = 4 * g + j;
-        float x = S[j];
-        if (PE == LAZYATTN_PE_ALIBI) x -= slope[nt] * static_cast<float>(p - (inf.start + krow));
-        x = (krow < inf.len) ? x : kNegInf;
-        S[j] = x;
-        lm = fmaxf(lm, x);
+    for (int sl = 0; sl < DEPTH; ++sl) {
+      if (more) {
+        const EntryInfo inf = curb[sl];
+        const int fr = frb[sl];
+        uint4 k[4] = {krb[sl][0], krb[sl][1], krb[sl][2], krb[sl][3]};
+        uint2 v[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) v[dt] = vrb[sl][dt];
+        const int e_ld = e + 4 * DEPTH;
+        if (e_ld < e_end) {
+          load_kv(nx.blk, krb[sl], vrb[sl]);
+          curb[sl] = nx;
+          frb[sl] = fr_nx;
+          if (e_ld + 4 < e_end) {
+            nx = entry_info(trow, e_ld + 4, ne, L);
+            if (PE == kPeFramed) fr_nx = frow[e_ld + 4];
+          }
+        }
+        process(inf, fr, k, v, it);
+        ++it;
+        e += 4;
+        more = e < e_end;
       }
-      // raise the reference only when a score outgrows it by 2^8 (exact:
-      // numerator and denominator share it); the test is one compare and a ballot
-      const bool want = (lm > kRescaleSlack) || (m_run[nt] == kNegInf && lm > kNegInf);
-      if (__builtin_amdgcn_ballot_w64(want)) {
-        float pm = fmaxf(lm, __shfl_xor(lm, 16));
-        pm = fmaxf(pm, __shfl_xor(pm, 32));
-        const bool raise = (pm > kRescaleSlack) || (m_run[nt] == kNegInf && pm > kNegInf);
-        const float m_new = raise ? m_use[nt] + pm : m_run[nt];
-        const float mu_new = (m_new == kNegInf) ? 0.f : m_new;
-        const float delta = mu_new - m_use[nt];
-        const float alpha = (m_new == m_run[nt]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-        S -= delta;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) O[dt][nt] *= alpha;
-        l_run[nt] *= alpha;
-        m_run[nt] = m_new;
-        m_use[nt] = mu_new;
-        negm[nt] = f32x4{-mu_new, -mu_new, -mu_new, -mu_new};
-      }
-      float pe[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pe[j] = __builtin_amdgcn_exp2f(S[j]);
-      const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
-      // row sum of the bf16-rounded weights that enter P.V
-      l_run[nt] += (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23));
-      s16x4 pb = __builtin_bit_cast(s16x4, make_uint2(p01, p23));
-      if (KV8) {
-        // each token's value scale goes on its weight (tokens past the entry's
-        // length have weight 0 and codes zeroed above)
-        pb = __builtin_bit_cast(s16x4, make_uint2(pack_bf16x2(pe[0] * exp_scale(vexp, 0), pe[1] * exp_scale(vexp, 1)),
-                                                  pack_bf16x2(pe[2] * exp_scale(vexp, 2), pe[3] * exp_scale(vexp, 3))));
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) O[dt][nt] = mfma16x16x16(__builtin_bit_cast(s16x4, v[dt]), pb, O[dt][nt]);
     }
-    e = e_next;
   }
 
   // ---- merge the four waves ------------------------------------------------------
@@ -1358,7 +1388,8 @@ static lazyattn_status check_batch(const lazyattn_batch* b) {
 constexpr size_t kDecodeLdsFloor = 56 * 1024;
 
 static size_t decode_lds_bytes(int nt, int group) {
-  const size_t need = (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(group) * kOS) * sizeof(float);
+  const size_t need = (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(group) * kOS + 16 * 64 * 2) *
+                      sizeof(float);
   return need > kDecodeLdsFloor ? need : kDecodeLdsFloor;
 }
 
