@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 #pragma unroll
         for (int k = 0; k < 8; ++k) kr[k] = rotate_pair(kr[k], ph);
       }
-      mask_v(ln);
+      if (ln < kBlock) mask_v(ln);
       stage_write(0);
       entry_of(wv1, 1, E_own, blk, st, ln);
       load_kv(blk);
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         if (PE == kPeFramed) kr[kk] = rotate_pair(kr[kk], ph);
         if (kk == 3) {
           if (KV8) convert_v8();
-          mask_v(nln);
+          if (nln < kBlock) mask_v(nln);
         }
       }
       stage_write((i + 1) & 1);
@@ -776,7 +776,13 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   const int e_begin = split * A.eps;
   const int e_end = min(ne, e_begin + A.eps);
 
-  // query fragments: lane (g, n) holds head column nt*16+n, channels 32g + 8s + 0..7,
+  // Channels of contraction step s held by lane (g, n): c0(s) .. c0(s) + 7 with
+  // c0(s) = 32s + 8g for bf16 pools (each of a lane's four 16-byte K loads then
+  // covers 64 contiguous bytes of every key row) and 32g + 8s for FP8 pools (a
+  // lane's 32 code bytes are contiguous).  Any such assignment works as long as
+  // q and K agree; the channel pair of word jj is c0(s) / 2 + jj.
+  auto c0 = [&](int s) { return KV8 ? 32 * g + 8 * s : 32 * s + 8 * g; };
+  // query fragments: lane (g, n) holds head column nt*16+n, channels c0(s) + 0..7,
   // scaled by scale*log2(e) and rounded to bf16
   // (framed pool: the raw fragments are kept, and qb is formed per frame)
   bf16x8 qb[NT][4];
@@ -791,7 +797,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 raw = make_uint4(0, 0, 0, 0);
-      if (ok) raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(r) * Hq + h) * kPD + 32 * g + 8 * s);
+      if (ok) raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(r) * Hq + h) * kPD + c0(s));
       qraw[nt][s] = raw;
       uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -808,7 +814,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + 256 * q, i = idx >> 6, l = idx & 63;
-      rtab[idx] = unit_phase(l & 15, A.rope.rev[16 * (l >> 4) + i]);
+      const int pair = KV8 ? 16 * (l >> 4) + i : 16 * (i >> 2) + 4 * (l >> 4) + (i & 3);   // c0(i / 4) / 2 + i % 4
+      rtab[idx] = unit_phase(l & 15, A.rope.rev[pair]);
     }
     __syncthreads();
   }
@@ -836,8 +843,9 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     negm[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // FP8 pool: lane (g, n) holds the 32 codes of key row n, channels 32g..32g+31
-  // (kr[0..1]), the codes of tokens 4g..4g+3 of channel rows 16dt+n (vr[dt].x)
+  // bf16 pool: lane (g, n) holds key row n, channels c0(s)..+7 (k[s]), and V
+  // channel rows 16dt+n, tokens 4g..4g+3 (v[dt]).  FP8 pool: lane (g, n) holds
+  // the 32 codes of key row n, channels 32g..32g+31 (k[0..1]), the codes of tokens 4g..4g+3 of channel rows 16dt+n (vr[dt].x)
   // and the exponents of key rows / tokens 4g..4g+3 (kr[2].x, kr[2].y)
   auto load_kv = [&](uint32_t blk, uint4 (&k)[4], uint2 (&v)[8]) {
     if (KV8) {
@@ -853,9 +861,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       for (int dt = 0; dt < 8; ++dt) v[dt].x = *reinterpret_cast<const uint32_t*>(vc + (16 * dt + n) * kBlock + 4 * g);
     } else {
       const uint16_t* kb = A.kpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kBlock * kPD);
-      const uint4* kp = reinterpret_cast<const uint4*>(kb + n * kPD + 32 * g);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) k[s] = kp[s];
+      for (int s = 0; s < 4; ++s) k[s] = *reinterpret_cast<const uint4*>(kb + n * kPD + c0(s));
       const uint16_t* vb = A.vpool + (static_cast<size_t>(blk) * Hkv + kvh) * (kPD * kBlock);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) v[dt] = *reinterpret_cast<const uint2*>(vb + (16 * dt + n) * kBlock + 4 * g);
@@ -863,20 +870,20 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   };
 
   // Entries are processed in the wave-uniform order e_begin + wave, + 4, ...;
-  // the table words make scalar loads.  While one entry is processed, the K/V
-  // of the next DEPTH are in flight (FP8: two; the bf16 registers allow one),
-  // and the words of the next entry to load are fetched an entry ahead of its
-  // K/V loads, so those loads never wait on them.
-  constexpr int DEPTH = KV8 ? 2 : 1;
-  uint4 krb[DEPTH][4];
-  uint2 vrb[DEPTH][8];
-  EntryInfo curb[DEPTH];
-  int frb[DEPTH];
+  // the table words make scalar loads.  Two ring slots hold the K/V of the
+  // entry being processed and of the next one (in flight); a slot is refilled
+  // with the entry after next as soon as its entry is done, so its loads have
+  // a whole entry's time to land and no registers are copied.  The words of
+  // the entry to load next are fetched one entry ahead of its K/V loads.
+  uint4 krb[2][4];
+  uint2 vrb[2][8];
+  EntryInfo curb[2];
+  int frb[2];
   EntryInfo nx{};
   int fr_nx = 0;
   int e = __builtin_amdgcn_readfirstlane(e_begin + wave);
 #pragma unroll
-  for (int sl = 0; sl < DEPTH; ++sl) {
+  for (int sl = 0; sl < 2; ++sl) {
     const int ee = e + 4 * sl;
     frb[sl] = 0;
     if (ee < e_end) {
@@ -885,12 +892,12 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       if (PE == kPeFramed) frb[sl] = frow[ee];
     }
   }
-  if (e + 4 * DEPTH < e_end) {
-    nx = entry_info(trow, e + 4 * DEPTH, ne, L);
-    if (PE == kPeFramed) fr_nx = frow[e + 4 * DEPTH];
+  if (e + 8 < e_end) {
+    nx = entry_info(trow, e + 8, ne, L);
+    if (PE == kPeFramed) fr_nx = frow[e + 8];
   }
 
-  // one entry: its K/V arrived in k, v
+  // one entry, its K/V in k and v (converted in place for FP8)
   auto process = [&](const EntryInfo inf, const int fr, uint4 (&k)[4], uint2 (&v)[8], const int it)
                      __attribute__((always_inline)) {
       const uint32_t kexp = k[2].x, vexp = k[2].y;
@@ -922,7 +929,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
             uint32_t w4[4] = {qraw[nt][s].x, qraw[nt][s].y, qraw[nt][s].z, qraw[nt][s].w};
   #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-              const float2 ph = bw[16 * g + 4 * s + jj];     // pair 16g + 4s + jj
+              const float2 ph = bw[c0(s) / 2 + jj];
               const float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
               w4[jj] = pack_bf16x2((x0 * ph.x - x1 * ph.y) * A.scale_log2, (x0 * ph.y + x1 * ph.x) * A.scale_log2);
             }
@@ -951,7 +958,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const int i = 4 * s + jj;                    // pair 16g + i
-              w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[16 * g + i], rtab[i * 64 + lane]));
+              w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[c0(s) / 2 + jj], rtab[i * 64 + lane]));
             }
             ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
           }
@@ -962,7 +969,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const int i = 4 * s + jj;                    // pair 16g + i
-              w4[jj] = rotate_pair(w4[jj], cmul(bw[16 * g + i], rtab[i * 64 + lane]));
+              w4[jj] = rotate_pair(w4[jj], cmul(bw[c0(s) / 2 + jj], rtab[i * 64 + lane]));
             }
             ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
           }
@@ -1045,15 +1052,10 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   bool more = e < e_end;
   while (more) {
 #pragma unroll
-    for (int sl = 0; sl < DEPTH; ++sl) {
+    for (int sl = 0; sl < 2; ++sl) {
       if (more) {
-        const EntryInfo inf = curb[sl];
-        const int fr = frb[sl];
-        uint4 k[4] = {krb[sl][0], krb[sl][1], krb[sl][2], krb[sl][3]};
-        uint2 v[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) v[dt] = vrb[sl][dt];
-        const int e_ld = e + 4 * DEPTH;
+        process(curb[sl], frb[sl], krb[sl], vrb[sl], it);
+        const int e_ld = e + 8;
         if (e_ld < e_end) {
           load_kv(nx.blk, krb[sl], vrb[sl]);
           curb[sl] = nx;
@@ -1063,7 +1065,6 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
             if (PE == kPeFramed) fr_nx = frow[e_ld + 4];
           }
         }
-        process(inf, fr, k, v, it);
         ++it;
         e += 4;
         more = e < e_end;
