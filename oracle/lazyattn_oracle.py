@@ -743,9 +743,15 @@ def fp8_empty_pools(num_blocks: int, num_kv_heads: int):
     return np.full(shape, 0xFF, dtype=np.uint8), np.full(shape, 0xFF, dtype=np.uint8)
 
 
-def append_kv_fp8(k_chunks, v_chunks, k_new, v_new, slots, dtype: str, block_size: int = 16):
-    """Quantise new tokens' K/V [n][Hkv][D] (in ``dtype``) row by row into pool slots, in place."""
-    k = to_f64(k_new, dtype).astype(np.float32)
+def append_kv_fp8(k_chunks, v_chunks, k_new, v_new, slots, dtype: str, block_size: int = 16,
+                  frame_index=None, inv_freq=None):
+    """Quantise new tokens' K/V [n][Hkv][D] (in ``dtype``) row by row into pool slots, in place.
+    With ``frame_index`` the keys are first turned into their document-local frames (section 6b),
+    exactly, then rounded to float32 and quantised."""
+    k = to_f64(k_new, dtype)
+    if frame_index is not None:
+        k = rotate_into_frames(k, frame_index, inv_freq)
+    k = k.astype(np.float32)
     v = to_f64(v_new, dtype).astype(np.float32)
     kc, ke = quantize_fp8_rows(k)
     vc, ve = quantize_fp8_rows(v)

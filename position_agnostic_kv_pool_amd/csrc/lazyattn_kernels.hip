@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   // the rotation's rounding.
   auto key_fp8 = [&](int k, float2 ph) -> uint32_t {
     const float sc = exp_scale(k < 4 ? kx.x : kx.y, k & 3);
-    if (PE == LAZYATTN_PE_ROPE) {
+    if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) {
       const float2 x = fp8x2_to_f32(kr[k], false);
       const float x0 = x.x * sc, x1 = x.y * sc;
       return pack_bf16x2(x0 * ph.x - x1 * ph.y, x0 * ph.y + x1 * ph.x);
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
           kr[k] = KV8 ? key_fp8(k, ph) : rotate_pair(kr[k], ph);
           ph = cmul(ph, r1);
         }
-      } else if (KV8) {
+      } else if (KV8 && PE != kPeFramed) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) kr[k] = key_fp8(k, make_float2(1.f, 0.f));
       }
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         // every row of the entry turns by the same R(F - p0)
         const float2 ph = unit_phase_turns(__builtin_amdgcn_readlane(fv0, E_own) - p0, A.rope.rev[lane]);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) kr[k] = rotate_pair(kr[k], ph);
+        for (int k = 0; k < 8; ++k) kr[k] = KV8 ? key_fp8(k, ph) : rotate_pair(kr[k], ph);
       }
       if (ln < kBlock) mask_v(ln);
       stage_write(0);
@@ -504,9 +504,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
           kr[kk] = KV8 ? key_fp8(kk, ph) : rotate_pair(kr[kk], ph);
           ph = cmul(ph, r1);
         } else if (KV8) {
-          kr[kk] = key_fp8(kk, ph);
+          kr[kk] = key_fp8(kk, ph);                 // framed: turned by ph; else converted
+        } else if (PE == kPeFramed) {
+          kr[kk] = rotate_pair(kr[kk], ph);
         }
-        if (PE == kPeFramed) kr[kk] = rotate_pair(kr[kk], ph);
         if (kk == 3) {
           if (KV8) convert_v8();
           if (nln < kBlock) mask_v(nln);
@@ -1317,9 +1318,12 @@ __device__ __forceinline__ float wave_max64(float x) {
   return x;
 }
 
-// One wave per (token, KV head); lane l holds channels 2l, 2l+1.
+// One wave per (token, KV head); lane l holds channels 2l, 2l+1.  With
+// frame_index (a pool in document-local frames) the key is first turned by
+// R(frame_index[i]) in float, then quantised.
 __global__ __launch_bounds__(64) void append_kv_fp8_kernel(uint8_t* kpool, uint8_t* vpool, const uint16_t* knew,
-                                                           const uint16_t* vnew, const int64_t* slots, int Hkv) {
+                                                           const uint16_t* vnew, const int64_t* slots,
+                                                           const int32_t* frame_index, int Hkv, const RopeRev rope) {
   const int i = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
   const int64_t slot = slots[i];
   const int64_t blk = slot / kBlock;
@@ -1327,7 +1331,13 @@ __global__ __launch_bounds__(64) void append_kv_fp8_kernel(uint8_t* kpool, uint8
   const size_t src = (static_cast<size_t>(i) * Hkv + h) * kPD;
   const uint32_t kw = reinterpret_cast<const uint32_t*>(knew + src)[l];
   const uint32_t vw = reinterpret_cast<const uint32_t*>(vnew + src)[l];
-  const float k0 = bf_lo(kw), k1 = bf_hi(kw);
+  float k0 = bf_lo(kw), k1 = bf_hi(kw);
+  if (frame_index) {
+    const float2 ph = unit_phase(frame_index[i], rope.rev[l]);
+    const float y0 = k0 * ph.x - k1 * ph.y, y1 = k0 * ph.y + k1 * ph.x;
+    k0 = y0;
+    k1 = y1;
+  }
   const float v0 = bf_lo(vw), v1 = bf_hi(vw);
   const int ek = fp8_row_exponent(wave_max64(fmaxf(fabsf(k0), fabsf(k1))));
   const int ev = fp8_row_exponent(wave_max64(fmaxf(fabsf(v0), fabsf(v1))));
@@ -1425,7 +1435,6 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   const bool framed = batch->frame_starts != nullptr;
   const bool fp8 = cfg->kv_format == LAZYATTN_KV_FP8_E4M3;
   if (framed && (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE)) return LAZYATTN_EUNSUPPORTED;
-  if (framed && fp8) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32) {
     if (max_q_len > 0x7fffffff || R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), cu_q_lens, static_cast<const float*>(k_pool),
@@ -1454,7 +1463,8 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(gz));
   const dim3 block(kPrefillThreads);
   if (fp8) {
-    switch (cfg->pe) {
+    switch (framed ? kPeFramed : cfg->pe) {
+      case kPeFramed: hipLaunchKernelGGL((prefill_bf16_kernel<kPeFramed, 1>), grid, block, 0, stream, a); break;
       case LAZYATTN_PE_ROPE: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_ROPE, 1>), grid, block, 0, stream, a); break;
       case LAZYATTN_PE_NONE: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_NONE, 1>), grid, block, 0, stream, a); break;
       default: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_ALIBI, 1>), grid, block, 0, stream, a); break;
@@ -1515,7 +1525,6 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
 
   const bool framed = batch->frame_starts != nullptr;
   if (framed && (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE)) return LAZYATTN_EUNSUPPORTED;
-  if (framed && cfg->kv_format != LAZYATTN_KV_PLAIN) return LAZYATTN_EUNSUPPORTED;
   if (cfg->dtype == LAZYATTN_F32) {
     if (R > 65535 || Hq > 65535) return LAZYATTN_EUNSUPPORTED;
     NaiveArgs a{static_cast<const float*>(q), nullptr, static_cast<const float*>(k_pool),
@@ -1623,7 +1632,7 @@ lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, voi
   if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3) {
     hipLaunchKernelGGL(append_kv_fp8_kernel, grid, dim3(64), 0, stream, static_cast<uint8_t*>(k_pool),
                        static_cast<uint8_t*>(v_pool), static_cast<const uint16_t*>(k_new),
-                       static_cast<const uint16_t*>(v_new), slots, cfg->num_kv_heads);
+                       static_cast<const uint16_t*>(v_new), slots, nullptr, cfg->num_kv_heads, make_rope_rev(cfg));
   } else if (cfg->dtype == LAZYATTN_BF16) {
     hipLaunchKernelGGL(append_kv_kernel<uint16_t>, grid, dim3(128), 0, stream, static_cast<uint16_t*>(k_pool),
                        static_cast<uint16_t*>(v_pool), static_cast<const uint16_t*>(k_new),
@@ -1642,11 +1651,17 @@ lazyattn_status lazyattn_append_kv_framed(const lazyattn_config* cfg, void* k_po
   lazyattn_status st = check_config(cfg);
   if (st != LAZYATTN_OK) return st;
   if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE) return LAZYATTN_EUNSUPPORTED;
-  if (cfg->kv_format != LAZYATTN_KV_PLAIN) return LAZYATTN_EUNSUPPORTED;
   if (n < 0 || num_blocks < 0) return LAZYATTN_EINVAL;
   if (n == 0) return LAZYATTN_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slots || !frame_index || num_blocks < 1) return LAZYATTN_EINVAL;
   if (cfg->num_kv_heads > 65535) return LAZYATTN_EUNSUPPORTED;
+  if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3) {
+    hipLaunchKernelGGL(append_kv_fp8_kernel, dim3(n, cfg->num_kv_heads), dim3(64), 0, stream,
+                       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool),
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slots, frame_index,
+                       cfg->num_kv_heads, make_rope_rev(cfg));
+    return launched();
+  }
   hipLaunchKernelGGL(append_kv_framed_kernel, dim3(n, cfg->num_kv_heads), dim3(64), 0, stream,
                      static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool),
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), slots, frame_index,

@@ -128,20 +128,25 @@ def gpu_f64(t) -> np.ndarray:
 
 class OracleFp8State:
     """The oracle's own FP8 pools for a workload: every referenced document quantised by the
-    oracle, grown by its own quantising appends; attention over the dequantised values."""
+    oracle, grown by its own quantising appends; attention over the dequantised values.
+    ``framed``: keys in document-local frames (attention through the framed definition)."""
 
-    def __init__(self, wl):
+    def __init__(self, wl, framed=False):
         self.wl = wl
+        self.framed = framed
         s = wl.spec
+        self.inv_freq = O.rope_inv_freq(s.head_dim, s.rope_theta)
         self.kc, self.vc = O.fp8_empty_pools(wl.num_blocks, s.num_kv_heads)
         for d in wl.referenced_docs:
             k, v = wl.doc_kv(int(d))
-            slots, _ = wl.doc_frame_tokens(int(d))
-            O.append_kv_fp8(self.kc, self.vc, k, v, slots, s.dtype)
+            slots, j = wl.doc_frame_tokens(int(d))
+            O.append_kv_fp8(self.kc, self.vc, k, v, slots, s.dtype, frame_index=j if framed else None,
+                            inv_freq=self.inv_freq)
 
     def append(self, inputs):
         if inputs is not None:
-            O.append_kv_fp8(self.kc, self.vc, inputs["k_new"], inputs["v_new"], inputs["slots"], self.wl.spec.dtype)
+            O.append_kv_fp8(self.kc, self.vc, inputs["k_new"], inputs["v_new"], inputs["slots"], self.wl.spec.dtype,
+                            frame_index=inputs["frame_index"] if self.framed else None, inv_freq=self.inv_freq)
 
     def _common(self, inputs):
         s = self.wl.spec
@@ -152,8 +157,20 @@ class OracleFp8State:
                     rope_theta=s.rope_theta)
 
     def prefill(self, inputs, token_subset=None, requests=None, pe=None):
+        if self.framed:
+            c = self._common(inputs)
+            for key in ("num_kv_heads", "pool_dtype"):
+                c.pop(key)
+            c["dtype"] = self.wl.spec.dtype
+            return O.prefill_framed(q=inputs["q"], cu_q_lens=inputs["cu_q_lens"], frame_starts=inputs["frame_starts"],
+                                    token_subset=token_subset, requests=requests, **c)
         return O.prefill(q=inputs["q"], cu_q_lens=inputs["cu_q_lens"], pe=pe or self.wl.spec.pe,
                          token_subset=token_subset, requests=requests, **self._common(inputs))
 
     def decode(self, inputs, requests=None, pe=None):
+        if self.framed:
+            c = self._common(inputs)
+            for key in ("num_kv_heads", "pool_dtype"):
+                c.pop(key)
+            return O.decode_framed(q=inputs["q"], frame_starts=inputs["frame_starts"], requests=requests, **c)
         return O.decode(q=inputs["q"], pe=pe or self.wl.spec.pe, requests=requests, **self._common(inputs))

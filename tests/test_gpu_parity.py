@@ -712,6 +712,82 @@ def test_fp8_prefill_mqa_sampled():
     say(f"FP8 MQA prefill: max {mx:.2e} mean {mn:.2e}")
 
 
+def test_fp8_edge_single_token_contexts_and_zero_rows():
+    say("FP8 edge: requests without documents (one-token contexts), then all-zero K/V rows")
+    wl = W.build_workload(W.spec(2, requests=[3], docs=(0, 0), q_len=1, n_decode=2))
+    s = wl.spec
+    cfg = staging.config_for(s, kv_format="fp8")
+    pools = staging.WrittenPools(wl, cfg, DEV)
+    orc = OracleFp8State(wl)
+    pb = wl.prefill_batch()
+    # token 1 of the batch: K and V rows all zero (exponent 0, every code +0)
+    pb = dict(pb, k_new=pb["k_new"].copy(), v_new=pb["v_new"].copy())
+    pb["k_new"][1] = 0
+    pb["v_new"][1] = 0
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    orc.append(pb)
+    got = gpu_f64(staging.PrefillCall(cfg, s, pb, DEV).run(pools))
+    ref = orc.prefill(pb)
+    cu = pb["cu_q_lens"]
+    assert_parity(np.concatenate([got[cu[r]:cu[r + 1]] for r in ref]), np.concatenate([ref[r] for r in ref]),
+                  "bf16", "FP8 one-token contexts")
+    np.testing.assert_array_equal(got[1], 0.0)      # the zero token attends only to itself
+    for step in range(2):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+    out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+    ref = orc.decode(d)
+    mx, mn = assert_parity(out, np.stack([ref[r] for r in range(len(ref))]), "bf16", "FP8 decode after zero rows")
+    say(f"FP8 edge decode: max {mx:.2e} mean {mn:.2e}")
+
+
+def test_fp8_framed_pool_append_prefill_and_decode():
+    say("FP8 pool in document-local frames: append (vs exact rotation), 8B prefill and decode")
+    wl = W.build_workload(W.spec(3, requests=[6], n_decode=3))
+    s = wl.spec
+    cfg = staging.config_for(s, kv_format="fp8")
+    pools = staging.FramedPools(wl, cfg, DEV)
+    sync()
+    # appended chunks: every value within half a code step (or half a subnormal step) of the
+    # exact R(j) k, and almost every code equal to the oracle's (float rounding of the rotation
+    # may move a value across a rounding boundary)
+    orc = OracleFp8State(wl, framed=True)
+    d0 = int(wl.referenced_docs[0])
+    k, _ = wl.doc_kv(d0)
+    slots, j = wl.doc_frame_tokens(d0)
+    exact = O.rotate_into_frames(O.bf16_to_f64(k), j, O.rope_inv_freq(s.head_dim, s.rope_theta))
+    blocks = np.unique(slots // 16)
+    got = O.Fp8PoolView(pools.k[torch.from_numpy(blocks).to(DEV)].cpu().numpy(), "k")[np.arange(blocks.size)]
+    pos = {int(b): i for i, b in enumerate(blocks)}
+    g = np.stack([got[pos[int(sl // 16)], :, int(sl % 16), :] for sl in slots])
+    _, exps = O.quantize_fp8_rows(exact.astype(np.float32))
+    bound = np.maximum(2.0 ** -4 * np.abs(exact), np.ldexp(1.0, exps.astype(np.int32) - 10)[..., None]) * (1 + 1e-5)
+    assert np.all(np.abs(g - exact) <= bound + 1e-30)
+    gb = pools.k[torch.from_numpy(blocks).to(DEV)].cpu().numpy()
+    same = float(np.mean(gb == orc.kc[blocks]))
+    say(f"framed FP8 append: {same:.5f} of the K chunk bytes equal the oracle's")
+    assert same >= 0.99
+    # prefill and decode against the oracle over its own framed FP8 pool
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    orc.append(pb)
+    got = gpu_f64(staging.PrefillCall(cfg, s, pb, DEV, framed=True).run(pools))
+    ref = orc.prefill(pb)
+    cu = pb["cu_q_lens"]
+    mx, mn = assert_parity(np.concatenate([got[cu[r]:cu[r + 1]] for r in ref]), np.concatenate([ref[r] for r in ref]),
+                           "bf16", "framed FP8 prefill")
+    say(f"framed FP8 prefill: max {mx:.2e} mean {mn:.2e}")
+    for step in range(3):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+    out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, framed=True).run(pools))
+    ref = orc.decode(d)
+    mx, mn = assert_parity(out, np.stack([ref[r] for r in range(len(ref))]), "bf16", "framed FP8 decode")
+    say(f"framed FP8 decode step 2: max {mx:.2e} mean {mn:.2e}")
+
+
 def test_fp8_decode_llama8b():
     say("FP8 decode: 8B, 16 requests, steps 0 and 16 (RoPE), step 16 rotation-free and ALiBi")
     wl = W.build_workload(W.spec(3, requests=[16], n_decode=17))
