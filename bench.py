@@ -241,12 +241,14 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = Tru
     # the same steps over an FP8 pool (quantised by the library's append)
     cfg8 = staging.config_for(s, kv_format="fp8")
     pools8 = staging.WrittenPools(wl, cfg8, "cuda") if framed else None
+    fpools8 = staging.FramedPools(wl, cfg8, "cuda") if framed else None
     if framed:
         staging.append_tokens(cfg8, pools8, wl.tokens_before_step(0), s.dtype, "cuda")
+        staging.append_tokens(cfg8, fpools8, wl.tokens_before_step(0), s.dtype, "cuda")
     t = torch
     tot_ms, tot_merge_ms, tot_ms_none, tot_bytes, tot_unique, tokens = 0.0, 0.0, 0.0, 0, 0, 0
     tot_kv = 0
-    tot_ms_framed, tot_ms_fp8 = 0.0, 0.0
+    tot_ms_framed, tot_ms_fp8, tot_ms_fp8f = 0.0, 0.0, 0.0
     for step in range(-2, n_steps):          # two untimed warm-up launches on step 0's inputs
         d = wl.decode_step(max(step, 0))
         if step >= 0:
@@ -254,18 +256,21 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = Tru
             if framed:
                 staging.append_tokens(cfg, fpools, d, s.dtype, "cuda")
                 staging.append_tokens(cfg8, pools8, d, s.dtype, "cuda")
+                staging.append_tokens(cfg8, fpools8, d, s.dtype, "cuda")
         call = staging.DecodeCall(cfg, s, d, "cuda")
         call_none = staging.DecodeCall(cfg_none, s, d, "cuda")
         timer = Timer(t)
         ms_att = timer.span(lambda: call.attend(pools), 3)
         ms_step = timer.span(lambda: call.run(pools), 3)
         ms_none = timer.span(lambda: call_none.attend(pools), 3)
-        ms_framed, ms_fp8 = 0.0, 0.0
+        ms_framed, ms_fp8, ms_fp8f = 0.0, 0.0, 0.0
         if framed:
             call_framed = staging.DecodeCall(cfg, s, d, "cuda", framed=True)
             ms_framed = timer.span(lambda: call_framed.attend(fpools), 3)
             call8 = staging.DecodeCall(cfg8, s, d, "cuda")
             ms_fp8 = timer.span(lambda: call8.attend(pools8), 3)
+            call8f = staging.DecodeCall(cfg8, s, d, "cuda", framed=True)
+            ms_fp8f = timer.span(lambda: call8f.attend(fpools8), 3)
         if step < 0:
             continue
         tot_ms += ms_att
@@ -273,6 +278,7 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = Tru
         tot_ms_none += ms_none
         tot_ms_framed += ms_framed
         tot_ms_fp8 += ms_fp8
+        tot_ms_fp8f += ms_fp8f
         by = decode_bytes(d, wl)
         tot_bytes += by["logical"]
         tot_kv += by["kv_logical"]
@@ -280,7 +286,7 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = Tru
         tokens += len(d["ctx_lens"])
     n = max(n_steps, 1)
     return dict(ms=tot_ms / n, merge_ms=tot_merge_ms / n, ms_none=tot_ms_none / n, ms_framed=tot_ms_framed / n,
-                ms_fp8=tot_ms_fp8 / n, bytes=tot_bytes / n, kv_bytes=tot_kv / n,
+                ms_fp8=tot_ms_fp8 / n, ms_fp8f=tot_ms_fp8f / n, bytes=tot_bytes / n, kv_bytes=tot_kv / n,
                 unique=tot_unique / n,
                 tokens=tokens, splits=_abi.decode_splits(cfg, len(wl.requests), wl.table_arrays(wl.requests)[0].shape[1]))
 
@@ -477,7 +483,8 @@ def main() -> int:
             "attention_kernel_us": round(dec["ms_fp8"] * 1e3, 2),
             "bytes_per_launch_logical": round(fp8_bytes),
             "GBps": round(fp8_bytes / (dec["ms_fp8"] * 1e-3) / 1e9, 1),
-            "speedup_vs_bf16_pool": round(dec["ms"] / dec["ms_fp8"], 3)}
+            "speedup_vs_bf16_pool": round(dec["ms"] / dec["ms_fp8"], 3),
+            "framed_attention_kernel_us": round(dec["ms_fp8f"] * 1e3, 2)}
         out["document_frames"]["decode_attention_us"] = round(dec["ms_framed"] * 1e3, 2)
         out["document_frames"]["decode_overhead_vs_norotation"] = round(dec["ms_framed"] / dec["ms_none"] - 1.0, 4)
         print(f"# decode done: {dec['ms'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
