@@ -508,11 +508,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         } else if (PE == kPeFramed) {
           kr[kk] = rotate_pair(kr[kk], ph);
         }
-        if (kk == 3) {
-          if (KV8) convert_v8();
-          if (nln < kBlock) mask_v(nln);
-        }
+        if (kk == 3 && KV8) convert_v8();
+        // keep this row's rotation between this k-step's products (the compiler
+        // would otherwise sink it to the LDS write after the loop)
+        asm volatile("" : "+v"(kr[kk]));
       }
+      if (nln < kBlock) mask_v(nln);
       stage_write((i + 1) & 1);
       // loads of tile i + 2, words of tile i + 3
       int lblk, lst, lln;
