@@ -135,8 +135,9 @@ __device__ __forceinline__ f32x4 mfma16x16x16(const s16x4& a, const s16x4& b, co
 //   S^T (keys x rows) = K~ (keys x D) . Q~^T       16  32x32x16 MFMA
 //   P = 2^(S - m), rounded to bf16                 (base 2, scale folded into Q~)
 //   O^T (D x rows)   += V^T (D x keys) . P^T       16  32x32x16 MFMA
-// plus 4 MFMAs of a ones matrix by P^T, whose every row is the sum of exactly
-// the bf16 weights that enter P.V (the softmax denominator).
+// The softmax denominator sums exactly the bf16 weights that enter P.V: each
+// lane accumulates its 8-key slices with v_dot2_f32_bf16 against ones, and the
+// two key halves (lanes c, c + 32) are added at the end.
 //
 // Key order.  Within a 32-key half (tau) of the tile, S^T row i holds the key
 // that `krow_of` maps to it, chosen so that the accumulator leaves each lane,
@@ -423,10 +424,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       qf[8 * nt + kk] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
     }
 
-  f32x16 O[4][NT], O1[NT];
+  f32x16 O[4][NT];
+  float lsum[NT];                                    // this lane's part of the row sum (keys 8h..8h+7)
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   float m_ref[NT] = {0.f};                           // reference per row (raw score units)
   f32x16 negm[NT];
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   // One pass over the key tiles.  maxpass: scores only, folded into the exact
   // row maximum mx[].  Otherwise P.V with the reference m_ref (taken from the
@@ -610,7 +613,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
               for (int nt = 0; nt < NT; ++nt) O[dt][nt] = mfma32x32x16(av[n % 3], Pk[nt], O[dt][nt]);
             }
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) O1[nt] = mfma32x32x16(ones, Pk[nt], O1[nt]);
+            for (int nt = 0; nt < NT; ++nt) {
+              const uint4 pw = __builtin_bit_cast(uint4, Pk[nt]);
+              lsum[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.x), ones2, lsum[nt], false);
+              lsum[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.y), ones2, lsum[nt], false);
+              lsum[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.z), ones2, lsum[nt], false);
+              lsum[nt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.w), ones2, lsum[nt], false);
+            }
           }
       }
       wv0 = wv1;
@@ -627,7 +636,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) O[dt][nt] = f32x16{};
-      O1[nt] = f32x16{};
+      lsum[nt] = 0.f;
       negm[nt] = f32x16{};
     }
   };
@@ -639,7 +648,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     // redo the work-group with the exact maximum
     bool bad = false;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bad = bad || (row_ok[nt] && !(O1[nt][0] < kSumLimit));
+    for (int nt = 0; nt < NT; ++nt) {
+      const float lt = lsum[nt] + __shfl_xor(lsum[nt], 32);
+      bad = bad || (row_ok[nt] && !(lt < kSumLimit));
+    }
     if (tid == 0) redo_s = 0;
     __syncthreads();
     if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) redo_s = 1;
@@ -660,11 +672,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   }
 
   // ---- epilogue ----------------------------------------------------------------
-  // every row of the ones tile holds the row sum; O register r: channel
-  // 32 dt + 8 (r / 4) + 4 h + r % 4
+  // row sum = this lane's half + the other key half's (lane c + 32); O register
+  // r: channel 32 dt + 8 (r / 4) + 4 h + r % 4
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float lt = O1[nt][0];
+    const float lt = lsum[nt] + __shfl_xor(lsum[nt], 32);
     if (!row_ok[nt]) continue;
     const size_t rowoff = static_cast<size_t>(tok[nt]) * Hq + head[nt];
     if (A.splits == 1) {
