@@ -31,10 +31,13 @@
  *    this interface.
  *
  * Data layout (B = block_size = 16, D = head_dim, Hkv = KV heads, Hq = query
- * heads, G = Hq / Hkv; element type = config dtype):
+ * heads, G = Hq / Hkv; element type = config dtype for the plain pool format):
  *  - K pool  [num_blocks][Hkv][B][D]   one block = B token rows of D channels
  *  - V pool  [num_blocks][Hkv][D][B]   one block = D channel rows of B tokens
- *    Both hold content only: keys are never rotated in storage.
+ *    By default both hold content only: keys are never rotated in storage.
+ *    Two variants are selected per call: keys in document-local frames
+ *    (lazyattn_batch.frame_starts, "Key frames" below) and an FP8 chunk
+ *    format (lazyattn_config.kv_format, "Pool formats" below).
  *  - Table word (uint64): bits 63..32 logical start, bits 31..0 block id.
  *    A request's words are ordered by logical start; the context is dense:
  *    entry e covers logical positions [start_e, start_{e+1}) (the last one
@@ -42,8 +45,8 @@
  *    the entry's length are padding and are never read into a result.
  *  - Query head h reads KV head h / G.
  *  - RoPE pairs are interleaved channels (2i, 2i+1), frequency
- *    theta^(-2i/D); a query at position p and a key at t score
- *    scale * q^T R(t - p) k.
+ *    theta^(-2i/D) or the caller's table (lazyattn_config.rope_inv_freq); a
+ *    query at position p and a key at t score scale * q^T R(t - p) k.
  */
 #ifndef LAZYATTN_H
 #define LAZYATTN_H
@@ -128,7 +131,8 @@ typedef struct {
  * kernels need one rotation R(F - p) per (query, frame) instead of one per key
  * (gist.science, Technical Implementation > Decoding: the query is rotated
  * only when the offset changes; > Prefilling: one relative rotation per key
- * tile).  pe ROPE, bf16 only. */
+ * tile).  pe ROPE and dtype bf16 (plain or FP8 pool); other configs return
+ * LAZYATTN_EUNSUPPORTED when frame_starts is set. */
 typedef struct {
   int32_t num_reqs;                /* R >= 0 */
   int32_t max_entries;             /* row stride of block_tables, >= every num_entries[r] */
@@ -267,8 +271,10 @@ lazyattn_status lazyattn_merge_splits(const lazyattn_config* cfg, int32_t num_ro
 
 /* Write n new tokens' content-only K/V into the pool (gist.science,
  * Methodology: the cache stores content-based keys and values, no rotation).
- *  k_new, v_new device [n][Hkv][D]; slots device [n] int64 = block*B + row,
- *  every slot < num_blocks*B (not checked on the device). */
+ *  k_new, v_new device [n][Hkv][D] in cfg->dtype; slots device [n] int64 =
+ *  block*B + row, every slot < num_blocks*B (not checked on the device).
+ *  FP8 pool format: k_new/v_new are bf16 and each row is quantised as
+ *  "Pool formats" describes (the row's exponent is written with it). */
 lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, void* v_pool,
                                    int64_t num_blocks, const void* k_new, const void* v_new,
                                    const int64_t* slots, int32_t n, hipStream_t stream);
@@ -281,7 +287,8 @@ lazyattn_status lazyattn_append_kv(const lazyattn_config* cfg, void* k_pool, voi
  * calls build that copy so its cost can be measured next to the deferred
  * kernels: materialise the KV, rotate the queries, then run lazyattn_prefill
  * with pe = NONE on the copy (same result up to rounding, since
- * R(p)^T R(t) = R(t - p)).  bf16, D = 128, pe ROPE only. */
+ * R(p)^T R(t) = R(t - p)).  bf16, D = 128, pe ROPE, plain content-only pools
+ * only (frame_starts set or an FP8 format: LAZYATTN_EUNSUPPORTED). */
 
 /* Copy every entry of every request from the shared pool into the private
  * block that dst_tables names at the same (request, entry), K rows rotated by
@@ -306,7 +313,8 @@ lazyattn_status lazyattn_rotate_queries(const lazyattn_config* cfg, const void* 
 /* lazyattn_append_kv for a pool in document-local frames: token i's key is
  * stored as R(frame_index[i]) k_new[i] (frame_index = its logical position
  * minus its frame's start), its value unchanged.  frame_index device [n]
- * int32.  pe ROPE, bf16 only. */
+ * int32.  pe ROPE, bf16 only; with the FP8 pool format the key is turned in
+ * float and then quantised. */
 lazyattn_status lazyattn_append_kv_framed(const lazyattn_config* cfg, void* k_pool, void* v_pool,
                                           int64_t num_blocks, const void* k_new, const void* v_new,
                                           const int64_t* slots, const int32_t* frame_index, int32_t n,
