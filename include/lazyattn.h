@@ -196,10 +196,11 @@ int32_t lazyattn_decode_splits(const lazyattn_config* cfg, int32_t num_reqs, int
 
 /* Workspace bytes for a prefill/decode call with these sizes (num_splits as
  * passed to the call; 0 => the heuristic).  0 means no workspace needed.
- * A call that splits the key range into S > 1 parts writes fp32 partial
- * results to the workspace: o [S][rows][Hq][D] then (m, l) [S][rows][Hq][2]
- * (rows = total_q for prefill, num_reqs for decode); the merge kernel then
- * combines them.  The workspace needs no initialisation; calls that may run
+ * A call that splits the key range into S > 1 parts writes partial results
+ * to the workspace: each part's output already divided by its own softmax
+ * sum, as IEEE half, o [S][rows][Hq][D], then its reference and sum (m, l)
+ * as fp32 [S][rows][Hq][2] (rows = total_q for prefill, num_reqs for
+ * decode), S*rows*Hq*(2D + 8) bytes; the merge kernel then combines them.  The workspace needs no initialisation; calls that may run
  * concurrently must not share one. */
 size_t lazyattn_prefill_workspace_size(const lazyattn_config* cfg, int32_t num_reqs, int32_t total_q,
                                        int32_t max_q_len, int32_t max_entries, int32_t num_splits);
@@ -261,10 +262,11 @@ lazyattn_status lazyattn_decode_attend(const lazyattn_config* cfg, const void* q
                                        size_t workspace_bytes, hipStream_t stream);
 
 /* Log-sum-exp merge of S split partials into out [num_rows][Hq][D] (bf16):
- * out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, summed in
- * split order.  num_rows = total_q (prefill) or num_reqs (decode); workspace as
- * written by the matching *_attend call with S = num_splits.  num_splits 1 is a
- * no-op.  EWORKSPACE if workspace_bytes is short of S*num_rows*Hq*(D+2)*4. */
+ * with w_s = 2^(m_s - M) l_s and M = max_s m_s, out = sum_s w_s o_s / sum_s w_s
+ * (o_s already divided by l_s), summed in split order.  num_rows = total_q
+ * (prefill) or num_reqs (decode); workspace as written by the matching
+ * *_attend call with S = num_splits.  num_splits 1 is a no-op.  EWORKSPACE if
+ * workspace_bytes is short of S*num_rows*Hq*(2D+8). */
 lazyattn_status lazyattn_merge_splits(const lazyattn_config* cfg, int32_t num_rows, int32_t num_splits,
                                       const void* workspace, size_t workspace_bytes, void* out,
                                       hipStream_t stream);

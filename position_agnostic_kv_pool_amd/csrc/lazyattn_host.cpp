@@ -217,7 +217,7 @@ size_t lazyattn_prefill_workspace_size(const lazyattn_config* cfg, int32_t num_r
   int s = num_splits > 0 ? num_splits : choose_prefill_splits(cfg, num_reqs, max_q_len, max_entries);
   if (s <= 1) return 0;
   const size_t rows = static_cast<size_t>(total_q) * cfg->num_q_heads;
-  return static_cast<size_t>(s) * rows * (static_cast<size_t>(cfg->head_dim) + 2) * sizeof(float);
+  return static_cast<size_t>(s) * rows * (static_cast<size_t>(cfg->head_dim) * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_reqs,
@@ -227,7 +227,7 @@ size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_re
   int s = num_splits > 0 ? num_splits : choose_decode_splits(cfg, num_reqs, max_entries);
   if (s <= 1) return 0;
   const size_t rows = static_cast<size_t>(num_reqs) * cfg->num_q_heads;
-  return static_cast<size_t>(s) * rows * (static_cast<size_t>(cfg->head_dim) + 2) * sizeof(float);
+  return static_cast<size_t>(s) * rows * (static_cast<size_t>(cfg->head_dim) * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 }  // extern "C"

@@ -63,6 +63,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Round two floats to IEEE half (nearest even); `a` goes to the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t u) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> 16)));
+}
+
 // Rotate the interleaved channel pair held in one 32-bit bf16x2 word.
 __device__ __forceinline__ uint32_t rotate_pair(uint32_t u, float2 ph) {
   const float x0 = bf_lo(u), x1 = bf_hi(u);
@@ -191,8 +204,8 @@ struct PrefillArgs {
   const int32_t* frames;         // [R][max_entries] frame starts (document-local frames) or NULL
   const float* alibi;
   uint16_t* out;
-  float* o_part;
-  float* ml_part;
+  uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
+  float* ml_part;                // and (m, l) [splits][rows][Hq][2]
   int32_t Hq, Hkv, G, max_entries, total_q, m_q, eps, splits;
   int32_t exact;                 // nonzero: always take the two-pass exact-maximum route
   float scale_log2;
@@ -692,12 +705,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       // this split's unnormalised output, reference maximum and sum
       const size_t prow = static_cast<size_t>(split) * A.total_q * Hq + rowoff;
       if (lt > 0.f) {
+        const float inv = 1.0f / lt;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq)
-            *reinterpret_cast<f32x4*>(A.o_part + prow * kPD + 32 * dt + 8 * qq + 4 * h) =
-                f32x4{O[dt][nt][4 * qq], O[dt][nt][4 * qq + 1], O[dt][nt][4 * qq + 2], O[dt][nt][4 * qq + 3]};
+            *reinterpret_cast<uint2*>(A.o_part + prow * kPD + 32 * dt + 8 * qq + 4 * h) =
+                make_uint2(pack_f16x2(O[dt][nt][4 * qq] * inv, O[dt][nt][4 * qq + 1] * inv),
+                           pack_f16x2(O[dt][nt][4 * qq + 2] * inv, O[dt][nt][4 * qq + 3] * inv));
       }
       if (h == 0)
         *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(lt > 0.f ? m_ref[nt] : kNegInf, lt);
@@ -706,11 +721,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s with
-// M = max_s m_s, summed in split order (bit-for-bit reproducible).  One
-// 32-lane group per (row, head), 4 channels per lane.
+// Split merge: with w_s = 2^(m_s - M) l_s and M = max_s m_s, out = sum_s w_s
+// (o_s / l_s) / sum_s w_s, summed in split order (bit-for-bit reproducible).
+// Each split's output is stored already divided by its own sum, in fp16 (a
+// relative rounding of 2^-11, under the bf16 rounding of the result), which
+// halves the partial traffic.  One 32-lane group per (row, head), 4 channels
+// per lane.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void merge_kernel(const float* o_part, const float* ml_part, uint16_t* out,
+__global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, const float* ml_part, uint16_t* out,
                                                     int rows, int splits) {
   const int idx = blockIdx.x * 8 + (threadIdx.x >> 5);
   const int c = threadIdx.x & 31;
@@ -724,11 +742,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* o_part, const f
       const size_t row = static_cast<size_t>(s) * rows + idx;
       const float2 ml = *reinterpret_cast<const float2*>(ml_part + row * 2);
       if (ml.x == kNegInf) continue;
-      const float w = __builtin_amdgcn_exp2f(ml.x - M);
-      lsum = fmaf(w, ml.y, lsum);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(o_part + row * kPD + 4 * c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = fmaf(w, o[j], acc[j]);
+      const float w = __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+      lsum += w;
+      const uint2 o = *reinterpret_cast<const uint2*>(o_part + row * kPD + 4 * c);
+      acc[0] = fmaf(w, f16_lo(o.x), acc[0]);
+      acc[1] = fmaf(w, f16_hi(o.x), acc[1]);
+      acc[2] = fmaf(w, f16_lo(o.y), acc[2]);
+      acc[3] = fmaf(w, f16_hi(o.y), acc[3]);
     }
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
@@ -761,8 +781,8 @@ struct DecodeArgs {
   const int32_t* frames;         // [R][max_entries] frame starts (document-local frames) or NULL
   const float* alibi;
   uint16_t* out;
-  float* o_part;
-  float* ml_part;
+  uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
+  float* ml_part;                // and (m, l) [splits][rows][Hq][2]
   int32_t R, Hq, Hkv, G, max_entries, eps, splits;
   float scale_log2;
   RopeRev rope;
@@ -1130,7 +1150,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       A.out[rowoff * kPD + d] = static_cast<uint16_t>(pack_bf16x2(val, 0.f) & 0xffffu);
     } else {
       const size_t prow = static_cast<size_t>(split) * A.R * Hq + rowoff;
-      A.o_part[prow * kPD + d] = osum;
+      A.o_part[prow * kPD + d] = static_cast<uint16_t>(pack_f16x2(lsum > 0.f ? osum / lsum : 0.f, 0.f) & 0xffffu);
       if (d == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(M, lsum);
     }
   }
@@ -1422,8 +1442,8 @@ static size_t decode_lds_bytes(int nt, int group) {
 // ---------------------------------------------------------------------------
 
 static lazyattn_status merge_launch(int rows_total, int splits, const void* workspace, void* out, hipStream_t stream) {
-  const float* o_part = static_cast<const float*>(workspace);
-  const float* ml_part = o_part + static_cast<size_t>(splits) * rows_total * kPD;
+  const uint16_t* o_part = static_cast<const uint16_t*>(workspace);
+  const float* ml_part = reinterpret_cast<const float*>(o_part + static_cast<size_t>(splits) * rows_total * kPD);
   hipLaunchKernelGGL(merge_kernel, dim3((rows_total + 7) / 8), dim3(256), 0, stream, o_part, ml_part,
                      static_cast<uint16_t*>(out), rows_total, splits);
   return launched();
@@ -1466,8 +1486,9 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   const long long gx = (max_q_len + m_q - 1) / m_q;
   const long long gz = static_cast<long long>(Hkv) * splits;
   if (R > 65535 || gz > 65535 || gx > 0x7fffffff) return LAZYATTN_EUNSUPPORTED;
-  float* o_part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  float* ml_part = splits > 1 ? o_part + static_cast<size_t>(splits) * total_q * Hq * kPD : nullptr;
+  uint16_t* o_part = splits > 1 ? static_cast<uint16_t*>(workspace) : nullptr;
+  float* ml_part = splits > 1 ? reinterpret_cast<float*>(o_part + static_cast<size_t>(splits) * total_q * Hq * kPD)
+                              : nullptr;
   PrefillArgs a{static_cast<const uint16_t*>(q), cu_q_lens, static_cast<const uint16_t*>(k_pool),
                 static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
                 batch->frame_starts, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, Hq, Hkv, G, batch->max_entries,
@@ -1553,8 +1574,8 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   const size_t need = lazyattn_decode_workspace_size(cfg, R, batch->max_entries, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return LAZYATTN_EWORKSPACE;
   if (R > 65535 || Hkv > 65535) return LAZYATTN_EUNSUPPORTED;
-  float* o_part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  float* ml_part = splits > 1 ? o_part + static_cast<size_t>(splits) * R * Hq * kPD : nullptr;
+  uint16_t* o_part = splits > 1 ? static_cast<uint16_t*>(workspace) : nullptr;
+  float* ml_part = splits > 1 ? reinterpret_cast<float*>(o_part + static_cast<size_t>(splits) * R * Hq * kPD) : nullptr;
   DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
                batch->frame_starts, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, R, Hq, Hkv, G,
@@ -1626,7 +1647,7 @@ lazyattn_status lazyattn_merge_splits(const lazyattn_config* cfg, int32_t num_ro
   if (cfg->dtype != LAZYATTN_BF16) return LAZYATTN_EUNSUPPORTED;
   if (!workspace || !out) return LAZYATTN_EINVAL;
   const long long rows_total = static_cast<long long>(num_rows) * cfg->num_q_heads;
-  const size_t need = static_cast<size_t>(num_splits) * rows_total * (kPD + 2) * sizeof(float);
+  const size_t need = static_cast<size_t>(num_splits) * rows_total * (kPD * sizeof(uint16_t) + 2 * sizeof(float));
   if (workspace_bytes < need) return LAZYATTN_EWORKSPACE;
   if (rows_total > 0x7fffffffLL - 8) return LAZYATTN_EUNSUPPORTED;
   return merge_launch(static_cast<int>(rows_total), num_splits, workspace, out, stream);

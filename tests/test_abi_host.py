@@ -146,7 +146,7 @@ def test_split_heuristics_and_workspace_sizes():
     # 16 requests x 8 KV heads of one 64-position tile -> too few work-groups: split the keys
     s = _abi.prefill_splits(c, 16, 64, 260)
     assert s == 2
-    assert _abi.prefill_workspace_size(c, 16, 1024, 64, 260) == s * 1024 * 32 * 130 * 4
+    assert _abi.prefill_workspace_size(c, 16, 1024, 64, 260) == s * 1024 * 32 * (128 * 2 + 8)
     assert _abi.prefill_workspace_size(c, 16, 1024, 64, 260, 1) == 0
     # 128 requests x 8 KV heads is plenty for decode
     assert _abi.decode_splits(c, 128, 274) == 1
@@ -154,7 +154,7 @@ def test_split_heuristics_and_workspace_sizes():
     c70 = _cfg(num_q_heads=64, num_kv_heads=8)
     s = _abi.decode_splits(c70, 4, 2184)
     assert s >= 16
-    assert _abi.decode_workspace_size(c70, 4, 2184) == s * 4 * 64 * 130 * 4
+    assert _abi.decode_workspace_size(c70, 4, 2184) == s * 4 * 64 * (128 * 2 + 8)
     assert _abi.decode_workspace_size(_cfg(dtype="f32", head_dim=64), 4, 100, 8) == 0
 
 
@@ -188,7 +188,7 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch():
     # merge: bad counts, short workspace, and the no-op cases
     assert lib.lazyattn_merge_splits(ctypes.byref(c), 4, 0, P, 1 << 20, P, None) == _abi.EINVAL
     assert lib.lazyattn_merge_splits(ctypes.byref(c), -1, 2, P, 1 << 20, P, None) == _abi.EINVAL
-    assert lib.lazyattn_merge_splits(ctypes.byref(c), 4, 2, P, 4 * 4 * 2 * 130 * 4 - 1, P, None) == _abi.EWORKSPACE
+    assert lib.lazyattn_merge_splits(ctypes.byref(c), 4, 2, P, 2 * 4 * 4 * (128 * 2 + 8) - 1, P, None) == _abi.EWORKSPACE
     assert lib.lazyattn_merge_splits(ctypes.byref(c), 4, 1, None, 0, None, None) == _abi.OK
     assert lib.lazyattn_merge_splits(ctypes.byref(c), 0, 3, None, 0, None, None) == _abi.OK
     # document-local frames: RoPE and bf16 only; the framed append needs its indices
