@@ -144,6 +144,19 @@ class Timer:
         t.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    def launches(self, fn, n):
+        """Per-launch times (ms) of n back-to-back launches, each bracketed by its own events."""
+        t = self.torch
+        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
+        t.cuda.synchronize()
+        self.busy()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        t.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in ev)
+
     def steps(self, attend, merge, n):
         """n steps of [attention kernel, merge kernel]: (ms per step, ms per attention launch)."""
         t = self.torch
@@ -209,6 +222,9 @@ def bench_prefill(torch, args, W, staging, _abi):
             acc.append(timer.span(lambda: fn(pools), 1))
     del flush
     med = lambda v: sorted(v)[len(v) // 2]
+    # distribution of single attention launches (50, each between its own events)
+    per = timer.launches(lambda: call.attend(pools), 50)
+    pct = {"p10": per[len(per) // 10], "p50": per[len(per) // 2], "p90": per[(9 * len(per)) // 10]}
     # materialise-then-attend baseline on the same batch: private rotated copies of every
     # request's blocks, rotated queries, then the rotation-free kernel over the copy
     mat = staging.MaterializedPrefill(s, pb, "cuda")
@@ -221,7 +237,7 @@ def bench_prefill(torch, args, W, staging, _abi):
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
     return dict(wl=wl, pb=pb, ms=ms, ms_attend=med(att), ms_none=med(step_none), ms_none_attend=med(att_none),
                 att=att, att_none=att_none, att_framed=att_framed, ms_framed_attend=med(att_framed),
-                ms_fp8_attend=med(att_fp8), cold=med(cold), cold_none=med(cold_none), flops=flops, base=base,
+                ms_fp8_attend=med(att_fp8), pct=pct, cold=med(cold), cold_none=med(cold_none), flops=flops, base=base,
                 splits=call.splits, pools=pools)
 
 
@@ -273,6 +289,8 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = Tru
             ms_fp8f = timer.span(lambda: call8f.attend(fpools8), 3)
         if step < 0:
             continue
+        if step % 64 == 63:
+            print(f"# decode step {step + 1}/{n_steps}", file=sys.stderr, flush=True)
         tot_ms += ms_att
         tot_merge_ms += max(ms_step - ms_att, 0.0)
         tot_ms_none += ms_none
@@ -320,6 +338,63 @@ def hit_ratio_study(W, _abi) -> dict:
             row["agnostic_over_prefix"] = round(row["agnostic"] / max(row["prefix"], 1e-12), 2)
             out["token_hit_ratio"][f"zipf{skew}_{gib}GiB"] = row
     out["requests_per_s"] = round(n_admits / t_run, 1)
+    return out
+
+
+def bench_configs(torch, W, staging, _abi) -> dict:
+    """The other configurations, warm (medians of three 10-launch spans), each with its
+    rotation-free control on the same inputs: the Llama-3.1-70B 32k shape (a 2048-token chunk of
+    each of 4 requests, and a decode step with split-K) and the MQA stress sweep (four access skews,
+    uniform = the no-reuse control, each under RoPE, ALiBi and no encoding)."""
+    timer = Timer(torch)
+    med = lambda v: sorted(v)[len(v) // 2]
+    span = lambda fn: med([timer.span(fn, 10) for _ in range(3)])
+    out = {}
+
+    def one(wl, encodings):
+        s = wl.spec
+        pools = staging.DevicePools(wl, "cuda")
+        pb = wl.prefill_batch()
+        cfg = staging.config_for(s)
+        res = {}
+        if pb is not None:
+            staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
+            flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
+            for pe in encodings:
+                c = staging.PrefillCall(staging.config_for(s, pe=pe), s, pb, "cuda")
+                c.run(pools)
+                ms = span(lambda: c.run(pools))
+                res[f"prefill_{pe}_us"] = round(ms * 1e3, 2)
+                res[f"prefill_{pe}_TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 2)
+        staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, "cuda")
+        d = wl.decode_step(0)
+        if d is not None:
+            staging.append_tokens(cfg, pools, d, s.dtype, "cuda")
+            by = decode_bytes(d, wl)
+            for pe in encodings:
+                c = staging.DecodeCall(staging.config_for(s, pe=pe), s, d, "cuda")
+                c.run(pools)
+                ms = span(lambda: c.run(pools))
+                res[f"decode_{pe}_us"] = round(ms * 1e3, 2)
+                res[f"decode_{pe}_GBps_logical"] = round(by["logical"] / (ms * 1e-3) / 1e9, 1)
+            res["decode_GB_logical"] = round(by["logical"] / 1e9, 4)
+            res["decode_GB_unique"] = round(by["unique"] / 1e9, 4)
+        for ph in ("prefill", "decode"):
+            if f"{ph}_rope_us" in res and f"{ph}_none_us" in res:
+                res[f"{ph}_rope_overhead"] = round(res[f"{ph}_rope_us"] / res[f"{ph}_none_us"] - 1.0, 4)
+        del pools
+        torch.cuda.empty_cache()
+        return res
+
+    wl = W.build_workload(W.spec(4, n_decode=1))
+    out["llama70b_32k"] = dict(what="4 requests x 64 Zipf(1.0) documents x 512 tokens; 2048-token chunk; "
+                                    "decode step 0 with the split-K heuristic", **one(wl, ("rope", "none")))
+    print("# 70B config done", file=sys.stderr, flush=True)
+    for skew in W.CFG5_SKEWS:
+        wl = W.build_workload(W.spec(5, skew=skew))
+        out[f"mqa_skew{skew}"] = one(wl, ("rope", "alibi", "none"))
+    out["mqa_what"] = ("MQA stress: 32 prefill requests (128-token queries) + 96 decode requests, 4..32 lognormal "
+                       "documents each; skew 0.0 = uniform access, the no-reuse control")
     return out
 
 
@@ -372,7 +447,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-steps", type=int, default=16)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-configs", action="store_true", help="skip the 70B and MQA configuration timings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time the prefill launches only")
     ap.add_argument("--decode-only", action="store_true", help="run decode launches only (for profiling)")
@@ -417,6 +493,7 @@ def main() -> int:
                 "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "prefill_bf16_kernel<ROPE>", "flops_per_launch": pre["flops"],
                 "avg_launch_us": round(pre["ms_attend"] * 1e3, 2),
+                "launch_us_p10_p50_p90": [round(pre["pct"][k] * 1e3, 2) for k in ("p10", "p50", "p90")],
                 "cold_launch_us": round(pre["cold"] * 1e3, 2),
                 "merge_kernel_us": round((pre["ms"] - pre["ms_attend"]) * 1e3, 2)}
     rope_overhead = {"prefill_rope_us": round(pre["ms_attend"] * 1e3, 2),
@@ -493,6 +570,9 @@ def main() -> int:
         out["document_frames"]["decode_attention_us"] = round(dec["ms_framed"] * 1e3, 2)
         out["document_frames"]["decode_overhead_vs_norotation"] = round(dec["ms_framed"] / dec["ms_none"] - 1.0, 4)
         print(f"# decode done: {dec['ms'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    if not args.prefill_only and not args.no_configs:
+        out["configs"] = bench_configs(torch, W, staging, _abi)
+        print("# configs done", file=sys.stderr, flush=True)
     out["pool_hit_ratio"] = hit_ratio_study(W, _abi)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre, W)
