@@ -220,6 +220,7 @@ constexpr int kPrefillThreads = 512;    // threads per prefill work-group
 constexpr int kKS = kPD + 8;             // K~ row stride in bf16 (272 B: conflict-free 16 B reads)
 constexpr int kVE = kPD * kBlock;        // one entry of V, channel-major [D][16], in bf16
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64: larger row sums redo with the exact maximum
+constexpr float kSumFloor = 5.42101086242752217e-20f;  // 2^-64: a row with a visible key and a smaller sum redoes too
 
 // LDS row of tile-local key (entry E, row rho) in the K~ buffer (S^T row order)
 __device__ __forceinline__ int krow_of(int E, int rho) {
@@ -279,6 +280,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     e_stop = lo;
   }
   const int T = (e_stop - e_begin + 3) >> 2;          // key tiles of this work-group
+  const int st_first = (T > 0) ? static_cast<int>(word_start(trow[e_begin])) : L;   // first key position
+  // ALiBi walks the tiles nearest-first: the first tile then holds the keys of
+  // largest bias, whose maximum is the softmax reference (its key weighs exactly
+  // 1, as on the exact route); the bias only lowers the scores of later tiles
+  constexpr bool kNearestFirst = (PE == LAZYATTN_PE_ALIBI);
+  auto tile_e0 = [&](int j) { return e_begin + 4 * (kNearestFirst ? (T - 1 - j) : j); };
 
   // ---- this lane's query row: column c of the wave's 32-row tile -------------------
   constexpr int NT = 1;
@@ -300,9 +307,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   const uint64_t sentinel = static_cast<uint64_t>(static_cast<uint32_t>(L)) << 32;   // start = L
   auto load_words = [&](int j) -> uint64_t {
     const int x = lane & 7;
-    const int e = e_begin + 4 * j + x;
-    const uint64_t w = trow[min(e, ne - 1)];
-    return (x < 5 && e < ne) ? w : sentinel;
+    const int e = tile_e0(j) + x;
+    const uint64_t w = trow[max(min(e, ne - 1), 0)];
+    return (x < 5 && e < ne && e >= e_begin) ? w : sentinel;
   };
   // entry x of the tile whose words are in wv: (block, start, length); past the
   // split's last entry the length is 0 and the start L
@@ -311,7 +318,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     const int b = __builtin_amdgcn_readlane(static_cast<int>(lo_w), x);
     const int s0 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x);
     const int s1 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x + 1);
-    const bool valid = e_begin + 4 * j + x < e_stop;
+    const int e = tile_e0(j) + x;
+    const bool valid = e < e_stop && e >= e_begin;
     blk = valid ? b : 0;
     st = valid ? s0 : L;
     ln = valid ? s1 - s0 : 0;
@@ -654,16 +662,18 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     }
   };
   clear_acc();
-  bool two_pass = (PE == LAZYATTN_PE_ALIBI) || (A.exact != 0);
+  bool two_pass = A.exact != 0;
   if (T > 0 && !two_pass) {
     pass(false, true);
-    // a row sum this large means some score outgrew the first tile's maximum:
-    // redo the work-group with the exact maximum
+    // a row sum this large means some score outgrew the first tile's maximum,
+    // and one this small (with a visible key) that every weight underflowed:
+    // either way, redo the work-group with the exact maximum
     bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float lt = lsum[nt] + __shfl_xor(lsum[nt], 32);
-      bad = bad || (row_ok[nt] && !(lt < kSumLimit));
+      const bool visible = st_first <= p_row[nt];
+      bad = bad || (row_ok[nt] && (!(lt < kSumLimit) || (visible && !(lt >= kSumFloor))));
     }
     if (tid == 0) redo_s = 0;
     __syncthreads();

@@ -325,6 +325,30 @@ def test_other_encodings_llama8b_prefill(pe):
     compare_prefill(wl, pb, got, orc, pe=pe, label=f"8B prefill pe={pe}")
 
 
+@pytest.mark.parametrize("num_splits", [1, 5])
+def test_alibi_prefill_running_reference(num_splits):
+    """ALiBi's softmax reference follows the running row maximum.  One split puts a
+    whole 4k-token context in one work-group (the reference moves tile after tile);
+    five splits start some work-groups far from the query.  Both against the oracle
+    and against the exact-maximum route on the same inputs."""
+    say(f"8B ALiBi prefill, running reference, splits={num_splits}")
+    wl = W.build_workload(W.spec(2, requests=[4]))
+    pb, got, pools = run_prefill(wl, pe="alibi", num_splits=num_splits)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, pe="alibi", label=f"8B ALiBi prefill splits={num_splits}")
+    _, exact, _ = run_prefill(wl, pe="alibi", exact_max=True, num_splits=num_splits, pools=pools, pb=pb)
+    compare_prefill(wl, pb, exact, orc, pe="alibi", label=f"8B ALiBi prefill, exact route, splits={num_splits}")
+    # steep heads weigh a few keys, so outputs reach |o| ~ 4 and each route carries
+    # the bf16 weights' rounding (~1e-2 there): two results each within the bf16 bar
+    # of the exact value (half a step + 1e-2) are within one step + 2e-2 of each other
+    d = np.abs(got - exact)
+    excess = d - 2.0 * half_ulp(np.maximum(np.abs(got), np.abs(exact)), "bf16")
+    say(f"running vs exact reference: max {d.max():.2e} (beyond one bf16 step {excess.max():.2e}) "
+        f"mean {d.mean():.2e}")
+    assert excess.max() <= 2e-2 and d.mean() <= 5e-4
+
+
 # ---------------------------------------------------------------------------
 # softmax reference: the exact two-pass route, forced and triggered
 # ---------------------------------------------------------------------------
@@ -368,6 +392,67 @@ def test_prefill_redo_when_scores_outgrow_the_first_tile():
     mx, mn = diff_stats(g, rr)
     say(f"scaled queries vs oracle: max {mx:.2e} mean {mn:.2e}")
     assert mn <= 5e-2
+
+
+def test_alibi_prefill_far_keys_with_huge_scores():
+    # ALiBi walks each work-group's key tiles nearest-first and takes the softmax
+    # reference from the nearest tile.  Request 0's first document with keys
+    # scaled by 64 (exact in bf16) scores ~200 base-2 units above the rest.  On
+    # heads 0..11 (slope >= 1/8) its bias over > 3.5k positions exceeds 600 units:
+    # it weighs nothing, and the outputs follow the oracle at the usual bar.  On
+    # heads 20..31 it dominates and the row sums pass 2^64, so those work-groups
+    # redo their rows with the exact maximum: bit for bit the exact route's.
+    say("8B ALiBi prefill, first document's keys scaled by 64")
+    wl = W.build_workload(W.spec(2, requests=[2]))
+    pb = wl.prefill_batch()
+    blocks = wl.doc_blocks(int(pb["requests"][0].doc_ids[0]))
+    pools = staging.DevicePools(wl, DEV)
+    bi = torch.from_numpy(np.asarray(blocks, dtype=np.int64)).to(DEV)
+    pools.k[bi] = pools.k[bi] * 64
+    orc = OracleState(wl)
+    orc.k[blocks] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(orc.k[blocks]) * np.float32(64.0))
+    orc.append(pb)
+    _, fast, _ = run_prefill(wl, pe="alibi", num_splits=1, pools=pools, pb=pb)
+    _, exact, _ = run_prefill(wl, pe="alibi", num_splits=1, pools=pools, pb=pb, exact_max=True)
+    assert np.all(np.isfinite(fast))
+    a, b = int(pb["cu_q_lens"][0]), int(pb["cu_q_lens"][1])
+    assert np.array_equal(fast[a:b, 20:], exact[a:b, 20:])
+    steep = list(range(12))
+    ref = orc.prefill(pb, pe="alibi", requests=[0], heads=steep)[0]
+    mx, mn = assert_parity(fast[a:b, steep], ref, "bf16", "ALiBi, far keys with huge scores")
+    say(f"ALiBi far huge keys, heads 0..11 of request 0: max {mx:.2e} mean {mn:.2e}")
+
+
+def test_alibi_prefill_redo_when_every_weight_underflows():
+    # A 496-token document (31 entries) then a 64-token chunk: one split holds
+    # 35 entries, so the nearest tile is entries 32..34 (positions 512..559) and
+    # the chunk's first 16 rows (positions 496..511) see none of its keys; they
+    # keep reference 0.  Every key equal to (1, ..., 1) and every query to
+    # -12.25 (..., 1) put every score at -200 base-2 units: those rows' weights
+    # all underflow, and the work-groups must redo them with the exact maximum
+    # (bit for bit the exact route's; without the redo they would divide 0 by 0).
+    say("8B ALiBi prefill, constant scores of -200 (underflow redo route)")
+    wl = W.build_workload(W.spec(2, requests=[1], docs=(1, 1), doc_len=496))
+    s = wl.spec
+    pb = dict(wl.prefill_batch())
+    assert int(pb["num_entries"][0]) == 35 and int(pb["table_starts"][0][31]) == 496
+    one = W.f32_to_bf16_bits(np.float32(1.0))
+    pb["k_new"] = np.full_like(pb["k_new"], one)
+    pb["q"] = np.full_like(pb["q"], W.f32_to_bf16_bits(np.float32(-12.25)))
+    blocks = wl.doc_blocks(int(pb["requests"][0].doc_ids[0]))
+    pools = staging.DevicePools(wl, DEV)
+    bi = torch.from_numpy(np.asarray(blocks, dtype=np.int64)).to(DEV)
+    pools.k[bi] = 1.0
+    orc = OracleState(wl)
+    orc.k[blocks] = np.full_like(orc.k[blocks], one)
+    orc.append(pb)
+    _, fast, _ = run_prefill(wl, pe="alibi", num_splits=1, pools=pools, pb=pb)
+    _, exact, _ = run_prefill(wl, pe="alibi", num_splits=1, pools=pools, pb=pb, exact_max=True)
+    assert np.all(np.isfinite(fast))
+    assert np.array_equal(fast, exact)
+    ref = orc.prefill(pb, pe="alibi")[0]
+    mx, mn = assert_parity(fast, ref, s.dtype, "ALiBi underflow redo")
+    say(f"ALiBi underflow redo: max {mx:.2e} mean {mn:.2e}")
 
 
 # ---------------------------------------------------------------------------
