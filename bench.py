@@ -442,6 +442,26 @@ def calibrate_copy(torch) -> None:
     print(json.dumps({"copy_bytes": n, "dispatches": 3}), flush=True)
 
 
+def copy_bandwidth(torch) -> float:
+    """GB/s of a plain 1 GiB device-to-device copy (2 GiB moved), median of 5: the
+    HBM bandwidth this GPU reaches with a library kernel, as context for the others."""
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * n / (sorted(ts)[2] * 1e-3) / 1e9
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -573,6 +593,7 @@ def main() -> int:
     if not args.prefill_only and not args.no_configs:
         out["configs"] = bench_configs(torch, W, staging, _abi)
         print("# configs done", file=sys.stderr, flush=True)
+    out["device_copy_GBps"] = round(copy_bandwidth(torch), 1)
     out["pool_hit_ratio"] = hit_ratio_study(W, _abi)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pre, W)

@@ -44,5 +44,7 @@ int choose_prefill_splits(const lazyattn_config* cfg, int num_reqs, int max_q_le
 int choose_decode_splits(const lazyattn_config* cfg, int num_reqs, int max_entries);
 int prefill_entries_per_split(int max_entries, int splits);
 int decode_entries_per_split(int max_entries, int splits);
+// decode work-groups per (request, KV head, split): 2 for groups of more than 16 heads
+int decode_halves(int group);
 
 }  // namespace lazyattn

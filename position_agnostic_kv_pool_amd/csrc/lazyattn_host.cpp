@@ -77,12 +77,18 @@ int choose_prefill_splits(const lazyattn_config* cfg, int num_reqs, int max_q_le
   return std::max(1, std::min(s, 64));
 }
 
+int decode_halves(int group) { return group > 16 ? 2 : 1; }
+
 int choose_decode_splits(const lazyattn_config* cfg, int num_reqs, int max_entries) {
   if (cfg->dtype != LAZYATTN_BF16) return 1;
-  const long long units = static_cast<long long>(num_reqs) * cfg->num_kv_heads;
+  const long long units = static_cast<long long>(num_reqs) * cfg->num_kv_heads *
+                          decode_halves(cfg->num_q_heads / cfg->num_kv_heads);
   const int target = 1024;  // four work-groups per compute unit
   if (units >= target) return 1;
-  int s = ceil_div(target, std::max(1LL, units));
+  // enough work-groups, and splits of at most ~128 entries so that the longest
+  // request does not hold the tail when context lengths differ (splits past a
+  // request's end exit at once; more splits cost more in the merge)
+  int s = std::max(ceil_div(target, std::max(1LL, units)), ceil_div(max_entries, 128));
   // keep at least 32 entries (8 per wave) per split
   s = std::min(s, std::max(1, max_entries / 32));
   return std::max(1, std::min(s, 256));

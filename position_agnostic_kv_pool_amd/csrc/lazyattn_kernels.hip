@@ -116,8 +116,13 @@ struct EntryInfo {
 };
 
 // Decode table entry e of a request: block id, logical start and valid length
-// (next entry's start, or the context length for the last entry).
-__device__ __forceinline__ EntryInfo entry_info(const uint64_t* row, int e, int n_ent, int ctx) {
+// (next entry's start, or the context length for the last entry).  The words
+// are read through the constant address space: tables are never written while
+// a kernel runs, and a wave-uniform index then always makes a scalar load,
+// whatever stores the kernel holds.
+typedef const __attribute__((address_space(4))) uint64_t* const_words;
+__device__ __forceinline__ EntryInfo entry_info(const uint64_t* row_ptr, int e, int n_ent, int ctx) {
+  const const_words row = (const_words)row_ptr;   // an address-space cast
   const uint64_t w = row[e];
   EntryInfo r;
   r.blk = word_block(w);
@@ -308,8 +313,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   auto load_words = [&](int j) -> uint64_t {
     const int x = lane & 7;
     const int e = tile_e0(j) + x;
-    const uint64_t w = trow[max(min(e, ne - 1), 0)];
-    return (x < 5 && e < ne && e >= e_begin) ? w : sentinel;
+    // nearest-first: tiles past the last (j >= T) lie below e_begin
+    const uint64_t w = trow[kNearestFirst ? max(min(e, ne - 1), 0) : min(e, ne - 1)];
+    return (x < 5 && e < ne && (!kNearestFirst || e >= e_begin)) ? w : sentinel;
   };
   // entry x of the tile whose words are in wv: (block, start, length); past the
   // split's last entry the length is 0 and the start L
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     const int s0 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x);
     const int s1 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x + 1);
     const int e = tile_e0(j) + x;
-    const bool valid = e < e_stop && e >= e_begin;
+    const bool valid = e < e_stop && (!kNearestFirst || e >= e_begin);
     blk = valid ? b : 0;
     st = valid ? s0 : L;
     ln = valid ? s1 - s0 : 0;
@@ -731,35 +737,54 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: with w_s = 2^(m_s - M) l_s and M = max_s m_s, out = sum_s w_s
-// (o_s / l_s) / sum_s w_s, summed in split order (bit-for-bit reproducible).
-// Each split's output is stored already divided by its own sum, in fp16 (a
-// relative rounding of 2^-11, under the bf16 rounding of the result), which
-// halves the partial traffic.  One 32-lane group per (row, head), 4 channels
-// per lane.
+// Split merge: out = sum_s w_s (o_s / l_s) / sum_s w_s with w_s = 2^(m_s - M) l_s
+// and M = max_s m_s.  Each split's output is stored already divided by its own
+// sum, in fp16 (a relative rounding of 2^-11, under the bf16 rounding of the
+// result), which halves the partial traffic.  One 32-lane group per (row,
+// head), 4 channels per lane.  Splits are taken four at a time with all eight
+// loads issued together; M is the running maximum, and what was summed before
+// a chunk raised it is rescaled (the order is fixed: reproducible bit for
+// bit).  A split with m = -inf (no visible key, or past its request's end)
+// weighs 0, and its output, which may never have been written, is dropped by a
+// select.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, const float* ml_part, uint16_t* out,
                                                     int rows, int splits) {
   const int idx = blockIdx.x * 8 + (threadIdx.x >> 5);
   const int c = threadIdx.x & 31;
   if (idx >= rows) return;
-  float M = kNegInf;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml_part[(static_cast<size_t>(s) * rows + idx) * 2]);
+  float M = kNegInf, lsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < splits; ++s) {
-      const size_t row = static_cast<size_t>(s) * rows + idx;
-      const float2 ml = *reinterpret_cast<const float2*>(ml_part + row * 2);
-      if (ml.x == kNegInf) continue;
-      const float w = __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
-      lsum += w;
-      const uint2 o = *reinterpret_cast<const uint2*>(o_part + row * kPD + 4 * c);
-      acc[0] = fmaf(w, f16_lo(o.x), acc[0]);
-      acc[1] = fmaf(w, f16_hi(o.x), acc[1]);
-      acc[2] = fmaf(w, f16_lo(o.y), acc[2]);
-      acc[3] = fmaf(w, f16_hi(o.y), acc[3]);
+  for (int s0 = 0; s0 < splits; s0 += 4) {
+    float2 ml[4];
+    uint2 o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const size_t row = static_cast<size_t>(min(s0 + j, splits - 1)) * rows + idx;
+      ml[j] = *reinterpret_cast<const float2*>(ml_part + row * 2);
+      o[j] = *reinterpret_cast<const uint2*>(o_part + row * kPD + 4 * c);
     }
+    bool live[4];
+    float mc = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      live[j] = (s0 + j < splits) && (ml[j].x != kNegInf);
+      mc = fmaxf(mc, live[j] ? ml[j].x : kNegInf);
+    }
+    const float Mn = fmaxf(M, mc);
+    const float f = (M == kNegInf || Mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(M - Mn);
+    lsum *= f;
+    acc *= f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float w = live[j] ? __builtin_amdgcn_exp2f(ml[j].x - Mn) * ml[j].y : 0.f;
+      lsum += w;
+      acc[0] = fmaf(w, live[j] ? f16_lo(o[j].x) : 0.f, acc[0]);
+      acc[1] = fmaf(w, live[j] ? f16_hi(o[j].x) : 0.f, acc[1]);
+      acc[2] = fmaf(w, live[j] ? f16_lo(o[j].y) : 0.f, acc[2]);
+      acc[3] = fmaf(w, live[j] ? f16_hi(o[j].y) : 0.f, acc[3]);
+    }
+    M = Mn;
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   *reinterpret_cast<uint2*>(out + static_cast<size_t>(idx) * kPD + 4 * c) =
@@ -794,6 +819,7 @@ struct DecodeArgs {
   uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
   float* ml_part;                // and (m, l) [splits][rows][Hq][2]
   int32_t R, Hq, Hkv, G, max_entries, eps, splits;
+  int32_t halves;                // 2: groups of 17..32 heads, one work-group per 16-head half
   float scale_log2;
   RopeRev rope;
 };
@@ -806,19 +832,49 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   extern __shared__ __attribute__((aligned(16))) float dsm[];
   float2* bsh = reinterpret_cast<float2*>(dsm);             // [4 waves][2][64]
   float* ml_s = dsm + 4 * 2 * 64 * 2;                         // [4][NT*16][2]
-  float* o_s = ml_s + 4 * NT * 16 * 2;                        // [4][G][kOS]
-  float2* rtab = reinterpret_cast<float2*>(o_s + 4 * A.G * kOS);  // [16][64] R(n), RoPE only
+  float* o_s = ml_s + 4 * NT * 16 * 2;                        // [4][Gw][kOS] (NT * 16 rows reserved)
+  float2* rtab = reinterpret_cast<float2*>(o_s + 4 * NT * 16 * kOS);  // [16][64] R(n), RoPE only
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
-  const int split = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
   const int G = A.G, Hq = A.Hq, Hkv = A.Hkv;
+  // Groups of more than 16 heads run as two work-groups of 16 heads each over
+  // the same entries.  Their linear ids differ by 8, so round-robin dispatch
+  // puts them on one XCD at about the same time and the second read of each
+  // block hits that XCD's L2: ids 16 j + i and 16 j + 8 + i (i < 8) are the
+  // two halves of work item 8 j + i = (split, kvh, request), split fastest.
+  int split, kvh, r, half = 0;
+  if (A.halves == 1) {
+    split = blockIdx.x;
+    kvh = blockIdx.y;
+    r = blockIdx.z;
+  } else {
+    const int id = blockIdx.x;
+    const int item = (id >> 4) * 8 + (id & 7);
+    half = (id >> 3) & 1;
+    if (item >= A.splits * Hkv * A.R) return;
+    split = item % A.splits;
+    const int rest = item / A.splits;
+    kvh = rest % Hkv;
+    r = rest / Hkv;
+  }
+  const int hb = 16 * half;                          // first head column of this work-group
+  const int Gw = min(16 * NT, G - hb);               // its head columns
   const int L = A.ctx[r];
   const int p = L - 1;
   const int ne = A.n_ent[r];
   const uint64_t* trow = A.tables + static_cast<size_t>(r) * A.max_entries;
   const int e_begin = split * A.eps;
   const int e_end = min(ne, e_begin + A.eps);
+  // a split past the request's last entry leaves only an empty (m, l) = (-inf, 0),
+  // which the merge skips without reading its output
+  if (A.splits > 1 && e_begin >= ne) {
+    if (tid < Gw) {
+      const size_t prow = static_cast<size_t>(split) * A.R * Hq + static_cast<size_t>(r) * Hq + kvh * G + hb + tid;
+      *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(kNegInf, 0.f);
+    }
+    return;
+  }
 
   // Channels of contraction step s held by lane (g, n): c0(s) .. c0(s) + 7 with
   // c0(s) = 32s + 8g for bf16 pools (each of a lane's four 16-byte K loads then
@@ -835,8 +891,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = nt * 16 + n;
-    const bool ok = col < G;
-    const int h = kvh * G + (ok ? col : 0);
+    const bool ok = col < Gw;
+    const int h = kvh * G + hb + (ok ? col : 0);
     slope[nt] = (PE == LAZYATTN_PE_ALIBI) ? alibi_slope(A.alibi, h, Hq) * kLog2e : 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1131,17 +1187,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = nt * 16 + n;
-    if (col >= G) continue;
+    if (col >= Gw) continue;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[(w * NT * 16 + col) * 2]);
     const float f = (M == kNegInf || m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - M);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<f32x4*>(o_s + (wave * G + col) * kOS + 16 * dt + 4 * g) = O[dt][nt] * f;
+      *reinterpret_cast<f32x4*>(o_s + (wave * Gw + col) * kOS + 16 * dt + 4 * g) = O[dt][nt] * f;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kPD; idx += 256) {
+  for (int idx = tid; idx < Gw * kPD; idx += 256) {
     const int col = idx / kPD, d = idx - col * kPD;
     float M = kNegInf;
 #pragma unroll
@@ -1151,9 +1207,9 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     for (int w = 0; w < 4; ++w) {
       const float mw = ml_s[(w * NT * 16 + col) * 2];
       if (M != kNegInf && mw != kNegInf) lsum += __builtin_amdgcn_exp2f(mw - M) * ml_s[(w * NT * 16 + col) * 2 + 1];
-      osum += o_s[(w * G + col) * kOS + d];
+      osum += o_s[(w * Gw + col) * kOS + d];
     }
-    const int h = kvh * G + col;
+    const int h = kvh * G + hb + col;
     const size_t rowoff = static_cast<size_t>(r) * Hq + h;
     if (A.splits == 1) {
       const float val = lsum > 0.f ? osum / lsum : 0.f;
@@ -1441,8 +1497,8 @@ static lazyattn_status check_batch(const lazyattn_batch* b) {
 // keeps the occupancy of the RoPE kernel it is compared with.
 constexpr size_t kDecodeLdsFloor = 56 * 1024;
 
-static size_t decode_lds_bytes(int nt, int group) {
-  const size_t need = (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(group) * kOS + 16 * 64 * 2) *
+static size_t decode_lds_bytes(int nt) {
+  const size_t need = (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(nt) * 16 * kOS + 16 * 64 * 2) *
                       sizeof(float);
   return need > kDecodeLdsFloor ? need : kDecodeLdsFloor;
 }
@@ -1534,21 +1590,12 @@ static void launch_decode_one(dim3 grid, size_t lds, hipStream_t stream, const D
 }
 
 template <int KV8>
-static void launch_decode(int pe_sel, int nt, dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
-  if (nt == 1) {
-    switch (pe_sel) {
-      case kPeFramed: launch_decode_one<kPeFramed, 1, KV8>(grid, lds, stream, a); break;
-      case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 1, KV8>(grid, lds, stream, a); break;
-      case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 1, KV8>(grid, lds, stream, a); break;
-      default: launch_decode_one<LAZYATTN_PE_ALIBI, 1, KV8>(grid, lds, stream, a); break;
-    }
-  } else {
-    switch (pe_sel) {
-      case kPeFramed: launch_decode_one<kPeFramed, 2, KV8>(grid, lds, stream, a); break;
-      case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 2, KV8>(grid, lds, stream, a); break;
-      case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 2, KV8>(grid, lds, stream, a); break;
-      default: launch_decode_one<LAZYATTN_PE_ALIBI, 2, KV8>(grid, lds, stream, a); break;
-    }
+static void launch_decode(int pe_sel, dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
+  switch (pe_sel) {
+    case kPeFramed: launch_decode_one<kPeFramed, 1, KV8>(grid, lds, stream, a); break;
+    case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 1, KV8>(grid, lds, stream, a); break;
+    case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 1, KV8>(grid, lds, stream, a); break;
+    default: launch_decode_one<LAZYATTN_PE_ALIBI, 1, KV8>(grid, lds, stream, a); break;
   }
 }
 
@@ -1589,16 +1636,20 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
                batch->frame_starts, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, R, Hq, Hkv, G,
-               batch->max_entries, decode_entries_per_split(batch->max_entries, splits), splits, scale * kLog2e,
-               rope};
-  const dim3 grid(splits, Hkv, R);
-  const int nt = G <= 16 ? 1 : 2;
-  const size_t lds = decode_lds_bytes(nt, G);
+               batch->max_entries, decode_entries_per_split(batch->max_entries, splits), splits,
+               decode_halves(G), scale * kLog2e, rope};
+  dim3 grid(splits, Hkv, R);
+  if (a.halves == 2) {
+    const long long items = static_cast<long long>(splits) * Hkv * R;
+    if ((items + 7) / 8 * 16 > 0x7fffffffLL) return LAZYATTN_EUNSUPPORTED;
+    grid = dim3(static_cast<unsigned>((items + 7) / 8 * 16), 1, 1);
+  }
+  const size_t lds = decode_lds_bytes(1);
   const int pe_sel = framed ? kPeFramed : cfg->pe;
   if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3)
-    launch_decode<1>(pe_sel, nt, grid, lds, stream, a);
+    launch_decode<1>(pe_sel, grid, lds, stream, a);
   else
-    launch_decode<0>(pe_sel, nt, grid, lds, stream, a);
+    launch_decode<0>(pe_sel, grid, lds, stream, a);
   *splits_out = splits;
   return launched();
 }
