@@ -83,12 +83,15 @@ int choose_decode_splits(const lazyattn_config* cfg, int num_reqs, int max_entri
   if (cfg->dtype != LAZYATTN_BF16) return 1;
   const long long units = static_cast<long long>(num_reqs) * cfg->num_kv_heads *
                           decode_halves(cfg->num_q_heads / cfg->num_kv_heads);
-  const int target = 1024;  // four work-groups per compute unit
+  const int target = 512;   // two work-groups per compute unit: what the LDS reservation lets run at once
   if (units >= target) return 1;
-  // enough work-groups, and splits of at most ~128 entries so that the longest
-  // request does not hold the tail when context lengths differ (splits past a
-  // request's end exit at once; more splits cost more in the merge)
-  int s = std::max(ceil_div(target, std::max(1LL, units)), ceil_div(max_entries, 128));
+  // one round of work-groups; when the longest request would then give a
+  // split more than ~160 entries (the tail of a batch with mixed context
+  // lengths), whole rounds more (a round and a bit would run a short second
+  // round as long as the first; splits past a request's end exit at once)
+  const int s0 = ceil_div(target, std::max(1LL, units));
+  const int s1 = ceil_div(max_entries, 160);
+  int s = s1 > s0 ? s0 * ceil_div(s1, s0) : s0;
   // keep at least 32 entries (8 per wave) per split
   s = std::min(s, std::max(1, max_entries / 32));
   return std::max(1, std::min(s, 256));

@@ -223,7 +223,12 @@ constexpr int kPD = 128;                 // head dim of the bf16 kernels
 constexpr int kPeFramed = 3;
 constexpr int kPrefillThreads = 512;    // threads per prefill work-group
 constexpr int kKS = kPD + 8;             // K~ row stride in bf16 (272 B: conflict-free 16 B reads)
-constexpr int kVE = kPD * kBlock;        // one entry of V, channel-major [D][16], in bf16
+// V of one entry in LDS: two planes [token half][channel][8 tokens], so that an
+// MFMA operand read (8 tokens of consecutive channels per lane) covers
+// contiguous bytes; the second plane sits 64 B off a 128 B boundary, which
+// puts the even and odd lanes of a staging write on different banks
+constexpr int kVH = kPD * 8 + 32;        // plane stride in bf16 (2112 B)
+constexpr int kVEs = 2 * kVH;            // entry stride in bf16
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64: larger row sums redo with the exact maximum
 constexpr float kSumFloor = 5.42101086242752217e-20f;  // 2^-64: a row with a visible key and a smaller sum redoes too
 
@@ -235,7 +240,7 @@ __device__ __forceinline__ int krow_of(int E, int rho) {
 template <int PE, int KV8>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const PrefillArgs A) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][4 * kVE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][4 * kVEs];
   __shared__ int redo_s;
 
   const int tid = threadIdx.x;
@@ -416,12 +421,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   // write the staged K~ and V into LDS buffer b
   auto stage_write = [&](int b) {
     uint32_t* kdst = reinterpret_cast<uint32_t*>(Ks[b]) + lane;
-    uint16_t* vdst = Vs[b] + E_own * kVE;
+    uint16_t* vdst = Vs[b] + E_own * kVEs + (lane & 1) * kVH;
 #pragma unroll
     for (int k = 0; k < 8; ++k) kdst[krow_of(E_own, 8 * part + k) * (kKS / 2)] = kr[k];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
-      *reinterpret_cast<uint4*>(&vdst[(64 * part + 32 * cc + (lane >> 1)) * kBlock + 8 * (lane & 1)]) = vr[cc];
+      *reinterpret_cast<uint4*>(&vdst[(64 * part + 32 * cc + (lane >> 1)) * 8]) = vr[cc];
   };
 
   // ---- query: rotated by R(m), scaled by scale*log2(e), rounded to bf16 -----------
@@ -608,12 +613,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       }
       if (!maxpass) {
         // P^T operands (weights of keys 8 h .. 8 h + 7 of entry 2 tau + ks) and
-        // O^T += V^T P^T, V of entry E read in the pool's channel-major layout;
+        // O^T += V^T P^T, V of entry E read from its token-half planes;
         // the exponentials of one entry overlap the products of the previous
         const uint16_t* vb = Vs[i & 1];
         // V operands (entry E, channel tile dt: read number 4 E + dt) two reads ahead
         auto vread = [&](int n) {
-          return *reinterpret_cast<const bf16x8*>(&vb[(n >> 2) * kVE + (32 * (n & 3) + c) * kBlock + 8 * h]);
+          return *reinterpret_cast<const bf16x8*>(&vb[(n >> 2) * kVEs + h * kVH + (32 * (n & 3) + c) * 8]);
         };
         bf16x8 av[3];
         av[0] = vread(0);

@@ -151,17 +151,20 @@ def test_split_heuristics_and_workspace_sizes():
     # 128 requests x 8 KV heads is plenty for decode
     assert _abi.decode_splits(c, 128, 274) == 1
     assert _abi.decode_workspace_size(c, 128, 274) == 0
+    # the 70B shape: 32 (request, KV head) units -> one round of 16 splits (137 entries each)
     c70 = _cfg(num_q_heads=64, num_kv_heads=8)
     s = _abi.decode_splits(c70, 4, 2184)
-    assert s >= 16
+    assert s == 16
     assert _abi.decode_workspace_size(c70, 4, 2184) == s * 4 * 64 * (128 * 2 + 8)
     assert _abi.decode_workspace_size(_cfg(dtype="f32", head_dim=64), 4, 100, 8) == 0
     # groups of more than 16 heads decode as two work-groups per (request, KV head,
-    # split): 96 MQA requests make 192 of them, so 6 splits reach 1024 work-groups,
-    # but 1300 entries make splits of at most 128 entries: 11
-    assert _abi.decode_splits(_cfg(num_q_heads=32, num_kv_heads=1), 96, 1300) == 11
+    # split): 96 MQA requests make 192 of them, so 3 splits fill one round of 512
+    # work-groups; 1300 entries would leave splits of 434 entries, so whole rounds
+    # more until they hold at most 160: 9
+    assert _abi.decode_splits(_cfg(num_q_heads=32, num_kv_heads=1), 96, 1300) == 9
     assert _abi.decode_splits(_cfg(num_q_heads=32, num_kv_heads=1), 96, 600) == 6
-    assert _abi.decode_splits(_cfg(num_q_heads=16, num_kv_heads=1), 96, 300) == 9   # 11 capped at 300 / 32
+    assert _abi.decode_splits(_cfg(num_q_heads=16, num_kv_heads=1), 96, 300) == 6
+    assert _abi.decode_splits(_cfg(num_q_heads=16, num_kv_heads=1), 96, 100) == 3   # 6 capped at 100 / 32
 
 
 def test_gpu_entry_points_reject_bad_arguments_before_launch():
