@@ -350,6 +350,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   const int E_own = ws >> 1, part = ws & 1;
   float2 r1 = make_float2(1.f, 0.f);               // R(1) at this lane's pair
   if (PE == LAZYATTN_PE_ROPE) r1 = unit_phase(1, A.rope.rev[lane]);
+  // The phases of a lane's 8 consecutive key rows: R(a + 1) = R(a) R(1), then
+  // R(a + k + 1) = 2 cos(f) R(a + k) - R(a + k - 1), one fused multiply-add per
+  // component instead of a complex product.  Over 8 rows the recurrence's
+  // rounding error stays within a few units in the last place of fp32: a
+  // perturbation at row j reaches row k scaled by sin((k - j) f) / sin(f) <= k - j.
+  const float two_cos = 2.0f * r1.x;
+  auto next_phase = [&](int k, float2& cur, float2& prev) {
+    if (k == 0) {
+      prev = cur;
+      cur = cmul(cur, r1);
+    } else {
+      const float2 nx = make_float2(fmaf(two_cos, cur.x, -prev.x), fmaf(two_cos, cur.y, -prev.y));
+      prev = cur;
+      cur = nx;
+    }
+  };
   uint32_t kr[8];
   uint4 vr[2];
   // FP8 pool: kr[k] holds the two codes of row 8 part + k (low 16 bits), vr[cc].xy
@@ -481,11 +497,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       }
       load_kv(blk);
       if (PE == LAZYATTN_PE_ROPE) {
-        float2 ph = unit_phase_turns(st - p0 + 8 * part, A.rope.rev[lane]);
+        float2 ph = unit_phase_turns(st - p0 + 8 * part, A.rope.rev[lane]), pq;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           kr[k] = KV8 ? key_fp8(k, ph) : rotate_pair(kr[k], ph);
-          ph = cmul(ph, r1);
+          if (k < 7) next_phase(k, ph, pq);
         }
       } else if (KV8 && PE != kPeFramed) {
 #pragma unroll
@@ -516,7 +532,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) S[tau][nt] = negm[nt];
-      float2 ph = make_float2(1.f, 0.f);
+      float2 ph = make_float2(1.f, 0.f), pq = ph;
       if (PE == LAZYATTN_PE_ROPE) ph = unit_phase_turns(nst - p0 + 8 * part, A.rope.rev[lane]);
       if (PE == kPeFramed) ph = unit_phase_turns(__builtin_amdgcn_readlane(fv1, E_own) - p0, A.rope.rev[lane]);
       // K~ operands are read one k-step ahead of their products
@@ -537,7 +553,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
           for (int nt = 0; nt < NT; ++nt) S[tau][nt] = mfma32x32x16(ak[kk & 1][tau], qf[8 * nt + kk], S[tau][nt]);
         if (PE == LAZYATTN_PE_ROPE) {
           kr[kk] = KV8 ? key_fp8(kk, ph) : rotate_pair(kr[kk], ph);
-          ph = cmul(ph, r1);
+          if (kk < 7) next_phase(kk, ph, pq);
         } else if (KV8) {
           kr[kk] = key_fp8(kk, ph);                 // framed: turned by ph; else converted
         } else if (PE == kPeFramed) {
