@@ -564,7 +564,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         // would otherwise sink it to the LDS write after the loop)
         asm volatile("" : "+v"(kr[kk]));
       }
-      if (nln < kBlock) mask_v(nln);
+      // a real branch: the masks cost 24 VALU a tile when computed unconditionally
+      if (__builtin_expect(nln < kBlock, 0)) mask_v(nln);
       stage_write((i + 1) & 1);
       // loads of tile i + 2, words of tile i + 3
       int lblk, lst, lln;
@@ -1099,7 +1100,9 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   #pragma unroll
         for (int s = 0; s < 4; ++s) ka[s] = __builtin_bit_cast(bf16x8, k[s]);
       }
-      if (inf.len < kBlock) {
+      // (the rare branches below are marked so: computed unconditionally, the V
+      // masks and the rescale would cost about 80 VALU instructions an entry)
+      if (__builtin_expect(inf.len < kBlock, 0)) {
         // zero V rows past the entry's length (they may hold anything, even NaN)
   #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -1135,7 +1138,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
         // raise the reference only when a score outgrows it by 2^8 (exact:
         // numerator and denominator share it); the test is one compare and a ballot
         const bool want = (lm > kRescaleSlack) || (m_run[nt] == kNegInf && lm > kNegInf);
-        if (__builtin_amdgcn_ballot_w64(want)) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(want) != 0, 0)) {
           float pm = fmaxf(lm, __shfl_xor(lm, 16));
           pm = fmaxf(pm, __shfl_xor(pm, 32));
           const bool raise = (pm > kRescaleSlack) || (m_run[nt] == kNegInf && pm > kNegInf);
