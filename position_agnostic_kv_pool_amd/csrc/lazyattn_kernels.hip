@@ -942,6 +942,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     __syncthreads();
   }
   if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) my_rev = A.rope.rev[lane];
+  // This lane's R(n) at its 16 pairs, held in registers: reading them from LDS
+  // at each entry put an LDS round trip on every entry's path (the empty asm
+  // keeps the compiler from turning the copies back into LDS reads at the uses)
+  float2 rn[16];
+  if (PE == LAZYATTN_PE_ROPE) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      rn[i] = rtab[i * 64 + lane];
+      asm volatile("" : "+v"(rn[i].x), "+v"(rn[i].y));
+    }
+  }
   // framed pool: frame starts of this request's entries, and the frame the
   // query fragments qb are currently turned to (none yet)
   const int32_t* frow = A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0);
@@ -1004,6 +1015,15 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   EntryInfo nx{};
   int fr_nx = 0;
   int e = __builtin_amdgcn_readfirstlane(e_begin + wave);
+  // RoPE: R(S - p) of a slot's entry at pair l, formed by lane l into the slot's
+  // LDS row as soon as the entry's loads are issued, so that the entry's
+  // rotation reads it without an LDS round trip on its own path
+  auto put_phase = [&](int sl, int start) {
+    if (PE == LAZYATTN_PE_ROPE) {
+      bsh[(wave * 2 + sl) * 64 + lane] = unit_phase_turns(start - p, my_rev);
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
     const int ee = e + 4 * sl;
@@ -1011,6 +1031,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     if (ee < e_end) {
       curb[sl] = entry_info(trow, ee, ne, L);
       load_kv(curb[sl].blk, krb[sl], vrb[sl]);
+      put_phase(sl, curb[sl].start);
       if (PE == kPeFramed) frb[sl] = frow[ee];
     }
   }
@@ -1020,7 +1041,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   }
 
   // one entry, its K/V in k and v (converted in place for FP8)
-  auto process = [&](const EntryInfo inf, const int fr, uint4 (&k)[4], uint2 (&v)[8], const int it)
+  auto process = [&](const EntryInfo inf, const int fr, uint4 (&k)[4], uint2 (&v)[8], const int sl)
                      __attribute__((always_inline)) {
       const uint32_t kexp = k[2].x, vexp = k[2].y;
       if (KV8) {
@@ -1065,11 +1086,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       // ---- rotate the key rows: R(S - p + n) = R(S - p) R(n) ------------------
       bf16x8 ka[4];
       if (PE == LAZYATTN_PE_ROPE) {
-        float2* bw = bsh + (wave * 2 + (it & 1)) * 64;
-        bw[lane] = unit_phase_turns(inf.start - p, my_rev);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // R(S - p) at pair l, written by lane l when the slot was loaded
+        const float2* bw = bsh + (wave * 2 + sl) * 64;
         if (KV8) {
           // the lane's 32 codes are in k[0..1]
   #pragma unroll
@@ -1079,8 +1097,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
             uint32_t w4[4];
   #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-              const int i = 4 * s + jj;                    // pair 16g + i
-              w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[c0(s) / 2 + jj], rtab[i * 64 + lane]));
+              // pair 16g + 4s + jj
+              w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[c0(s) / 2 + jj], rn[4 * s + jj]));
             }
             ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
           }
@@ -1090,8 +1108,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
             uint32_t w4[4] = {k[s].x, k[s].y, k[s].z, k[s].w};
   #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-              const int i = 4 * s + jj;                    // pair 16g + i
-              w4[jj] = rotate_pair(w4[jj], cmul(bw[c0(s) / 2 + jj], rtab[i * 64 + lane]));
+              w4[jj] = rotate_pair(w4[jj], cmul(bw[c0(s) / 2 + jj], rn[4 * s + jj]));   // pair 16s + 4g + jj
             }
             ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
           }
@@ -1172,16 +1189,18 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       }
   };
 
-  int it = 0;
   bool more = e < e_end;
   while (more) {
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       if (more) {
-        process(curb[sl], frb[sl], krb[sl], vrb[sl], it);
+        process(curb[sl], frb[sl], krb[sl], vrb[sl], sl);
         const int e_ld = e + 8;
         if (e_ld < e_end) {
           load_kv(nx.blk, krb[sl], vrb[sl]);
+          // the slot's phase row is rewritten only after this entry's reads of it
+          // (the same wave's LDS operations complete in order)
+          put_phase(sl, nx.start);
           curb[sl] = nx;
           frb[sl] = fr_nx;
           if (e_ld + 4 < e_end) {
@@ -1189,7 +1208,6 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
             if (PE == kPeFramed) fr_nx = frow[e_ld + 4];
           }
         }
-        ++it;
         e += 4;
         more = e < e_end;
       }
