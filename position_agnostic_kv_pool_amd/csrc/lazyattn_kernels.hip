@@ -762,9 +762,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 // Split merge: out = sum_s w_s (o_s / l_s) / sum_s w_s with w_s = 2^(m_s - M) l_s
 // and M = max_s m_s.  Each split's output is stored already divided by its own
 // sum, in fp16 (a relative rounding of 2^-11, under the bf16 rounding of the
-// result), which halves the partial traffic.  One 32-lane group per (row,
-// head), 4 channels per lane.  Splits are taken four at a time with all eight
-// loads issued together; M is the running maximum, and what was summed before
+// result), which halves the partial traffic.  One 16-lane group per (row,
+// head), 8 channels (16 bytes) per lane.  Splits are taken four at a time with
+// their loads issued together (nothing is read past the last split); M is the
+// running maximum, and what was summed before
 // a chunk raised it is rescaled (the order is fixed: reproducible bit for
 // bit).  A split with m = -inf (no visible key, or past its request's end)
 // weighs 0, and its output, which may never have been written, is dropped by a
@@ -772,19 +773,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, const float* ml_part, uint16_t* out,
                                                     int rows, int splits) {
-  const int idx = blockIdx.x * 8 + (threadIdx.x >> 5);
-  const int c = threadIdx.x & 31;
+  const int idx = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;                  // channels 8c .. 8c + 7
   if (idx >= rows) return;
   float M = kNegInf, lsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += 4) {
     float2 ml[4];
-    uint2 o[4];
+    uint4 o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const size_t row = static_cast<size_t>(min(s0 + j, splits - 1)) * rows + idx;
-      ml[j] = *reinterpret_cast<const float2*>(ml_part + row * 2);
-      o[j] = *reinterpret_cast<const uint2*>(o_part + row * kPD + 4 * c);
+      // splits is the same for every thread: past the last split nothing is read
+      ml[j] = make_float2(kNegInf, 0.f);
+      o[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (s0 + j < splits) {
+        const size_t row = static_cast<size_t>(s0 + j) * rows + idx;
+        ml[j] = *reinterpret_cast<const float2*>(ml_part + row * 2);
+        o[j] = *reinterpret_cast<const uint4*>(o_part + row * kPD + 8 * c);
+      }
     }
     bool live[4];
     float mc = kNegInf;
@@ -796,21 +802,25 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, cons
     const float Mn = fmaxf(M, mc);
     const float f = (M == kNegInf || Mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(M - Mn);
     lsum *= f;
-    acc *= f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] *= f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float w = live[j] ? __builtin_amdgcn_exp2f(ml[j].x - Mn) * ml[j].y : 0.f;
       lsum += w;
-      acc[0] = fmaf(w, live[j] ? f16_lo(o[j].x) : 0.f, acc[0]);
-      acc[1] = fmaf(w, live[j] ? f16_hi(o[j].x) : 0.f, acc[1]);
-      acc[2] = fmaf(w, live[j] ? f16_lo(o[j].y) : 0.f, acc[2]);
-      acc[3] = fmaf(w, live[j] ? f16_hi(o[j].y) : 0.f, acc[3]);
+      const uint32_t ow[4] = {o[j].x, o[j].y, o[j].z, o[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(w, live[j] ? f16_lo(ow[q]) : 0.f, acc[2 * q]);
+        acc[2 * q + 1] = fmaf(w, live[j] ? f16_hi(ow[q]) : 0.f, acc[2 * q + 1]);
+      }
     }
     M = Mn;
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  *reinterpret_cast<uint2*>(out + static_cast<size_t>(idx) * kPD + 4 * c) =
-      make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  *reinterpret_cast<uint4*>(out + static_cast<size_t>(idx) * kPD + 8 * c) =
+      make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                 pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
 // ---------------------------------------------------------------------------
@@ -1552,7 +1562,7 @@ static size_t decode_lds_bytes(int nt) {
 static lazyattn_status merge_launch(int rows_total, int splits, const void* workspace, void* out, hipStream_t stream) {
   const uint16_t* o_part = static_cast<const uint16_t*>(workspace);
   const float* ml_part = reinterpret_cast<const float*>(o_part + static_cast<size_t>(splits) * rows_total * kPD);
-  hipLaunchKernelGGL(merge_kernel, dim3((rows_total + 7) / 8), dim3(256), 0, stream, o_part, ml_part,
+  hipLaunchKernelGGL(merge_kernel, dim3((rows_total + 15) / 16), dim3(256), 0, stream, o_part, ml_part,
                      static_cast<uint16_t*>(out), rows_total, splits);
   return launched();
 }
