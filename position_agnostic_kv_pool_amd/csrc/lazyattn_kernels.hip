@@ -974,7 +974,10 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   }
   // framed pool: frame starts of this request's entries, and the frame the
   // query fragments qb are currently turned to (none yet)
-  const int32_t* frow = A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0);
+  // (read through the constant address space, like the table words: a vector
+  // load here would be followed by a wait that drains the K/V ring)
+  typedef const __attribute__((address_space(4))) int32_t* const_frames;
+  const const_frames frow = (const_frames)(A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0));
   int q_frame = 0, q_turns = 0;
   bool q_set = false;
 
