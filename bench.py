@@ -292,7 +292,9 @@ def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = Tru
         if step % 64 == 63:
             print(f"# decode step {step + 1}/{n_steps}", file=sys.stderr, flush=True)
         tot_ms += ms_att
-        tot_merge_ms += max(ms_step - ms_att, 0.0)
+        # with one split the step is the attention kernel alone (no merge is launched)
+        if call.splits > 1:
+            tot_merge_ms += max(ms_step - ms_att, 0.0)
         tot_ms_none += ms_none
         tot_ms_framed += ms_framed
         tot_ms_fp8 += ms_fp8
