@@ -347,6 +347,89 @@ def test_decode_equals_last_row_of_prefill():
     np.testing.assert_allclose(dec, pre[-1], rtol=0, atol=1e-14)
 
 
+# ---------------------------------------------------------------------------
+# appends: what the content-only pool holds after new tokens arrive
+# ([gist:Methodology]: the cache stores content only, no rotation).  Checked
+# against the documented layout, K [block][head][row][d] and V [block][head][d][row],
+# by reading every written element back with explicit indices, and against a
+# NaN-poisoned pool: every slot not written must still be NaN (np.isnan, since
+# assert_allclose would take NaN == NaN as a match).
+# ---------------------------------------------------------------------------
+_APPEND_SLOTS = [(1, 15), (2, 0), (2, 7), (0, 3), (3, 15)]     # (block, row): a last row, a partial block
+
+
+def _poisoned_pools(nb, Hkv, B, D, dtype=np.float64):
+    return np.full((nb, Hkv, B, D), np.nan, dtype=dtype), np.full((nb, Hkv, D, B), np.nan, dtype=dtype)
+
+
+def _hand_kv(n, Hkv, D):
+    # value i*1000 + h*100 + d (K) and its negative minus 0.5 (V): every element distinct
+    i, h, d = np.meshgrid(np.arange(n), np.arange(Hkv), np.arange(D), indexing="ij")
+    k = (1000.0 * i + 100.0 * h + d).astype(np.float64)
+    return k, -k - 0.5
+
+
+def test_append_kv_layout_and_untouched_slots():
+    B, Hkv, D, nb = 16, 2, 4, 5
+    kp, vp = _poisoned_pools(nb, Hkv, B, D)
+    k, v = _hand_kv(len(_APPEND_SLOTS), Hkv, D)
+    O.append_kv(kp, vp, k, v, [b * B + r for b, r in _APPEND_SLOTS], B)
+    written_k = np.zeros(kp.shape, dtype=bool)
+    written_v = np.zeros(vp.shape, dtype=bool)
+    for i, (b, r) in enumerate(_APPEND_SLOTS):
+        for h in range(Hkv):
+            for d in range(D):
+                assert kp[b, h, r, d] == 1000 * i + 100 * h + d
+                assert vp[b, h, d, r] == -(1000 * i + 100 * h + d) - 0.5
+                written_k[b, h, r, d] = True
+                written_v[b, h, d, r] = True
+    assert np.isnan(kp[~written_k]).all() and np.isnan(vp[~written_v]).all()
+    assert not np.isnan(kp[written_k]).any() and not np.isnan(vp[written_v]).any()
+
+
+def test_append_kv_bf16_bit_patterns_and_overwrite():
+    # bf16 pools are uint16 bit patterns: the append copies them unchanged; a second
+    # append to the same slot replaces it and leaves its neighbours alone
+    B, Hkv, D, nb = 16, 1, 2, 3
+    nan_bits = np.uint16(0x7FC0)
+    kp = np.full((nb, Hkv, B, D), nan_bits, dtype=np.uint16)
+    vp = np.full((nb, Hkv, D, B), nan_bits, dtype=np.uint16)
+    k = np.array([[[0x3F80, 0xBF80]], [[0x4000, 0x0001]]], dtype=np.uint16)   # 1, -1 ; 2, smallest subnormal
+    v = np.array([[[0x4040, 0x8000]], [[0x7F7F, 0xC000]]], dtype=np.uint16)   # 3, -0 ; max finite, -2
+    O.append_kv(kp, vp, k, v, [2 * B + 15, 0 * B + 0], B)
+    assert kp[2, 0, 15].tolist() == [0x3F80, 0xBF80] and vp[2, 0, :, 15].tolist() == [0x4040, 0x8000]
+    assert kp[0, 0, 0].tolist() == [0x4000, 0x0001] and vp[0, 0, :, 0].tolist() == [0x7F7F, 0xC000]
+    assert int((kp != nan_bits).sum()) == 4 and int((vp != nan_bits).sum()) == 4
+    O.append_kv(kp, vp, v[:1], k[:1], [2 * B + 15], B)
+    assert kp[2, 0, 15].tolist() == [0x4040, 0x8000] and vp[2, 0, :, 15].tolist() == [0x3F80, 0xBF80]
+    assert kp[2, 0, 14].tolist() == [nan_bits] * 2 and vp[2, 0, 0, 14] == nan_bits
+    assert int((kp != nan_bits).sum()) == 4 and int((vp != nan_bits).sum()) == 4
+
+
+def test_append_kv_framed_layout_and_quarter_turns():
+    # one channel pair at angular frequency pi/2 per position: frame index j turns a
+    # key by j quarter turns, (x, y) -> (-y, x) -> (-x, -y) -> (y, -x), values hand-derived;
+    # V is stored unrotated
+    B, Hkv, D, nb = 16, 2, 2, 4
+    kp, vp = _poisoned_pools(nb, Hkv, B, D)
+    k, v = _hand_kv(len(_APPEND_SLOTS), Hkv, D)
+    frames = [1, 2, 3, 0, 5]
+    O.append_kv_framed(kp, vp, k.astype(np.float32), v.astype(np.float32), [b * B + r for b, r in _APPEND_SLOTS],
+                       frames, B, np.array([math.pi / 2]), "f32")
+    turns = {0: lambda x, y: (x, y), 1: lambda x, y: (-y, x), 2: lambda x, y: (-x, -y), 3: lambda x, y: (y, -x)}
+    written_k = np.zeros(kp.shape, dtype=bool)
+    written_v = np.zeros(vp.shape, dtype=bool)
+    for i, (b, r) in enumerate(_APPEND_SLOTS):
+        for h in range(Hkv):
+            x, y = 1000.0 * i + 100.0 * h, 1000.0 * i + 100.0 * h + 1.0
+            ex = turns[frames[i] % 4](x, y)
+            assert abs(kp[b, h, r, 0] - ex[0]) <= 1e-9 * 1e4 and abs(kp[b, h, r, 1] - ex[1]) <= 1e-9 * 1e4
+            assert vp[b, h, 0, r] == -x - 0.5 and vp[b, h, 1, r] == -y - 0.5
+            written_k[b, h, r, :] = True
+            written_v[b, h, :, r] = True
+    assert np.isnan(kp[~written_k]).all() and np.isnan(vp[~written_v]).all()
+
+
 def test_bf16_conversion_exact():
     bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x3F81, 0x7F7F, 0x0001], dtype=np.uint16)
     want = [1.0, -1.0, 0.0, -0.0, 1.0 + 2.0 ** -7, (2 - 2.0 ** -7) * 2.0 ** 127, 2.0 ** -133]
