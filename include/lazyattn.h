@@ -200,7 +200,12 @@ int32_t lazyattn_decode_splits(const lazyattn_config* cfg, int32_t num_reqs, int
  * to the workspace: each part's output already divided by its own softmax
  * sum, as IEEE half, o [S][rows][Hq][D], then its reference and sum (m, l)
  * as fp32 [S][rows][Hq][2] (rows = total_q for prefill, num_reqs for
- * decode), S*rows*Hq*(2D + 8) bytes; the merge kernel then combines them.  The workspace needs no initialisation; calls that may run
+ * decode), S*rows*Hq*(2D + 8) bytes; the merge kernel then combines them.
+ * Range: each split's output is a convex combination of value rows, stored as
+ * IEEE half, so a call with S > 1 requires |v| <= 65504 for every value it
+ * reads (a larger value overflows its partial and the merged output is not
+ * finite); with S = 1 the output is written as bf16 directly and no such limit
+ * applies.  The workspace needs no initialisation; calls that may run
  * concurrently must not share one. */
 size_t lazyattn_prefill_workspace_size(const lazyattn_config* cfg, int32_t num_reqs, int32_t total_q,
                                        int32_t max_q_len, int32_t max_entries, int32_t num_splits);

@@ -16,6 +16,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblazyattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["lazyattn_kernels.hip", "lazyattn_host.cpp", "lazyattn_pool.cpp"]
+# peak probes for the benchmark (MFMA issue rate, HBM streaming read): a library of their own
+PROBE_LIB_PATH = os.path.join(PKG, "liblazyattn_probe.so")
+PROBE_SOURCES = ["lazyattn_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -27,14 +30,20 @@ def hipcc() -> str:
 
 
 def build(resource_usage: bool = False, verbose: bool = False) -> str:
-    out_tmp = LIB_PATH + ".tmp"
+    _build_one(SOURCES, LIB_PATH, resource_usage, verbose)
+    _build_one(PROBE_SOURCES, PROBE_LIB_PATH, False, verbose)
+    return LIB_PATH
+
+
+def _build_one(sources, lib_path, resource_usage, verbose) -> None:
+    out_tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed-FP32 instructions are kept out of generated code on this target
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", INCLUDE, "-I", CSRC]
     if resource_usage:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
-    cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out_tmp]
+    cmd += [os.path.join(CSRC, s) for s in sources] + ["-o", out_tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,8 +53,7 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{msgs}")
     if msgs.strip() and (verbose or resource_usage):
         print(msgs)
-    os.replace(out_tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(out_tmp, lib_path)
 
 
 if __name__ == "__main__":

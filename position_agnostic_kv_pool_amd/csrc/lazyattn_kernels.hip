@@ -172,8 +172,9 @@ __device__ __forceinline__ f32x4 mfma16x16x16(const s16x4& a, const s16x4& b, co
 // as long as 2^(s - m) stays finite; a row sum above 2^64 flags the rare case
 // where a later score outgrew m by that much, and the work-group then redoes
 // its rows with m set to the exact row maximum over all its keys (one QK-only
-// pass first).  ALiBi, whose bias grows toward the diagonal, always takes
-// that two-pass route.
+// pass first).  ALiBi, whose bias grows toward the diagonal, walks the key
+// tiles nearest-first, so the first tile's maximum is taken where the bias is
+// largest; it redoes only on the same out-of-range row sums.
 //
 // Staging.  Wave w stages rows 8 (w % 2) .. + 7 of entry w / 2 of the next
 // tile: lane l loads channel pair l of those 8 key rows (4 B each) and
@@ -181,7 +182,8 @@ __device__ __forceinline__ f32x4 mfma16x16x16(const s16x4& a, const s16x4& b, co
 // R(start - p0 + row) stepped by R(1) per row) between the QK products, and
 // writes K~ and V into the other LDS buffer.  One barrier per tile.  Table words are fetched three tiles ahead
 // and decoded per wave with lane reads.  With the key range split, each
-// split writes unnormalised (o, m, l) and the merge kernel combines them.
+// split writes its output divided by its own row sum, as IEEE half (so split
+// calls need |V| <= 65504), and fp32 (m, l); the merge kernel combines them.
 // ---------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -750,7 +752,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
               make_uint2(pack_bf16x2(O[dt][nt][4 * qq] * inv, O[dt][nt][4 * qq + 1] * inv),
                          pack_bf16x2(O[dt][nt][4 * qq + 2] * inv, O[dt][nt][4 * qq + 3] * inv));
     } else {
-      // this split's unnormalised output, reference maximum and sum
+      // this split's output divided by its own sum (fp16), reference and sum
       const size_t prow = static_cast<size_t>(split) * A.total_q * Hq + rowoff;
       if (lt > 0.f) {
         const float inv = 1.0f / lt;

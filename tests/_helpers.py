@@ -38,9 +38,22 @@ def within(got, ref, dtype) -> bool:
     return bool(np.all(np.isfinite(got))) and mx <= tmax and mn <= tmean
 
 
+# every assert_parity call appends (case, dtype, elements, raw max |d|, max excess
+# over the rounding allowance, mean |d|, max |ref|); conftest writes them out
+PARITY_RECORDS = []
+
+
+def write_parity_records(path):
+    with open(path, "a") as f:
+        for r in PARITY_RECORDS:
+            f.write("%-58s %-4s n=%-9d raw_max=%.3e excess_max=%.3e mean=%.3e ref_absmax=%.3g\n" % r)
+
+
 def assert_parity(got, ref, dtype, what=""):
     mx, mn = diff_stats(got, ref, dtype)
     raw = float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)))) if np.size(got) else 0.0
+    amax = float(np.max(np.abs(np.asarray(ref, np.float64)))) if np.size(ref) else 0.0
+    PARITY_RECORDS.append((what[:58], dtype, int(np.size(got)), raw, mx, mn, amax))
     tmax, tmean = TOL[dtype]
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert mx <= tmax and mn <= tmean, (f"{what}: max |d| {raw:.3e} (beyond output rounding {mx:.3e}, bar {tmax}), "

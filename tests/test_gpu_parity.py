@@ -185,37 +185,86 @@ def test_parity_llama8b_decode():
             say(f"8B decode step {step}: max {mx:.2e} mean {mn:.2e}")
 
 
-def test_parity_llama70b_long_context():
-    say("70B 32k: one request, 2048-token chunk (sampled rows), decode steps 0 and 127 with split-K")
-    wl = W.build_workload(W.spec(4, requests=[1], n_decode=128))
+@pytest.mark.timeout(300)
+def test_parity_llama8b_decode_full_batch_as_benched():
+    # the decode launch the benchmark times: all 128 requests, the heuristic split
+    # count (one split: the attention kernel writes bf16 outputs directly, no merge);
+    # the oracle checks every 8th request at the first two steps and the last one
+    say("8B decode, full batch of 128 requests, heuristic splits, steps 0, 1, 255 (every 8th request)")
+    wl = W.build_workload(W.spec(3, n_decode=256))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    orc = OracleState(wl)
+    reqs = list(range(0, 128, 8))
+    before = wl.tokens_before_step(0)
+    staging.append_tokens(cfg, pools, before, s.dtype, DEV)
+    orc.append(before)
+    for step in (0, 1, 255):
+        if step == 255:
+            # every token of steps 2..254, then step 255's own
+            rest = wl.tokens_before_step(255)
+            prev = wl.tokens_before_step(2)
+            keep = ~np.isin(rest["slots"], prev["slots"])
+            rest = {k: v[keep] for k, v in rest.items()}
+            staging.append_tokens(cfg, pools, rest, s.dtype, DEV)
+            orc.append(rest)
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+        call = staging.DecodeCall(cfg, s, d, DEV)
+        assert len(d["ctx_lens"]) == 128 and call.splits == 1 and call.workspace is None
+        out = gpu_f64(call.run(pools))
+        ref = orc.decode(d, requests=reqs)
+        mx, mn = assert_parity(out[reqs], np.stack([ref[r] for r in reqs]), "bf16",
+                               f"8B decode 128 req splits=1 step {step}")
+        say(f"8B decode full batch step {step}: max {mx:.2e} mean {mn:.2e}")
+
+
+@pytest.mark.timeout(400)
+def test_parity_llama70b_all_requests_as_benched():
+    # the 70B launches the benchmark times: the 2048-token chunk of all 4 requests
+    # (sampled rows of each), then decode of all 4 requests at the heuristic split
+    # count, steps 0 and 127
+    say("70B 32k: 4 requests, chunk prefill (sampled rows of each), decode steps 0 and 127 at heuristic splits")
+    wl = W.build_workload(W.spec(4, n_decode=128))
     s = wl.spec
     cfg = staging.config_for(s)
     pb, got, pools = run_prefill(wl)
     orc = OracleState(wl)
     orc.append(pb)
-    rng = np.random.default_rng(0)
-    toks = sorted(set([0, 1, 31, 32, 33, 1023, 1024, 2046, 2047]) | set(rng.choice(2048, 12, replace=False).tolist()))
-    compare_prefill(wl, pb, got, orc, token_subset={0: toks}, label="70B chunk prefill")
-    hist = wl.tokens_before_step(127)
-    # decode step 0 first, then jump to step 127
+    rng = np.random.default_rng(7)
+    # request 0: rows at and around the 32-position tile boundaries; the others sampled
+    subset = {0: np.array(sorted(set([0, 1, 31, 32, 33, 1023, 1024, 2046, 2047]) |
+                                 set(rng.choice(2048, 6, replace=False).tolist())))}
+    subset.update({r: sample_tokens(2048, 6, rng) for r in range(1, 4)})
+    compare_prefill(wl, pb, got, orc, token_subset=subset, label="70B chunk prefill, 4 requests")
     d0 = wl.decode_step(0)
     staging.append_tokens(cfg, pools, d0, s.dtype, DEV)
     orc.append(d0)
-    for splits in (0, 1, 7, 64):
+    ref0 = orc.decode(d0)
+    for splits in (1, 7, 64):
         out = gpu_f64(staging.DecodeCall(cfg, s, d0, DEV, num_splits=splits).run(pools))
-        ref = orc.decode(d0)
-        mx, mn = assert_parity(out, ref[0][None], "bf16", f"70B decode step 0 splits={splits}")
+        mx, mn = assert_parity(out, np.stack([ref0[r] for r in range(4)]), "bf16",
+                               f"70B decode 4 req splits={splits} step 0")
         say(f"70B decode step 0 splits={splits}: max {mx:.2e} mean {mn:.2e}")
-    rest = {k: v[pb["slots"].size + 1:] for k, v in hist.items()}
-    staging.append_tokens(cfg, pools, rest, s.dtype, DEV)
-    orc.append(rest)
-    d = wl.decode_step(127)
-    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
-    orc.append(d)
-    out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
-    ref = orc.decode(d)
-    mx, mn = assert_parity(out, ref[0][None], "bf16", "70B decode step 127")
-    say(f"70B decode step 127: max {mx:.2e} mean {mn:.2e}")
+    for step, d in ((0, d0), (127, None)):
+        if d is None:
+            rest = wl.tokens_before_step(127)
+            keep = ~np.isin(rest["slots"], wl.tokens_before_step(1)["slots"])
+            rest = {k: v[keep] for k, v in rest.items()}
+            staging.append_tokens(cfg, pools, rest, s.dtype, DEV)
+            orc.append(rest)
+            d = wl.decode_step(127)
+            staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+            orc.append(d)
+        call = staging.DecodeCall(cfg, s, d, DEV)
+        assert call.splits == _abi.decode_splits(cfg, 4, call.tables.batch.max_entries) and call.splits > 1
+        out = gpu_f64(call.run(pools))
+        ref = ref0 if step == 0 else orc.decode(d)
+        mx, mn = assert_parity(out, np.stack([ref[r] for r in range(4)]), "bf16",
+                               f"70B decode 4 req splits={call.splits} step {step}")
+        say(f"70B decode 4 requests step {step} splits {call.splits}: max {mx:.2e} mean {mn:.2e}")
 
 
 @pytest.mark.parametrize("skew", W.CFG5_SKEWS)
@@ -1082,3 +1131,40 @@ def test_attend_then_merge_equals_single_call():
     two.attend(pools2)
     two.merge()
     assert np.array_equal(a, gpu_f64(two.out))
+
+
+def test_split_partials_hold_large_values_within_half_range():
+    # split partials are stored as IEEE half: values up to |v| <= 65504 must come
+    # through a split call intact.  V scaled by 2^13 (exact in bf16; |v| up to ~4e4):
+    # the output scales by exactly 2^13, so it is checked against the unscaled oracle
+    say("large |V| (x 2^13) through split prefill and decode: splits 1 vs several vs the oracle")
+    wl = W.build_workload(W.spec(2, requests=[2], n_decode=1))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    pb = wl.prefill_batch()
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    orc = OracleState(wl)
+    orc.append(pb)
+    ref = orc.prefill(pb)
+    pools.v.mul_(8192.0)
+    vmax = float(torch.nan_to_num(pools.v.float(), nan=0.0).abs().max())
+    assert 8192.0 < vmax <= 65504.0
+    outs = {}
+    for k in (1, 5):
+        outs[k] = gpu_f64(staging.PrefillCall(cfg, s, pb, DEV, num_splits=k).run(pools)) / 8192.0
+        cu = pb["cu_q_lens"]
+        assert_parity(outs[k], np.concatenate([ref[r] for r in range(2)]), "bf16", f"large-V prefill splits={k}")
+    mx, mn = diff_stats(outs[5], outs[1])
+    assert mx <= 4e-3 and mn <= 2e-4
+    d = wl.decode_step(0)
+    dk = {key: d[key] for key in ("k_new", "v_new", "slots")}
+    orc.append(dk)
+    ref_d = orc.decode(d)
+    staging.append_tokens(cfg, pools, {"k_new": d["k_new"], "v_new": d["v_new"], "slots": d["slots"]}, s.dtype, DEV)
+    # the new token's value row is appended unscaled; scale that slot too
+    slots = torch.from_numpy(d["slots"]).to(DEV)
+    pools.v[slots // 16, :, :, slots % 16] *= 8192.0
+    for k in (1, 7):
+        out = gpu_f64(staging.DecodeCall(cfg, s, d, DEV, num_splits=k).run(pools)) / 8192.0
+        assert_parity(out, np.stack([ref_d[r] for r in range(2)]), "bf16", f"large-V decode splits={k}")
