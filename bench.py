@@ -1,18 +1,24 @@
 #!/usr/bin/env python3
 """Benchmark of deferred-RoPE attention over a position-agnostic paged KV pool on one MI355X.
 
-Workload (one step = one prefill launch over the whole batch): the
-Llama-3.1-8B attention-layer shape in bf16 (32 query heads, 8 KV heads,
-head_dim 128, RoPE theta 5e5, blocks of 16 tokens); 16 requests, each 8
-distinct documents of 512 tokens drawn Zipf(1.0) from a pool of 256
-documents and placed in random order (4096 context tokens), followed by a
-64-token query prefilled causally.  Inputs are seeded synthetic data already
-resident in HBM.  The new tokens' K/V are appended once before timing.
+Headline (one step = the prefill of a 2048-token chunk for each of 4
+requests): the Llama-3.1-70B single-layer attention shape in bf16 (64 query
+heads, 8 KV heads, head_dim 128, RoPE theta 5e5, blocks of 16 tokens).  Each
+request holds 64 distinct documents of 512 tokens drawn Zipf(1.0) from a pool
+of 4096 and placed in random order (32768 context tokens); its 2048 new
+tokens at positions 32768..34815 are prefilled causally over them.  The pool
+holds content-only K/V; RoPE is applied inside the kernel.  Inputs are seeded
+synthetic data already resident in HBM; the chunk's K/V are appended once
+before timing.  Every timed step runs cold: a 512 MiB write evicts the
+last-level cache before it, outside the step's own events.
 
-Also reported on the same line: the same launch with rotation disabled
-(deferred-RoPE overhead), decode on the Llama-3.1-8B decode shape (128
-requests x 8 Zipf(1.2) documents, per-step HBM bytes), and the fp64 CPU
-oracle on the same prefill batch.
+Also on the same line: the rotation-free control on the same inputs (the
+deferred-RoPE overhead); the 128 decode steps that follow the chunk (split-K,
+cold and warm, HBM roofline on unique bytes with the counter bytes beside
+them); the Llama-3.1-8B prefill and decode shapes and the MQA stress mixed
+step (32 prefills and 96 decodes on two streams) as extras; measured MFMA and
+HBM peaks; block-pool hit ratios; and the fp64 CPU oracle timed on a stated
+sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
   python bench.py --calibrate-copy           # a plain copy kernel, for counter scaling
@@ -21,6 +27,7 @@ oracle on the same prefill batch.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import glob
 import hashlib
 import json
@@ -34,9 +41,19 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill TFLOP/s + decode KV GB/s (% of MI355X peak), deferred-RoPE attention"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+FLUSH_BYTES = 512 << 20        # twice the 256 MiB last-level (MALL) cache
 KERNEL_SRC = os.path.join(ROOT, "position_agnostic_kv_pool_amd", "csrc", "lazyattn_kernels.hip")
-PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_bf16_llama8b_counters.txt")
-DECODE_COUNTERS = os.path.join(ROOT, "profiles", "decode_bf16_llama8b_counters.txt")
+PROBE_LIB = os.path.join(ROOT, "position_agnostic_kv_pool_amd", "liblazyattn_probe.so")
+COUNTERS = {
+    "prefill70b": os.path.join(ROOT, "profiles", "prefill_bf16_llama70b_counters.txt"),
+    "decode70b": os.path.join(ROOT, "profiles", "decode_bf16_llama70b_counters.txt"),
+    "prefill8b": os.path.join(ROOT, "profiles", "prefill_bf16_llama8b_counters.txt"),
+    "decode8b": os.path.join(ROOT, "profiles", "decode_bf16_llama8b_counters.txt"),
+}
+HEADLINE_WORKLOAD = ("prefill, Llama-3.1-70B attention layer (Hq 64, Hkv 8, d 128, RoPE theta 5e5, block 16): "
+                     "2048-token causal chunk of each of 4 requests over 64 Zipf(1.0) documents x 512 tokens "
+                     "(32k context); content-only pool, RoPE applied in-kernel; cold (last-level cache "
+                     "flushed before each step)")
 
 
 def kernel_source_hash() -> str:
@@ -45,8 +62,8 @@ def kernel_source_hash() -> str:
 
 
 def read_counter_summary(path: str):
-    """(bytes per dispatch from FETCH_SIZE + WRITE_SIZE scaled by the copy calibration) if the
-    summary was taken on the current kernel source, else None."""
+    """HBM bytes per dispatch (FETCH_SIZE + WRITE_SIZE, each scaled by the copy calibration)
+    from a committed summary, if it was taken on the current kernel source; else None."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -79,6 +96,21 @@ def summarize_rocprof(d: str) -> None:
             name = r.get("Name", r.get("KernelName", "?"))
             print(f"{name[:90]:90s} calls {r.get('Calls')}  avg_ns {float(r.get('AverageNs', 0)):.0f}  "
                   f"min_ns {r.get('MinNs')}  max_ns {r.get('MaxNs')}  pct {float(r.get('Percentage', 0)):.2f}")
+    for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        # per-kernel median dispatch duration (the stats file gives only the mean)
+        by = defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name", r.get("Kernel-Name", "?"))
+                try:
+                    by[name].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                except (KeyError, ValueError):
+                    pass
+        print(f"# kernel trace medians: {os.path.relpath(path, d)}")
+        for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+            v = sorted(v)
+            print(f"{name[:90]:90s} dispatches {len(v)}  median_ns {v[len(v) // 2]}  p10_ns {v[len(v) // 10]}  "
+                  f"p90_ns {v[(9 * len(v)) // 10]}")
     for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         print(f"# counters: {os.path.relpath(path, d)}")
         acc = defaultdict(list)
@@ -91,22 +123,26 @@ def summarize_rocprof(d: str) -> None:
 
 
 # ---------------------------------------------------------------------------
-# workloads
+# algorithmic work
 # ---------------------------------------------------------------------------
-def prefill_flops(pb, head_dim: int, num_q_heads: int) -> float:
+def prefill_flops(pb, head_dim: int, num_q_heads: int, token_subset=None) -> float:
     """4 * D * Hq * sum over queries of the keys each one sees (QK^T and PV, causal)."""
     tot = 0
     cu = pb["cu_q_lens"]
     for r, L in enumerate(pb["ctx_lens"]):
         m = int(cu[r + 1] - cu[r])
         p0 = int(L) - m
-        tot += m * p0 + m * (m + 1) // 2        # sum_{j<m} (p0 + j + 1)
+        if token_subset is None:
+            tot += m * p0 + m * (m + 1) // 2        # sum_{j<m} (p0 + j + 1)
+        elif r in token_subset:
+            tot += sum(p0 + int(j) + 1 for j in token_subset[r])
     return 4.0 * head_dim * num_q_heads * tot
 
 
 def decode_bytes(d, wl) -> dict:
     """Per-step bytes: logical (what a per-request paged kernel streams), unique (each
-    (block, KV head) once), plus queries, outputs and table words."""
+    (block, KV head) once: the HBM floor when shared blocks are read once), plus queries,
+    outputs and table words."""
     s = wl.spec
     esz = 2 if s.dtype == "bf16" else 4
     R = len(d["ctx_lens"])
@@ -120,11 +156,22 @@ def decode_bytes(d, wl) -> dict:
     return {"logical": kv_logical + other, "unique": kv_unique + other, "kv_logical": kv_logical}
 
 
+def med(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def pct(v):
+    v = sorted(v)
+    return [v[len(v) // 10], v[len(v) // 2], v[(9 * len(v)) // 10]]
+
+
 class Timer:
     """HIP events on the stream the kernels are launched on (torch's current stream)."""
 
     def __init__(self, torch):
         self.torch = torch
+        self.flush_buf = None
 
     def busy(self):
         # keep the GPU busy while the host enqueues the timed launches, so host
@@ -132,7 +179,16 @@ class Timer:
         if hasattr(self.torch.cuda, "_sleep"):
             self.torch.cuda._sleep(2_000_000)
 
+    def flush(self, rep=0):
+        if self.flush_buf is None:
+            self.flush_buf = self.torch.empty(FLUSH_BYTES, dtype=self.torch.uint8, device="cuda")
+        self.flush_buf.fill_(rep & 0xff)
+
+    def release(self):
+        self.flush_buf = None
+
     def span(self, fn, n):
+        """ms per call of n back-to-back calls between two events."""
         t = self.torch
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         t.cuda.synchronize()
@@ -144,37 +200,157 @@ class Timer:
         t.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    def launches(self, fn, n):
-        """Per-launch times (ms) of n back-to-back launches, each bracketed by its own events."""
+    def steps(self, fns, n, cold=True, arg=False):
+        """n steps; step i runs fns[0](i), fns[1](i), ... (or without the index), each
+        between its own events; with ``cold`` the last-level cache is flushed before every
+        step, outside its events.  Returns per-step lists of per-function ms."""
         t = self.torch
-        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
+        ev = [[t.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n)]
         t.cuda.synchronize()
         self.busy()
-        for a, b in ev:
-            a.record()
-            fn()
-            b.record()
+        for i in range(n):
+            if cold:
+                self.flush(i)
+            ev[i][0].record()
+            for j, fn in enumerate(fns):
+                fn(i) if arg else fn()
+                ev[i][j + 1].record()
         t.cuda.synchronize()
-        return sorted(a.elapsed_time(b) for a, b in ev)
-
-    def steps(self, attend, merge, n):
-        """n steps of [attention kernel, merge kernel]: (ms per step, ms per attention launch)."""
-        t = self.torch
-        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
-        end = t.cuda.Event(enable_timing=True)
-        t.cuda.synchronize()
-        self.busy()
-        for a, b in ev:
-            a.record()
-            attend()
-            b.record()
-            merge()
-        end.record()
-        t.cuda.synchronize()
-        return ev[0][0].elapsed_time(end) / n, sum(a.elapsed_time(b) for a, b in ev) / n
+        return [[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(fns))] for i in range(n)]
 
 
-def bench_prefill(torch, args, W, staging, _abi):
+# ---------------------------------------------------------------------------
+# the headline: Llama-3.1-70B 32k chunk prefill, then its decode steps
+# ---------------------------------------------------------------------------
+def bench_headline(torch, args, W, staging, _abi):
+    wl = W.build_workload(W.spec(4, n_decode=args.decode_steps))
+    s = wl.spec
+    pools = staging.DevicePools(wl, "cuda")
+    pb = wl.prefill_batch()
+    cfg = staging.config_for(s)
+    cfg_none = staging.config_for(s, pe="none")
+    staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
+    call = staging.PrefillCall(cfg, s, pb, "cuda")
+    call_none = staging.PrefillCall(cfg_none, s, pb, "cuda")
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    fns = [lambda: call.attend(pools)] + ([call.merge] if call.splits > 1 else [])
+    fns_none = [lambda: call_none.attend(pools)] + ([call_none.merge] if call_none.splits > 1 else [])
+    for _ in range(args.warmup):
+        call.run(pools)
+    torch.cuda.synchronize()
+    # the timed steps: exactly args.steps cold steps
+    st = timer.steps(fns, args.steps, cold=True)
+    step_ms = [sum(x) for x in st]
+    kern_ms = [x[0] for x in st]
+    print(f"# headline prefill: {sum(step_ms) / len(step_ms) * 1e3:.1f} us/step (cold)", file=sys.stderr, flush=True)
+    st_none = timer.steps(fns_none, max(5, args.steps // 2), cold=True)
+    warm = timer.span(lambda: call.run(pools), max(5, args.steps // 2))
+    warm_none = timer.span(lambda: call_none.run(pools), max(5, args.steps // 2))
+    flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
+    pre = dict(ms=sum(step_ms) / len(step_ms), step_ms=step_ms, kern_ms=kern_ms, flops=flops, splits=call.splits,
+               none_kern_ms=[x[0] for x in st_none], warm_ms=warm, warm_none_ms=warm_none,
+               seq_len=int(max(pb["ctx_lens"])), R=len(pb["ctx_lens"]))
+    del call, call_none
+
+    # decode steps 0..n-1: every step's token is appended first (setup); a step's call
+    # reads only its own context (ctx_lens, num_entries), so later tokens are invisible to it
+    n = args.decode_steps
+    allt = wl.tokens_before_step(n)
+    staging.append_tokens(cfg, pools, allt, s.dtype, "cuda")
+    steps = [wl.decode_step(i) for i in range(n)]
+    calls = [staging.DecodeCall(cfg, s, d, "cuda") for d in steps]
+    calls_none = [staging.DecodeCall(cfg_none, s, d, "cuda") for d in steps]
+    by = [decode_bytes(d, wl) for d in steps]
+    torch.cuda.synchronize()
+    for c in calls[:3]:
+        c.run(pools)
+    dec = {}
+    for tag, cs in (("rope", calls), ("none", calls_none)):
+        fns = [lambda i, cs=cs: cs[i].attend(pools), lambda i, cs=cs: cs[i].merge()]
+        cold = timer.steps(fns, n, cold=True, arg=True)
+        warm = timer.steps([lambda i, cs=cs: (cs[i].run(pools), cs[i].run(pools), cs[i].run(pools))], n,
+                           cold=False, arg=True)
+        dec[tag] = dict(cold_att=[x[0] for x in cold], cold_merge=[x[1] for x in cold],
+                        warm_step=[x[0] / 3.0 for x in warm])
+    print(f"# headline decode: {sum(dec['rope']['cold_att']) / n * 1e3:.1f} us attention per step (cold)",
+          file=sys.stderr, flush=True)
+    timer.release()
+    out = dict(pre=pre, dec=dec, bytes=by, splits=calls[0].splits, n=n, wl=wl, pb=pb, steps=steps)
+    del calls, calls_none, pools
+    torch.cuda.empty_cache()
+    return out
+
+
+def headline_json(h, args):
+    pre, dec, by, n = h["pre"], h["dec"], h["bytes"], h["n"]
+    flops = pre["flops"]
+    tflops = flops / (pre["ms"] * 1e-3) / 1e12
+    k_med = med(pre["kern_ms"])
+    kernel_tflops = flops / (k_med * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_counter_summary(COUNTERS["prefill70b"]),
+                "kernel": "prefill_bf16_kernel<ROPE>", "flops_per_launch": flops,
+                "launch_us_median_cold": round(k_med * 1e3, 2),
+                "launch_us_p10_p50_p90_cold": [round(x * 1e3, 2) for x in pct(pre["kern_ms"])],
+                "launch_us_warm_back_to_back": round(pre["warm_ms"] * 1e3, 2),
+                "note": "achieved = algorithmic FLOPs / median cold launch (the kernel's own events)"}
+    none_med = med(pre["none_kern_ms"])
+    rope_overhead = {"prefill_rope_us_cold": round(k_med * 1e3, 2), "prefill_norotation_us_cold": round(none_med * 1e3, 2),
+                     "prefill_overhead_cold": round(k_med / none_med - 1.0, 4),
+                     "prefill_rope_us_warm": round(pre["warm_ms"] * 1e3, 2),
+                     "prefill_norotation_us_warm": round(pre["warm_none_ms"] * 1e3, 2),
+                     "prefill_overhead_warm": round(pre["warm_ms"] / pre["warm_none_ms"] - 1.0, 4),
+                     # rotation work: 3 flops per rotated key element, each key tile rotated once per
+                     # work-group of 256 query rows (the pages' 3/(4M) cost model with M = 256)
+                     "prefill_rotation_flop_fraction": round(3.0 / (4.0 * 256), 5)}
+    r, z = dec["rope"], dec["none"]
+    att = sum(r["cold_att"]) / n
+    mrg = sum(r["cold_merge"]) / n
+    uniq = sum(b["unique"] for b in by) / n
+    logical = sum(b["logical"] for b in by) / n
+    traffic = read_counter_summary(COUNTERS["decode70b"])
+    gbs_unique = uniq / (att * 1e-3) / 1e9
+    decode = {
+        "workload": f"decode steps 0..{n - 1} after the chunk: 4 requests x 34817..{34816 + n} tokens, split-K "
+                    f"({h['splits']} splits) + merge; cold (cache flushed before each step)",
+        "us_per_step_cold": round((att + mrg) * 1e3, 2), "attention_kernel_us_cold": round(att * 1e3, 2),
+        "merge_kernel_us_cold": round(mrg * 1e3, 2),
+        "us_per_step_warm": round(sum(r["warm_step"]) / n * 1e3, 2),
+        "tokens_per_s_cold": round(h["pre"]["R"] / ((att + mrg) * 1e-3), 1),
+        "splits": h["splits"],
+        "roofline": {"bound": "hbm", "achieved": round(gbs_unique, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs_unique / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_bf16_kernel<ROPE,1>",
+                     "bytes_per_launch_unique": round(uniq),
+                     "counter_GBps": round(traffic / (att * 1e-3) / 1e9, 1) if traffic else None,
+                     "bytes_per_launch_logical": round(logical),
+                     "logical_GBps_context": round(logical / (att * 1e-3) / 1e9, 1),
+                     "note": "achieved = unique bytes (each block and KV head once, plus q, out, table words) / "
+                             "mean cold attention-kernel time; logical bytes re-count shared blocks"},
+        "norotation_attention_us_cold": round(sum(z["cold_att"]) / n * 1e3, 2),
+        "rope_overhead_cold": round(att / (sum(z["cold_att"]) / n) - 1.0, 4),
+        "rope_overhead_warm": round(sum(r["warm_step"]) / sum(z["warm_step"]) - 1.0, 4),
+    }
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": HEADLINE_WORKLOAD, "global_batch": pre["R"], "seq_len": pre["seq_len"],
+                   "parallelism": "single-gpu", "key_splits": pre["splits"],
+                   "step": "one prefill call (attention kernel; the merge too when the key range is split)"},
+        "roofline": roofline,
+        "rope_overhead": rope_overhead,
+        "decode": decode,
+    }
+    return out
+
+
+# ---------------------------------------------------------------------------
+# extras: the Llama-3.1-8B prefill and decode shapes
+# ---------------------------------------------------------------------------
+def bench_llama8b_prefill(torch, args, W, staging, _abi):
     wl = W.build_workload(W.spec(2))
     s = wl.spec
     pools = staging.DevicePools(wl, "cuda")
@@ -182,133 +358,272 @@ def bench_prefill(torch, args, W, staging, _abi):
     cfg = staging.config_for(s)
     staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
     call = staging.PrefillCall(cfg, s, pb, "cuda")
-    cfg_none = staging.config_for(s, pe="none")
-    call_none = staging.PrefillCall(cfg_none, s, pb, "cuda")
-    # the same batch over a pool in document-local frames
+    call_none = staging.PrefillCall(staging.config_for(s, pe="none"), s, pb, "cuda")
     fpools = staging.FramedPools(wl, cfg, "cuda")
     staging.append_tokens(cfg, fpools, pb, s.dtype, "cuda")
     call_framed = staging.PrefillCall(cfg, s, pb, "cuda", framed=True)
-    # and over an FP8 pool
     cfg8 = staging.config_for(s, kv_format="fp8")
     pools8 = staging.WrittenPools(wl, cfg8, "cuda")
     staging.append_tokens(cfg8, pools8, pb, s.dtype, "cuda")
     call8 = staging.PrefillCall(cfg8, s, pb, "cuda")
     torch.cuda.synchronize()
     timer = Timer(torch)
-    for _ in range(args.warmup):
+    for _ in range(5):
         call.run(pools)
-    # clocks and caches settle over ~20 ms of untimed launches before anything is timed
-    timer.span(lambda: call.attend(pools), 200)
-    # the timed steps: exactly args.steps steps (attention kernel, then the split merge),
-    # back-to-back between two events
-    ms = timer.span(lambda: call.run(pools), args.steps)
-    # the attention kernel alone and its rotation-free control, three interleaved rounds (medians)
-    att, att_none, step_none, att_framed, att_fp8 = [], [], [], [], []
-    call_framed.run(fpools)
-    call8.run(pools8)
-    for _ in range(3):
-        att.append(timer.span(lambda: call.attend(pools), args.steps))
-        att_none.append(timer.span(lambda: call_none.attend(pools), args.steps))
-        step_none.append(timer.span(lambda: call_none.run(pools), args.steps))
-        att_framed.append(timer.span(lambda: call_framed.attend(fpools), args.steps))
-        att_fp8.append(timer.span(lambda: call8.attend(pools8), args.steps))
+    timer.span(lambda: call.attend(pools), 200)        # clocks settle
+    n = 20
+    res = {}
+    for tag, c, p in (("rope", call, pools), ("none", call_none, pools), ("framed", call_framed, fpools),
+                      ("fp8", call8, pools8)):
+        fns = [lambda c=c, p=p: c.attend(p)] + ([c.merge] if c.splits > 1 else [])
+        cold = timer.steps(fns, n, cold=True)
+        res[tag] = dict(cold_att=med([x[0] for x in cold]), cold_step=med([sum(x) for x in cold]),
+                        warm_att=med([timer.span(lambda c=c, p=p: c.attend(p), n) for _ in range(3)]),
+                        warm_step=med([timer.span(lambda c=c, p=p: c.run(p), n) for _ in range(3)]))
     del fpools, pools8
-    # cold: the last-level cache flushed by a 512 MB write before each single launch
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold, cold_none = [], []
-    for rep in range(5):
-        for fn, acc in ((call.attend, cold), (call_none.attend, cold_none)):
-            flush.fill_(rep & 0xff)
-            acc.append(timer.span(lambda: fn(pools), 1))
-    del flush
-    med = lambda v: sorted(v)[len(v) // 2]
-    # distribution of single attention launches (50, each between its own events)
-    per = timer.launches(lambda: call.attend(pools), 50)
-    pct = {"p10": per[len(per) // 10], "p50": per[len(per) // 2], "p90": per[(9 * len(per)) // 10]}
-    # materialise-then-attend baseline on the same batch: private rotated copies of every
-    # request's blocks, rotated queries, then the rotation-free kernel over the copy
     mat = staging.MaterializedPrefill(s, pb, "cuda")
     mat.run(pools)
-    base = dict(materialize=timer.span(lambda: mat.materialize(pools), args.steps),
-                rotate_queries=timer.span(lambda: mat.rotate_queries(), args.steps),
-                attention=timer.span(lambda: mat.attend(), args.steps),
-                total=timer.span(lambda: mat.run(pools), args.steps), copied_bytes=mat.bytes_copied)
+    base = dict(materialize=timer.span(lambda: mat.materialize(pools), n),
+                rotate_queries=timer.span(lambda: mat.rotate_queries(), n),
+                attention=timer.span(lambda: mat.attend(), n),
+                total=timer.span(lambda: mat.run(pools), n), copied_bytes=mat.bytes_copied)
     del mat
+    timer.release()
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
-    return dict(wl=wl, pb=pb, ms=ms, ms_attend=med(att), ms_none=med(step_none), ms_none_attend=med(att_none),
-                att=att, att_none=att_none, att_framed=att_framed, ms_framed_attend=med(att_framed),
-                ms_fp8_attend=med(att_fp8), pct=pct, cold=med(cold), cold_none=med(cold_none), flops=flops, base=base,
-                splits=call.splits, pools=pools)
+    r = res["rope"]
+    traffic = read_counter_summary(COUNTERS["prefill8b"])
+    out = {
+        "workload": "prefill, Llama-3.1-8B attention layer (Hq 32, Hkv 8, d 128, RoPE theta 5e5, block 16): "
+                    "16 requests x 8 Zipf(1.0) documents x 512 tokens + 64-token causal query",
+        "key_splits": call.splits,
+        "step_us_cold": round(r["cold_step"] * 1e3, 2), "attention_us_cold": round(r["cold_att"] * 1e3, 2),
+        "step_us_warm": round(r["warm_step"] * 1e3, 2), "attention_us_warm": round(r["warm_att"] * 1e3, 2),
+        "TFLOPs_step_cold": round(flops / (r["cold_step"] * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (r["cold_att"] * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (r["cold_att"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "flops_per_launch": flops},
+        "rope_overhead_cold": round(r["cold_att"] / res["none"]["cold_att"] - 1.0, 4),
+        "rope_overhead_warm": round(r["warm_att"] / res["none"]["warm_att"] - 1.0, 4),
+        "norotation_attention_us_cold": round(res["none"]["cold_att"] * 1e3, 2),
+        "document_frames": {"attention_us_cold": round(res["framed"]["cold_att"] * 1e3, 2),
+                            "overhead_vs_norotation_cold": round(res["framed"]["cold_att"] /
+                                                                 res["none"]["cold_att"] - 1.0, 4)},
+        "fp8_pool": {"attention_us_cold": round(res["fp8"]["cold_att"] * 1e3, 2),
+                     "vs_bf16_pool": round(r["cold_att"] / res["fp8"]["cold_att"], 3)},
+        "materialize_baseline": {
+            "what": "private copies of every request's blocks with K rotated at absolute positions, queries "
+                    "rotated, then the rotation-free kernel over the copy (the approach deferred RoPE replaces); warm",
+            "materialize_us": round(base["materialize"] * 1e3, 2),
+            "rotate_queries_us": round(base["rotate_queries"] * 1e3, 2),
+            "attention_us": round(base["attention"] * 1e3, 2), "total_us": round(base["total"] * 1e3, 2),
+            "copied_bytes": int(base["copied_bytes"]),
+            "deferred_step_us_warm": round(r["warm_step"] * 1e3, 2),
+            "deferred_speedup": round(base["total"] / r["warm_step"], 3)},
+    }
+    del pools
+    torch.cuda.empty_cache()
+    return out
 
 
-def bench_decode(torch, args, W, staging, _abi, n_steps: int, framed: bool = True):
-    """Decode steps 0..n_steps-1 of the 8B decode shape.  Each step's new token is appended
-    untimed; then 3 back-to-back launches of its attention kernel are timed (they re-read the same
-    step's pool, as the step itself would), with and without the merge, and rotation-free."""
+def bench_llama8b_decode(torch, args, W, staging, _abi, n_steps: int):
+    """Decode steps 0..n_steps-1 of the 8B decode shape, cold and warm (3 back-to-back
+    launches of the same step), with the rotation-free, framed and FP8 variants warm."""
     wl = W.build_workload(W.spec(3, n_decode=max(n_steps, 1)))
     s = wl.spec
     cfg = staging.config_for(s)
     cfg_none = staging.config_for(s, pe="none")
-    pools = staging.DevicePools(wl, "cuda")
-    staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, "cuda")
-    fpools = staging.FramedPools(wl, cfg, "cuda") if framed else None
-    if framed:
-        staging.append_tokens(cfg, fpools, wl.tokens_before_step(0), s.dtype, "cuda")
-    # the same steps over an FP8 pool (quantised by the library's append)
     cfg8 = staging.config_for(s, kv_format="fp8")
-    pools8 = staging.WrittenPools(wl, cfg8, "cuda") if framed else None
-    fpools8 = staging.FramedPools(wl, cfg8, "cuda") if framed else None
-    if framed:
-        staging.append_tokens(cfg8, pools8, wl.tokens_before_step(0), s.dtype, "cuda")
-        staging.append_tokens(cfg8, fpools8, wl.tokens_before_step(0), s.dtype, "cuda")
-    t = torch
-    tot_ms, tot_merge_ms, tot_ms_none, tot_bytes, tot_unique, tokens = 0.0, 0.0, 0.0, 0, 0, 0
-    tot_kv = 0
-    tot_ms_framed, tot_ms_fp8, tot_ms_fp8f = 0.0, 0.0, 0.0
-    for step in range(-2, n_steps):          # two untimed warm-up launches on step 0's inputs
+    allt = wl.tokens_before_step(n_steps)
+    pools = staging.DevicePools(wl, "cuda")
+    staging.append_tokens(cfg, pools, allt, s.dtype, "cuda")
+    fpools = staging.FramedPools(wl, cfg, "cuda")
+    staging.append_tokens(cfg, fpools, allt, s.dtype, "cuda")
+    pools8 = staging.WrittenPools(wl, cfg8, "cuda")
+    staging.append_tokens(cfg8, pools8, allt, s.dtype, "cuda")
+    fpools8 = staging.FramedPools(wl, cfg8, "cuda")
+    staging.append_tokens(cfg8, fpools8, allt, s.dtype, "cuda")
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    acc = {k: 0.0 for k in ("cold", "cold_none", "warm", "none", "framed", "fp8", "fp8f")}
+    tot = {"logical": 0, "unique": 0, "kv_logical": 0}
+    splits = 0
+    for step in range(-2, n_steps):          # two untimed warm-up rounds on step 0's inputs
         d = wl.decode_step(max(step, 0))
-        if step >= 0:
-            staging.append_tokens(cfg, pools, d, s.dtype, "cuda")
-            if framed:
-                staging.append_tokens(cfg, fpools, d, s.dtype, "cuda")
-                staging.append_tokens(cfg8, pools8, d, s.dtype, "cuda")
-                staging.append_tokens(cfg8, fpools8, d, s.dtype, "cuda")
         call = staging.DecodeCall(cfg, s, d, "cuda")
-        call_none = staging.DecodeCall(cfg_none, s, d, "cuda")
-        timer = Timer(t)
-        ms_att = timer.span(lambda: call.attend(pools), 3)
-        ms_step = timer.span(lambda: call.run(pools), 3)
-        ms_none = timer.span(lambda: call_none.attend(pools), 3)
-        ms_framed, ms_fp8, ms_fp8f = 0.0, 0.0, 0.0
-        if framed:
-            call_framed = staging.DecodeCall(cfg, s, d, "cuda", framed=True)
-            ms_framed = timer.span(lambda: call_framed.attend(fpools), 3)
-            call8 = staging.DecodeCall(cfg8, s, d, "cuda")
-            ms_fp8 = timer.span(lambda: call8.attend(pools8), 3)
-            call8f = staging.DecodeCall(cfg8, s, d, "cuda", framed=True)
-            ms_fp8f = timer.span(lambda: call8f.attend(fpools8), 3)
+        cn = staging.DecodeCall(cfg_none, s, d, "cuda")
+        cf = staging.DecodeCall(cfg, s, d, "cuda", framed=True)
+        c8 = staging.DecodeCall(cfg8, s, d, "cuda")
+        c8f = staging.DecodeCall(cfg8, s, d, "cuda", framed=True)
+        splits = call.splits
+        cold = timer.steps([lambda: call.run(pools)], 1, cold=True)[0][0]
+        cold_none = timer.steps([lambda: cn.run(pools)], 1, cold=True)[0][0]
+        t = dict(cold=cold, cold_none=cold_none, warm=timer.span(lambda: call.run(pools), 3),
+                 none=timer.span(lambda: cn.run(pools), 3), framed=timer.span(lambda: cf.run(fpools), 3),
+                 fp8=timer.span(lambda: c8.run(pools8), 3), fp8f=timer.span(lambda: c8f.run(fpools8), 3))
         if step < 0:
             continue
         if step % 64 == 63:
-            print(f"# decode step {step + 1}/{n_steps}", file=sys.stderr, flush=True)
-        tot_ms += ms_att
-        # with one split the step is the attention kernel alone (no merge is launched)
-        if call.splits > 1:
-            tot_merge_ms += max(ms_step - ms_att, 0.0)
-        tot_ms_none += ms_none
-        tot_ms_framed += ms_framed
-        tot_ms_fp8 += ms_fp8
-        tot_ms_fp8f += ms_fp8f
-        by = decode_bytes(d, wl)
-        tot_bytes += by["logical"]
-        tot_kv += by["kv_logical"]
-        tot_unique += by["unique"]
-        tokens += len(d["ctx_lens"])
+            print(f"# 8B decode step {step + 1}/{n_steps}", file=sys.stderr, flush=True)
+        for k in acc:
+            acc[k] += t[k]
+        b = decode_bytes(d, wl)
+        for k in tot:
+            tot[k] += b[k]
+    timer.release()
     n = max(n_steps, 1)
-    return dict(ms=tot_ms / n, merge_ms=tot_merge_ms / n, ms_none=tot_ms_none / n, ms_framed=tot_ms_framed / n,
-                ms_fp8=tot_ms_fp8 / n, ms_fp8f=tot_ms_fp8f / n, bytes=tot_bytes / n, kv_bytes=tot_kv / n,
-                unique=tot_unique / n,
-                tokens=tokens, splits=_abi.decode_splits(cfg, len(wl.requests), wl.table_arrays(wl.requests)[0].shape[1]))
+    a = {k: v / n for k, v in acc.items()}
+    b = {k: v / n for k, v in tot.items()}
+    traffic = read_counter_summary(COUNTERS["decode8b"])
+    kv_unique = b["unique"]
+    out = {
+        "workload": "decode, Llama-3.1-8B shape: 128 requests x 8 Zipf(1.2) documents x 512 tokens "
+                    "+ 32-token suffix, steps 0..%d" % (n_steps - 1),
+        "splits": splits,
+        "us_per_step_cold": round(a["cold"] * 1e3, 2), "us_per_step_warm": round(a["warm"] * 1e3, 2),
+        "tokens_per_s_cold": round(128 / (a["cold"] * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(kv_unique / (a["cold"] * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(kv_unique / (a["cold"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "counter_GBps": round(traffic / (a["cold"] * 1e-3) / 1e9, 1) if traffic else None,
+                     "bytes_per_launch_unique": round(kv_unique),
+                     "bytes_per_launch_logical": round(b["logical"]),
+                     "logical_GBps_context": round(b["logical"] / (a["cold"] * 1e-3) / 1e9, 1),
+                     "note": "achieved = unique bytes / cold step time"},
+        "norotation_us_per_step_cold": round(a["cold_none"] * 1e3, 2),
+        "rope_overhead_cold": round(a["cold"] / a["cold_none"] - 1.0, 4),
+        "rope_overhead_warm": round(a["warm"] / a["none"] - 1.0, 4),
+        "document_frames_us_warm": round(a["framed"] * 1e3, 2),
+        "document_frames_overhead_warm": round(a["framed"] / a["none"] - 1.0, 4),
+        "fp8_pool_us_warm": round(a["fp8"] * 1e3, 2),
+        "fp8_framed_pool_us_warm": round(a["fp8f"] * 1e3, 2),
+    }
+    del pools, fpools, pools8, fpools8
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# extras: the MQA stress mixed step (32 prefills + 96 decodes on two streams)
+# ---------------------------------------------------------------------------
+def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
+    timer = Timer(torch)
+    out = {"what": "MQA stress (Hq 32, Hkv 1): 32 prefill requests (128-token queries) and 96 decode requests, "
+                   "4..32 lognormal documents each; one mixed step = the prefill call on one stream and the decode "
+                   "call on another, started together; times are medians of 3 x 10 warm steps; skew 0.0 = uniform "
+                   "access, the no-reuse control"}
+    main = torch.cuda.current_stream()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()     # default priority
+
+    def mixed(pc, dc, pools):
+        start = torch.cuda.Event()
+        start.record(main)
+        sa.wait_event(start)
+        sb.wait_event(start)
+        pc.run(pools, stream=sa)
+        dc.run(pools, stream=sb)
+        ea, eb = torch.cuda.Event(), torch.cuda.Event()
+        ea.record(sa)
+        eb.record(sb)
+        main.wait_event(ea)
+        main.wait_event(eb)
+
+    for skew in W.CFG5_SKEWS:
+        wl = W.build_workload(W.spec(5, skew=skew))
+        s = wl.spec
+        pools = staging.DevicePools(wl, "cuda")
+        pb = wl.prefill_batch()
+        cfg = staging.config_for(s)
+        staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
+        staging.append_tokens(cfg, pools, wl.tokens_before_step(1), s.dtype, "cuda")
+        d = wl.decode_step(0)
+        flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
+        by = decode_bytes(d, wl)
+        row = {}
+        for pe in ("rope", "alibi", "none"):
+            c = staging.config_for(s, pe=pe)
+            pc = staging.PrefillCall(c, s, pb, "cuda")
+            dc = staging.DecodeCall(c, s, d, "cuda")
+            pc.run(pools)
+            dc.run(pools)
+            mixed(pc, dc, pools)
+            tp = med([timer.span(lambda: pc.run(pools), 10) for _ in range(3)])
+            td = med([timer.span(lambda: dc.run(pools), 10) for _ in range(3)])
+            tm = med([timer.span(lambda: mixed(pc, dc, pools), 10) for _ in range(3)])
+            row[pe] = {"prefill_us": round(tp * 1e3, 2), "prefill_TFLOPs": round(flops / (tp * 1e-3) / 1e12, 1),
+                       "decode_us": round(td * 1e3, 2),
+                       "decode_GBps_unique": round(by["unique"] / (td * 1e-3) / 1e9, 1),
+                       "decode_GBps_logical": round(by["logical"] / (td * 1e-3) / 1e9, 1),
+                       "mixed_step_us": round(tm * 1e3, 2),
+                       "overlap_gain": round((tp + td) / tm, 3)}
+        row["prefill_rope_overhead"] = round(row["rope"]["prefill_us"] / row["none"]["prefill_us"] - 1.0, 4)
+        row["decode_rope_overhead"] = round(row["rope"]["decode_us"] / row["none"]["decode_us"] - 1.0, 4)
+        row["mixed_rope_overhead"] = round(row["rope"]["mixed_step_us"] / row["none"]["mixed_step_us"] - 1.0, 4)
+        row["decode_GB_unique"] = round(by["unique"] / 1e9, 4)
+        row["decode_GB_logical"] = round(by["logical"] / 1e9, 4)
+        row["prefill_GFLOP"] = round(flops / 1e9, 1)
+        out[f"skew{skew}"] = row
+        del pools
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# measured peaks, pool hit ratios, CPU baseline
+# ---------------------------------------------------------------------------
+def measured_peaks(torch) -> dict:
+    out = {}
+    L = ctypes.CDLL(PROBE_LIB)
+    L.lazyattn_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.lazyattn_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    timer = Timer(torch)
+    nwg, iters = 4096, 2000
+    sink = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        assert L.lazyattn_probe_mfma_bf16(nwg, iters, sink.data_ptr(), stream) == 0
+
+    mfma()
+    ms = med([timer.span(mfma, 3) for _ in range(3)])
+    out["mfma_bf16_TFLOPs"] = round(nwg * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12, 1)
+    n16 = (4 << 30) // 16
+    buf = torch.ones(n16 * 4, dtype=torch.int32, device="cuda")
+    rwg = 256 * 32
+
+    sink2 = torch.empty(rwg * 256, dtype=torch.float32, device="cuda")
+
+    def rd():
+        assert L.lazyattn_probe_hbm_read(buf.data_ptr(), n16, rwg, sink2.data_ptr(), stream) == 0
+
+    rd()
+    ms = med([timer.span(rd, 3) for _ in range(3)])
+    out["hbm_read_GBps"] = round(n16 * 16 / (ms * 1e-3) / 1e9, 1)
+    del buf, sink, sink2
+    out["device_copy_GBps"] = round(copy_bandwidth(torch), 1)
+    out["what"] = ("mfma: 4096 work-groups of 4 waves, 8 independent 32x32x16 bf16 MFMA chains each; hbm: "
+                   "grid-stride read of 4 GiB; copy: torch 1 GiB device copy (read + write bytes)")
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_bandwidth(torch) -> float:
+    """GB/s of a plain 1 GiB device-to-device copy (2 GiB moved), median of 5."""
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    return 2.0 * n / (sorted(ts)[2] * 1e-3) / 1e9
 
 
 def hit_ratio_study(W, _abi) -> dict:
@@ -343,65 +658,11 @@ def hit_ratio_study(W, _abi) -> dict:
     return out
 
 
-def bench_configs(torch, W, staging, _abi) -> dict:
-    """The other configurations, warm (medians of three 10-launch spans), each with its
-    rotation-free control on the same inputs: the Llama-3.1-70B 32k shape (a 2048-token chunk of
-    each of 4 requests, and a decode step with split-K) and the MQA stress sweep (four access skews,
-    uniform = the no-reuse control, each under RoPE, ALiBi and no encoding)."""
-    timer = Timer(torch)
-    med = lambda v: sorted(v)[len(v) // 2]
-    span = lambda fn: med([timer.span(fn, 10) for _ in range(3)])
-    out = {}
-
-    def one(wl, encodings):
-        s = wl.spec
-        pools = staging.DevicePools(wl, "cuda")
-        pb = wl.prefill_batch()
-        cfg = staging.config_for(s)
-        res = {}
-        if pb is not None:
-            staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
-            flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
-            for pe in encodings:
-                c = staging.PrefillCall(staging.config_for(s, pe=pe), s, pb, "cuda")
-                c.run(pools)
-                ms = span(lambda: c.run(pools))
-                res[f"prefill_{pe}_us"] = round(ms * 1e3, 2)
-                res[f"prefill_{pe}_TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 2)
-        staging.append_tokens(cfg, pools, wl.tokens_before_step(0), s.dtype, "cuda")
-        d = wl.decode_step(0)
-        if d is not None:
-            staging.append_tokens(cfg, pools, d, s.dtype, "cuda")
-            by = decode_bytes(d, wl)
-            for pe in encodings:
-                c = staging.DecodeCall(staging.config_for(s, pe=pe), s, d, "cuda")
-                c.run(pools)
-                ms = span(lambda: c.run(pools))
-                res[f"decode_{pe}_us"] = round(ms * 1e3, 2)
-                res[f"decode_{pe}_GBps_logical"] = round(by["logical"] / (ms * 1e-3) / 1e9, 1)
-            res["decode_GB_logical"] = round(by["logical"] / 1e9, 4)
-            res["decode_GB_unique"] = round(by["unique"] / 1e9, 4)
-        for ph in ("prefill", "decode"):
-            if f"{ph}_rope_us" in res and f"{ph}_none_us" in res:
-                res[f"{ph}_rope_overhead"] = round(res[f"{ph}_rope_us"] / res[f"{ph}_none_us"] - 1.0, 4)
-        del pools
-        torch.cuda.empty_cache()
-        return res
-
-    wl = W.build_workload(W.spec(4, n_decode=1))
-    out["llama70b_32k"] = dict(what="4 requests x 64 Zipf(1.0) documents x 512 tokens; 2048-token chunk; "
-                                    "decode step 0 with the split-K heuristic", **one(wl, ("rope", "none")))
-    print("# 70B config done", file=sys.stderr, flush=True)
-    for skew in W.CFG5_SKEWS:
-        wl = W.build_workload(W.spec(5, skew=skew))
-        out[f"mqa_skew{skew}"] = one(wl, ("rope", "alibi", "none"))
-    out["mqa_what"] = ("MQA stress: 32 prefill requests (128-token queries) + 96 decode requests, 4..32 lognormal "
-                       "documents each; skew 0.0 = uniform access, the no-reuse control")
-    return out
-
-
-def cpu_baseline(pre, W):
-    """The fp64 oracle on the same prefill batch (all 16 requests), host cores."""
+def cpu_baseline(h):
+    """The fp64 oracle on a sample of the headline workload, on the host's BLAS threads:
+    the first 256 chunk rows of requests 0, 1, ... (all 64 heads, each over its whole 32k
+    context) until about 12 s have been spent, then whole decode steps (all 4 requests) until
+    about 6 s more."""
     import numpy as np  # noqa: F401
     import oracle as O
     try:
@@ -409,26 +670,45 @@ def cpu_baseline(pre, W):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    wl, pb = pre["wl"], pre["pb"]
+    wl, pb = h["wl"], h["pb"]
     s = wl.spec
     kp, vp = wl.pools()
     kp, vp = kp.copy(), vp.copy()
     O.append_kv(kp, vp, pb["k_new"], pb["v_new"], pb["slots"], s.block_size)
     words = O.pack_table(pb["table_blocks"], pb["table_starts"])
-    # repeat whole calls until about 10 s of CPU work have been timed
-    calls, t0 = 0, time.perf_counter()
-    while True:
+    t_pre, flops, done = 0.0, 0.0, []
+    for r in range(len(pb["ctx_lens"])):
+        rows = {r: list(range(256))}
+        t0 = time.perf_counter()
         O.prefill(q=pb["q"], cu_q_lens=pb["cu_q_lens"], ctx_lens=pb["ctx_lens"], num_entries=pb["num_entries"],
                   table_words=words, k_pool=kp, v_pool=vp, num_kv_heads=s.num_kv_heads, block_size=s.block_size,
-                  dtype=s.dtype, pe=s.pe, rope_theta=s.rope_theta)
-        calls += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or calls >= 30:
+                  dtype=s.dtype, pe=s.pe, rope_theta=s.rope_theta, requests=[r], token_subset=rows)
+        t_pre += time.perf_counter() - t0
+        flops += prefill_flops(pb, s.head_dim, s.num_q_heads, token_subset=rows)
+        done.append(r)
+        if t_pre >= 12.0:
             break
-    return {"value": round(calls * pre["flops"] / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 3), "calls": calls,
-            "sample": "the whole timed prefill batch (16 requests x 64 queries over ~4.2k tokens), "
-                      "materialised-RoPE fp64 numpy oracle, whole calls repeated for about 10 s"}
+    t_dec, n_dec, dec_bytes = 0.0, 0, 0
+    for i, d in enumerate(h["steps"]):
+        O.append_kv(kp, vp, d["k_new"], d["v_new"], d["slots"], s.block_size)
+        t0 = time.perf_counter()
+        O.decode(q=d["q"], ctx_lens=d["ctx_lens"], num_entries=d["num_entries"],
+                 table_words=O.pack_table(d["table_blocks"], d["table_starts"]), k_pool=kp, v_pool=vp,
+                 num_kv_heads=s.num_kv_heads, block_size=s.block_size, dtype=s.dtype, pe=s.pe,
+                 rope_theta=s.rope_theta)
+        t_dec += time.perf_counter() - t0
+        n_dec += 1
+        dec_bytes += h["bytes"][i]["unique"]
+        if t_dec >= 6.0:
+            break
+    return {"value": round(flops / t_pre / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(t_pre, 3), "sample_flops": flops,
+            "decode_step_s": round(t_dec / n_dec, 3), "decode_steps_timed": n_dec,
+            "decode_GBps_unique": round(dec_bytes / t_dec / 1e9, 3),
+            "sample": f"headline workload (Llama-3.1-70B 32k chunk): the first 256 chunk rows of requests {done}, "
+                      "all 64 heads over each one's 32.8k-token context (the whole context gathered and rotated "
+                      f"per call), then decode steps 0..{n_dec - 1} of all 4 requests; materialised-RoPE fp64 "
+                      "numpy oracle, one call per request or step"}
 
 
 def calibrate_copy(torch) -> None:
@@ -444,36 +724,16 @@ def calibrate_copy(torch) -> None:
     print(json.dumps({"copy_bytes": n, "dispatches": 3}), flush=True)
 
 
-def copy_bandwidth(torch) -> float:
-    """GB/s of a plain 1 GiB device-to-device copy (2 GiB moved), median of 5: the
-    HBM bandwidth this GPU reaches with a library kernel, as context for the others."""
-    n = 1 << 30
-    a = torch.ones(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    b.copy_(a)
-    ts = []
-    for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    del a, b
-    torch.cuda.empty_cache()
-    return 2.0 * n / (sorted(ts)[2] * 1e-3) / 1e9
-
-
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--decode-steps", type=int, default=256)
-    ap.add_argument("--no-configs", action="store_true", help="skip the 70B and MQA configuration timings")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128, help="decode steps after the headline chunk")
+    ap.add_argument("--decode8b-steps", type=int, default=256)
+    ap.add_argument("--no-extras", action="store_true", help="headline only (8B and MQA extras, peaks skipped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prefill-only", action="store_true", help="time the prefill launches only")
-    ap.add_argument("--decode-only", action="store_true", help="run decode launches only (for profiling)")
+    ap.add_argument("--only", choices=["llama8b", "mqa", "peaks"], help="run one extra alone (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     args = ap.parse_args()
@@ -499,106 +759,34 @@ def main() -> int:
     from position_agnostic_kv_pool_amd import _abi, staging
     _abi.lib()
 
-    if args.decode_only:
-        dec = bench_decode(torch, args, W, staging, _abi, args.decode_steps, framed=False)
-        print(json.dumps({"decode_ms_per_step": dec["ms"], "decode_GBps": dec["bytes"] / dec["ms"] / 1e6}),
-              flush=True)
+    if args.only:
+        if args.only == "llama8b":
+            res = {"llama8b_prefill": bench_llama8b_prefill(torch, args, W, staging, _abi),
+                   "llama8b_decode": bench_llama8b_decode(torch, args, W, staging, _abi, args.decode8b_steps)}
+        elif args.only == "mqa":
+            res = {"mqa_mixed": bench_mqa_mixed(torch, W, staging, _abi)}
+        else:
+            res = {"measured_peaks": measured_peaks(torch)}
+        print(json.dumps(res), flush=True)
         return 0
 
-    pre = bench_prefill(torch, args, W, staging, _abi)
-    print(f"# prefill done: {pre['ms'] * 1e3:.1f} us/step, attention kernel {pre['ms_attend'] * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
-    tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
-    kernel_tflops = pre["flops"] / (pre["ms_attend"] * 1e-3) / 1e12
-    traffic = read_counter_summary(PREFILL_COUNTERS)
-    roofline = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "prefill_bf16_kernel<ROPE>", "flops_per_launch": pre["flops"],
-                "avg_launch_us": round(pre["ms_attend"] * 1e3, 2),
-                "launch_us_p10_p50_p90": [round(pre["pct"][k] * 1e3, 2) for k in ("p10", "p50", "p90")],
-                "cold_launch_us": round(pre["cold"] * 1e3, 2),
-                "merge_kernel_us": round((pre["ms"] - pre["ms_attend"]) * 1e3, 2)}
-    rope_overhead = {"prefill_rope_us": round(pre["ms_attend"] * 1e3, 2),
-                     "prefill_rope_rounds_us": [round(x * 1e3, 2) for x in pre["att"]],
-                     "prefill_norotation_us": round(pre["ms_none_attend"] * 1e3, 2),
-                     "prefill_norotation_rounds_us": [round(x * 1e3, 2) for x in pre["att_none"]],
-                     "prefill_overhead": round(pre["ms_attend"] / pre["ms_none_attend"] - 1.0, 4),
-                     # rotation work: 3 flops per rotated key element, each key tile rotated once per
-                     # work-group of 256 query rows (the pages' 3/(4M) cost model with M = 256)
-                     "prefill_rotation_flop_fraction": round(3.0 / (4.0 * 256), 5),
-                     "prefill_cold_rope_us": round(pre["cold"] * 1e3, 2),
-                     "prefill_cold_norotation_us": round(pre["cold_none"] * 1e3, 2)}
-    out = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "prefill, Llama-3.1-8B attention layer (Hq 32, Hkv 8, d 128, RoPE theta 5e5, "
-                               "block 16): 16 requests x 8 Zipf(1.0) documents x 512 tokens + 64-token causal "
-                               "query; content-only pool, RoPE applied in-kernel",
-                   "global_batch": 16, "seq_len": int(max(pre["pb"]["ctx_lens"])), "parallelism": "single-gpu",
-                   "key_splits": pre["splits"]},
-        "roofline": roofline,
-        "rope_overhead": rope_overhead,
-        "materialize_baseline": {
-            "what": "private copies of every request's blocks with K rotated at absolute positions, queries "
-                    "rotated, then the rotation-free kernel over the copy (the approach deferred RoPE replaces)",
-            "materialize_us": round(pre["base"]["materialize"] * 1e3, 2),
-            "rotate_queries_us": round(pre["base"]["rotate_queries"] * 1e3, 2),
-            "attention_us": round(pre["base"]["attention"] * 1e3, 2),
-            "total_us": round(pre["base"]["total"] * 1e3, 2),
-            "copied_bytes": int(pre["base"]["copied_bytes"]),
-            "deferred_step_us": round(pre["ms"] * 1e3, 2),
-            "deferred_speedup": round(pre["base"]["total"] / pre["ms"], 3)},
-        "fp8_pool_prefill": {
-            "what": "the prefill over an e4m3 pool with per-row power-of-two scales, converted to bf16 in staging",
-            "attention_us": round(pre["ms_fp8_attend"] * 1e3, 2),
-            "vs_bf16_pool": round(pre["ms_attend"] / pre["ms_fp8_attend"], 3)},
-        "document_frames": {
-            "what": "the same attention over a pool whose keys carry their index inside their document "
-                    "(stored R(j) k): prefill turns each key entry once by R(F - p0), decode turns the query "
-                    "once per document",
-            "prefill_attention_us": round(pre["ms_framed_attend"] * 1e3, 2),
-            "prefill_rounds_us": [round(x * 1e3, 2) for x in pre["att_framed"]],
-            "prefill_overhead_vs_norotation": round(pre["ms_framed_attend"] / pre["ms_none_attend"] - 1.0, 4)},
-    }
-    if not args.prefill_only:
-        del pre["pools"]
-        torch.cuda.empty_cache()
-        dec = bench_decode(torch, args, W, staging, _abi, args.decode_steps)
-        gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
-        dtraffic = read_counter_summary(DECODE_COUNTERS)
-        out["decode"] = {
-            "workload": "decode, Llama-3.1-8B shape: 128 requests x 8 Zipf(1.2) documents x 512 tokens "
-                        "+ 32-token suffix, steps 0..%d" % (args.decode_steps - 1),
-            "value": round(gbs, 1), "unit": "GB/s", "us_per_step": round((dec["ms"] + dec["merge_ms"]) * 1e3, 2),
-            "attention_kernel_us": round(dec["ms"] * 1e3, 2), "merge_kernel_us": round(dec["merge_ms"] * 1e3, 2),
-            "tokens_per_s": round(128 / ((dec["ms"] + dec["merge_ms"]) * 1e-3), 1), "splits": dec["splits"],
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dtraffic,
-                         "kernel": "decode_bf16_kernel<ROPE,1>", "bytes_per_launch_logical": round(dec["bytes"]),
-                         "bytes_per_launch_unique": round(dec["unique"])},
-            "norotation_us_per_step": round(dec["ms_none"] * 1e3, 2),
-            "rope_overhead": round(dec["ms"] / dec["ms_none"] - 1.0, 4),
-        }
-        fp8_bytes = dec["bytes"] - dec["kv_bytes"] + dec["kv_bytes"] * 2064 / 4096
-        out["decode"]["fp8_pool"] = {
-            "what": "the same decode steps over an e4m3 pool with per-row power-of-two scales "
-                    "(2064-byte chunks per block and KV head instead of 4096)",
-            "attention_kernel_us": round(dec["ms_fp8"] * 1e3, 2),
-            "bytes_per_launch_logical": round(fp8_bytes),
-            "GBps": round(fp8_bytes / (dec["ms_fp8"] * 1e-3) / 1e9, 1),
-            "speedup_vs_bf16_pool": round(dec["ms"] / dec["ms_fp8"], 3),
-            "framed_attention_kernel_us": round(dec["ms_fp8f"] * 1e3, 2)}
-        out["document_frames"]["decode_attention_us"] = round(dec["ms_framed"] * 1e3, 2)
-        out["document_frames"]["decode_overhead_vs_norotation"] = round(dec["ms_framed"] / dec["ms_none"] - 1.0, 4)
-        print(f"# decode done: {dec['ms'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-    if not args.prefill_only and not args.no_configs:
-        out["configs"] = bench_configs(torch, W, staging, _abi)
-        print("# configs done", file=sys.stderr, flush=True)
-    out["device_copy_GBps"] = round(copy_bandwidth(torch), 1)
-    out["pool_hit_ratio"] = hit_ratio_study(W, _abi)
+    h = bench_headline(torch, args, W, staging, _abi)
+    out = headline_json(h, args)
+    if not args.no_extras:
+        pk = measured_peaks(torch)
+        pk["prefill_frac_of_measured_mfma"] = round(out["roofline"]["achieved"] / pk["mfma_bf16_TFLOPs"], 4)
+        pk["decode_frac_of_measured_hbm_read"] = round(out["decode"]["roofline"]["achieved"] / pk["hbm_read_GBps"], 4)
+        out["measured_peaks"] = pk
+        print("# peaks done", file=sys.stderr, flush=True)
+        out["llama8b_prefill"] = bench_llama8b_prefill(torch, args, W, staging, _abi)
+        print("# 8B prefill done", file=sys.stderr, flush=True)
+        out["llama8b_decode"] = bench_llama8b_decode(torch, args, W, staging, _abi, args.decode8b_steps)
+        print("# 8B decode done", file=sys.stderr, flush=True)
+        out["mqa_mixed"] = bench_mqa_mixed(torch, W, staging, _abi)
+        print("# MQA mixed done", file=sys.stderr, flush=True)
+        out["pool_hit_ratio"] = hit_ratio_study(W, _abi)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(pre, W)
+        out["cpu_baseline"] = cpu_baseline(h)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -14,7 +14,9 @@ from typing import Optional
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblazyattn.so")
+# LAZYATTN_LIBRARY names another build of the same library to load (the tests'
+# host-sanitizer build); by default the in-tree build
+LIB_PATH = os.environ.get("LAZYATTN_LIBRARY") or os.path.join(_PKG, "liblazyattn.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 FLAG_EXACT_MAX = 1          # LAZYATTN_FLAG_EXACT_MAX

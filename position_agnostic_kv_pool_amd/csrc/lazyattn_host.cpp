@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <algorithm>
 
@@ -147,7 +148,11 @@ lazyattn_status lazyattn_rope_inv_freq_llama31(int32_t head_dim, double theta, d
 }
 
 const char* lazyattn_status_string(lazyattn_status s) {
-  switch (s) {
+  // callers may pass any integer: read it as one (an out-of-range value held in
+  // the enum type must not be loaded as that type)
+  int32_t v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case LAZYATTN_OK: return "ok";
     case LAZYATTN_EINVAL: return "invalid argument";
     case LAZYATTN_EUNSUPPORTED: return "unsupported configuration";
