@@ -250,6 +250,27 @@ lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const
                                 int32_t num_splits, void* out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* lazyattn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results, with the split partials written to a device
+ * array the library owns (LAZYATTN_DECODE_SCRATCH_BYTES per GPU, held from the
+ * first call on that GPU until the process ends) instead of a workspace
+ * argument.  The caller still passes q and out.  Makes no allocation.
+ *  - Returns LAZYATTN_EWORKSPACE, before any launch, when the call's split
+ *    partials (lazyattn_decode_workspace_size with the same arguments) exceed
+ *    LAZYATTN_DECODE_SCRATCH_BYTES; pass a smaller num_splits, or use
+ *    lazyattn_decode with a workspace.
+ *  - Every call on one GPU shares that GPU's array: calls that may overlap on
+ *    one GPU (several streams, several threads) race and must not be issued.
+ *    Nothing in it needs clearing between calls (each call writes every
+ *    partial it reads).
+ *  - The first call on a device looks up the array's device address there.
+ * Other arguments and errors as lazyattn_decode. */
+#define LAZYATTN_DECODE_SCRATCH_BYTES (16u << 20)
+lazyattn_status lazyattn_decode_noalloc(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                        const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                        int32_t num_splits, void* out, hipStream_t stream);
+
 /* The attention kernel of lazyattn_prefill / lazyattn_decode alone (same
  * arguments).  With one split it writes `out` directly; with S > 1 splits
  * (see lazyattn_prefill_splits / lazyattn_decode_splits for num_splits 0) it

@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
             "lazyattn_decode_workspace_size": (SZ, [CP, I32, I32, I32]),
             "lazyattn_prefill": (I32, [CP, P, P, I32, I32, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_decode": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
+            "lazyattn_decode_noalloc": (I32, [CP, P, P, P, I64, BP, I32, P, P]),
             "lazyattn_prefill_attend": (I32, [CP, P, P, I32, I32, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_decode_attend": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_merge_splits": (I32, [CP, I32, I32, P, SZ, P, P]),
@@ -272,6 +273,14 @@ def decode(cfg: Config, q, k_pool, v_pool, num_blocks: int, batch: Batch, out, w
                                ctypes.byref(batch), int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
                                _stream(stream))
     _check(st, "lazyattn_decode")
+
+
+def decode_noalloc(cfg: Config, q, k_pool, v_pool, num_blocks: int, batch: Batch, out, num_splits: int = 0,
+                   stream=None) -> None:
+    """lazyattn_decode with the split partials in the library's own device array (no workspace)."""
+    st = lib().lazyattn_decode_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), int(num_blocks),
+                                       ctypes.byref(batch), int(num_splits), _ptr(out), _stream(stream))
+    _check(st, "lazyattn_decode_noalloc")
 
 
 def prefill_attend(cfg: Config, q, cu_q_lens, total_q: int, max_q_len: int, k_pool, v_pool, num_blocks: int,

@@ -21,6 +21,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "lazyattn_common.hpp"
@@ -1721,6 +1722,33 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   return launched();
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free decode (lazyattn_decode_noalloc): the split partials go to a
+// device array owned by the library instead of a caller's workspace.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory, so its device
+// address is looked up once per device and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LAZYATTN_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on its first use there).
+static lazyattn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LAZYATTN_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LAZYATTN_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LAZYATTN_OK;
+}
+
 }  // namespace lazyattn
 
 using namespace lazyattn;
@@ -1764,6 +1792,22 @@ lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const
                                      workspace_bytes, stream, &splits);
   if (st != LAZYATTN_OK || splits <= 1) return st;
   return merge_launch(batch->num_reqs * cfg->num_q_heads, splits, workspace, out, stream);
+}
+
+lazyattn_status lazyattn_decode_noalloc(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                        const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
+                                        int32_t num_splits, void* out, hipStream_t stream) {
+  lazyattn_status st = check_config(cfg);
+  if (st != LAZYATTN_OK) return st;
+  if ((st = check_batch(batch)) != LAZYATTN_OK) return st;
+  if (num_splits < 0 || num_splits > 256) return LAZYATTN_EINVAL;
+  if (batch->num_reqs == 0) return LAZYATTN_OK;
+  const size_t need = lazyattn_decode_workspace_size(cfg, batch->num_reqs, batch->max_entries, num_splits);
+  if (need > LAZYATTN_DECODE_SCRATCH_BYTES) return LAZYATTN_EWORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_of_current_device(&ws)) != LAZYATTN_OK) return st;
+  return lazyattn_decode(cfg, q, k_pool, v_pool, num_blocks, batch, num_splits, out, ws,
+                         need > 0 ? static_cast<size_t>(LAZYATTN_DECODE_SCRATCH_BYTES) : 0, stream);
 }
 
 lazyattn_status lazyattn_merge_splits(const lazyattn_config* cfg, int32_t num_rows, int32_t num_splits,
