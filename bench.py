@@ -9,8 +9,9 @@ of 4096 and placed in random order (32768 context tokens); its 2048 new
 tokens at positions 32768..34815 are prefilled causally over them.  The pool
 holds content-only K/V; RoPE is applied inside the kernel.  Inputs are seeded
 synthetic data already resident in HBM; the chunk's K/V are appended once
-before timing.  Every timed step runs cold: a 512 MiB write evicts the
-last-level cache before it, outside the step's own events.
+before timing.  Every timed step runs cold: a 1 GiB read evicts the 256 MiB
+last-level cache before it, outside the step's own events (a read, so that no
+dirty lines of the eviction are written back inside the timed span).
 
 Also on the same line: the rotation-free control on the same inputs (the
 deferred-RoPE overhead); the 128 decode steps that follow the chunk (split-K,
@@ -41,7 +42,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill TFLOP/s + decode KV GB/s (% of MI355X peak), deferred-RoPE attention"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-FLUSH_BYTES = 512 << 20        # twice the 256 MiB last-level (MALL) cache
+FLUSH_BYTES = 1 << 30          # read before each cold step: four times the 256 MiB last-level (MALL) cache
 KERNEL_SRC = os.path.join(ROOT, "position_agnostic_kv_pool_amd", "csrc", "lazyattn_kernels.hip")
 PROBE_LIB = os.path.join(ROOT, "position_agnostic_kv_pool_amd", "liblazyattn_probe.so")
 COUNTERS = {
@@ -52,8 +53,8 @@ COUNTERS = {
 }
 HEADLINE_WORKLOAD = ("prefill, Llama-3.1-70B attention layer (Hq 64, Hkv 8, d 128, RoPE theta 5e5, block 16): "
                      "2048-token causal chunk of each of 4 requests over 64 Zipf(1.0) documents x 512 tokens "
-                     "(32k context); content-only pool, RoPE applied in-kernel; cold (last-level cache "
-                     "flushed before each step)")
+                     "(32k context); content-only pool, RoPE applied in-kernel; cold (a 1 GiB read evicts the "
+                     "last-level cache before each step)")
 
 
 def kernel_source_hash() -> str:
@@ -166,12 +167,24 @@ def pct(v):
     return [v[len(v) // 10], v[len(v) // 2], v[(9 * len(v)) // 10]]
 
 
+def probe_lib():
+    """liblazyattn_probe.so (peak probes: MFMA issue rate, streaming read, chunk gather)."""
+    L = ctypes.CDLL(PROBE_LIB)
+    L.lazyattn_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.lazyattn_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    L.lazyattn_probe_gather_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
 class Timer:
     """HIP events on the stream the kernels are launched on (torch's current stream)."""
 
     def __init__(self, torch):
         self.torch = torch
         self.flush_buf = None
+        self.probe = probe_lib()
 
     def busy(self):
         # keep the GPU busy while the host enqueues the timed launches, so host
@@ -180,9 +193,16 @@ class Timer:
             self.torch.cuda._sleep(2_000_000)
 
     def flush(self, rep=0):
+        """Evict the last-level cache by reading FLUSH_BYTES of another buffer.  A write
+        would leave that many dirty lines, whose write-back then lands inside the next timed
+        span (measured: +58 us on one 70B decode step)."""
+        t = self.torch
         if self.flush_buf is None:
-            self.flush_buf = self.torch.empty(FLUSH_BYTES, dtype=self.torch.uint8, device="cuda")
-        self.flush_buf.fill_(rep & 0xff)
+            self.flush_buf = t.ones(FLUSH_BYTES, dtype=t.uint8, device="cuda")
+            self.flush_sink = t.empty(8192 * 256, dtype=t.float32, device="cuda")
+        st = t.cuda.current_stream().cuda_stream
+        assert self.probe.lazyattn_probe_hbm_read(self.flush_buf.data_ptr(), FLUSH_BYTES // 16, 8192,
+                                                  self.flush_sink.data_ptr(), st) == 0
 
     def release(self):
         self.flush_buf = None
@@ -275,8 +295,38 @@ def bench_headline(torch, args, W, staging, _abi):
                         warm_step=[x[0] / 3.0 for x in warm])
     print(f"# headline decode: {sum(dec['rope']['cold_att']) / n * 1e3:.1f} us attention per step (cold)",
           file=sys.stderr, flush=True)
+    # decode step 0's own chunk list (each entry's K and V chunk of every KV head, in the
+    # kernel's order) read by a plain gather kernel, cold: what this access pattern reaches
+    # on this GPU, next to the decode kernel's time for the same step
+    d0 = steps[0]
+    chunk = s.block_size * s.head_dim * 2
+    dv = pools.v.data_ptr() - pools.k.data_ptr()
+    offs = []
+    for r in range(len(d0["ctx_lens"])):
+        blk = d0["table_blocks"][r, :int(d0["num_entries"][r])].astype("int64")
+        for hh in range(s.num_kv_heads):
+            for b in blk:
+                o = (int(b) * s.num_kv_heads + hh) * chunk
+                offs += [o, dv + o]
+    ot = torch.tensor(offs, dtype=torch.int64, device="cuda")
+    gsink = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def gather():
+        assert timer.probe.lazyattn_probe_gather_read(pools.k.data_ptr(), ot.data_ptr(), len(offs), chunk, 2048,
+                                                      gsink.data_ptr(), st) == 0
+
+    gather()
+    g_ms = med([x[0] for x in timer.steps([gather], 7, cold=True)])
+    d0_ms = med([x[0] for x in timer.steps([lambda: calls[0].attend(pools)], 7, cold=True)])
+    gather_probe = dict(us_cold=round(g_ms * 1e3, 2), bytes=len(offs) * chunk,
+                        GBps=round(len(offs) * chunk / (g_ms * 1e-3) / 1e9, 1),
+                        decode_step0_attention_us_cold=round(d0_ms * 1e3, 2),
+                        decode_vs_gather=round(g_ms / d0_ms, 4))
+    del ot, gsink
     timer.release()
-    out = dict(pre=pre, dec=dec, bytes=by, splits=calls[0].splits, n=n, wl=wl, pb=pb, steps=steps)
+    out = dict(pre=pre, dec=dec, bytes=by, splits=calls[0].splits, n=n, wl=wl, pb=pb, steps=steps,
+               gather_probe=gather_probe)
     del calls, calls_none, pools
     torch.cuda.empty_cache()
     return out
@@ -314,7 +364,7 @@ def headline_json(h, args):
     gbs_unique = uniq / (att * 1e-3) / 1e9
     decode = {
         "workload": f"decode steps 0..{n - 1} after the chunk: 4 requests x 34817..{34816 + n} tokens, split-K "
-                    f"({h['splits']} splits) + merge; cold (cache flushed before each step)",
+                    f"({h['splits']} splits) + merge; cold (a 1 GiB read evicts the cache before each step)",
         "us_per_step_cold": round((att + mrg) * 1e3, 2), "attention_kernel_us_cold": round(att * 1e3, 2),
         "merge_kernel_us_cold": round(mrg * 1e3, 2),
         "us_per_step_warm": round(sum(r["warm_step"]) / n * 1e3, 2),
@@ -329,6 +379,9 @@ def headline_json(h, args):
                      "logical_GBps_context": round(logical / (att * 1e-3) / 1e9, 1),
                      "note": "achieved = unique bytes (each block and KV head once, plus q, out, table words) / "
                              "mean cold attention-kernel time; logical bytes re-count shared blocks"},
+        "gather_probe": dict(what="step 0's K and V chunks (4 KiB each, every entry and KV head, the kernel's "
+                                  "order) read by a plain gather kernel, cold: the access pattern's practical "
+                                  "roofline on this GPU", **h["gather_probe"]),
         "norotation_attention_us_cold": round(sum(z["cold_att"]) / n * 1e3, 2),
         "rope_overhead_cold": round(att / (sum(z["cold_att"]) / n) - 1.0, 4),
         "rope_overhead_warm": round(sum(r["warm_step"]) / sum(z["warm_step"]) - 1.0, 4),
@@ -573,10 +626,7 @@ def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
 # ---------------------------------------------------------------------------
 def measured_peaks(torch) -> dict:
     out = {}
-    L = ctypes.CDLL(PROBE_LIB)
-    L.lazyattn_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    L.lazyattn_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
-                                          ctypes.c_void_p]
+    L = probe_lib()
     stream = torch.cuda.current_stream().cuda_stream
     timer = Timer(torch)
     nwg, iters = 4096, 2000

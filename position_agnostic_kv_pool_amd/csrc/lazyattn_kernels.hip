@@ -870,6 +870,8 @@ struct DecodeArgs {
 };
 
 constexpr int kOS = kPD + 4;  // LDS row stride (floats) of the wave-merge buffer
+constexpr int kTab = 2048;    // table entries staged in LDS at a time (in the merge buffer's space)
+static_assert((3 * kTab + 1) * 4 <= 4 * 16 * kOS * 4, "the staged table fits the wave-merge buffer");
 constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
 template <int PE, int NT, int KV8>
@@ -976,12 +978,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       asm volatile("" : "+v"(rn[i].x), "+v"(rn[i].y));
     }
   }
-  // framed pool: frame starts of this request's entries, and the frame the
-  // query fragments qb are currently turned to (none yet)
-  // (read through the constant address space, like the table words: a vector
-  // load here would be followed by a wait that drains the K/V ring)
-  typedef const __attribute__((address_space(4))) int32_t* const_frames;
-  const const_frames frow = (const_frames)(A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0));
+  // framed pool: the frame the query fragments qb are currently turned to (none yet)
   int q_frame = 0, q_turns = 0;
   bool q_set = false;
 
@@ -1028,19 +1025,40 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     }
   };
 
-  // Entries are processed in the wave-uniform order e_begin + wave, + 4, ...;
-  // the table words make scalar loads.  Two ring slots hold the K/V of the
-  // entry being processed and of the next one (in flight); a slot is refilled
-  // with the entry after next as soon as its entry is done, so its loads have
-  // a whole entry's time to land and no registers are copied.  The words of
-  // the entry to load next are fetched one entry ahead of its K/V loads.
+  // Entries are processed in the wave-uniform order e_begin + wave + 4k, k = 0, 1,
+  // ...  Two ring slots hold the K/V of the entry being processed and of the next
+  // one (in flight); a slot is refilled with the entry after next as soon as its
+  // entry is done, so its loads have a whole entry's time to land and no
+  // registers are copied.  Past the wave's last entry a slot reloads that entry
+  // (its block is already in L2, and the result is never used): every refill then
+  // issues the same loads on every path, so the wait for one slot's data never
+  // has to drain the other's.
+  //
+  // The split's table is staged in LDS by the whole work-group, up to kTab
+  // entries at a time: the logical start of every entry and of the one after
+  // the chunk, the block ids and (framed pools) the frame starts.  An entry's
+  // fields are then LDS reads, which complete in order: no wait for them
+  // involves the K/V loads in flight (table words read with scalar loads would
+  // share a counter with the LDS reads and return out of order; read with
+  // vector loads, they would share the K/V loads' counter).
   uint4 krb[2][4];
   uint2 vrb[2][8];
   EntryInfo curb[2];
   int frb[2];
-  EntryInfo nx{};
-  int fr_nx = 0;
-  int e = __builtin_amdgcn_readfirstlane(e_begin + wave);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);          // wave-uniform, so the loop branches are scalar
+  uint32_t* tst = reinterpret_cast<uint32_t*>(o_s);             // [kTab + 1] logical starts (o_s is free until the merge)
+  uint32_t* tbk = tst + kTab + 1;                                // [kTab] block ids
+  int32_t* tfr = reinterpret_cast<int32_t*>(tbk + kTab);         // [kTab] frame starts
+  const int32_t* frow_v = A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0);
+  int nk = 0, kl = 0;                                            // this wave's entries in the chunk; next to load
+  auto fetch = [&](EntryInfo& inf, int& fr) {
+    const int li = wv + 4 * min(kl, nk - 1);
+    inf.blk = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tbk[li])));
+    inf.start = __builtin_amdgcn_readfirstlane(static_cast<int>(tst[li]));
+    inf.len = __builtin_amdgcn_readfirstlane(static_cast<int>(tst[li + 1])) - inf.start;
+    fr = (PE == kPeFramed) ? __builtin_amdgcn_readfirstlane(tfr[li]) : 0;
+    ++kl;
+  };
   // RoPE: R(S - p) of a slot's entry at pair l, formed by lane l into the slot's
   // LDS row as soon as the entry's loads are issued, so that the entry's
   // rotation reads it without an LDS round trip on its own path
@@ -1050,22 +1068,6 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       __builtin_amdgcn_wave_barrier();
     }
   };
-#pragma unroll
-  for (int sl = 0; sl < 2; ++sl) {
-    const int ee = e + 4 * sl;
-    frb[sl] = 0;
-    if (ee < e_end) {
-      curb[sl] = entry_info(trow, ee, ne, L);
-      load_kv(curb[sl].blk, krb[sl], vrb[sl]);
-      put_phase(sl, curb[sl].start);
-      if (PE == kPeFramed) frb[sl] = frow[ee];
-    }
-  }
-  if (e + 8 < e_end) {
-    nx = entry_info(trow, e + 8, ne, L);
-    if (PE == kPeFramed) fr_nx = frow[e + 8];
-  }
-
   // one entry, its K/V in k and v (converted in place for FP8)
   auto process = [&](const EntryInfo inf, const int fr, uint4 (&k)[4], uint2 (&v)[8], const int sl)
                      __attribute__((always_inline)) {
@@ -1215,29 +1217,50 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       }
   };
 
-  bool more = e < e_end;
-  while (more) {
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      if (more) {
-        process(curb[sl], frb[sl], krb[sl], vrb[sl], sl);
-        const int e_ld = e + 8;
-        if (e_ld < e_end) {
-          load_kv(nx.blk, krb[sl], vrb[sl]);
-          // the slot's phase row is rewritten only after this entry's reads of it
-          // (the same wave's LDS operations complete in order)
-          put_phase(sl, nx.start);
-          curb[sl] = nx;
-          frb[sl] = fr_nx;
-          if (e_ld + 4 < e_end) {
-            nx = entry_info(trow, e_ld + 4, ne, L);
-            if (PE == kPeFramed) fr_nx = frow[e_ld + 4];
-          }
-        }
-        e += 4;
-        more = e < e_end;
+  const int n_split = max(0, e_end - e_begin);
+  for (int c0 = 0; c0 < n_split; c0 += kTab) {
+    const int cn = min(kTab, n_split - c0);
+    if (c0 > 0) __syncthreads();                     // every wave is done with the previous chunk
+    for (int i = tid; i <= cn; i += 256) {
+      const int ei = e_begin + c0 + i;
+      if (i < cn) {
+        const uint64_t w = trow[ei];
+        tst[i] = word_start(w);
+        tbk[i] = word_block(w);
+        if (PE == kPeFramed) tfr[i] = frow_v[ei];
+      } else {
+        tst[i] = (ei < ne) ? reinterpret_cast<const uint32_t*>(trow + ei)[1] : static_cast<uint32_t>(L);
       }
     }
+    __syncthreads();
+    nk = max(0, (cn - wv + 3) >> 2);
+    kl = 0;
+    if (nk == 0) continue;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      fetch(curb[sl], frb[sl]);
+      load_kv(curb[sl].blk, krb[sl], vrb[sl]);
+      put_phase(sl, curb[sl].start);
+    }
+    // Slot 0 always runs before slot 1 and the pair loop has one exit, after slot
+    // 1's refill: on every path into a slot's processing the other slot's loads
+    // are the newer ones, so the wait for this slot's data leaves them in flight.
+    const int npair = nk >> 1;
+    for (int it = 0; it < npair; ++it) {
+      process(curb[0], frb[0], krb[0], vrb[0], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(curb[0], frb[0]);
+      load_kv(curb[0].blk, krb[0], vrb[0]);
+      put_phase(0, curb[0].start);
+      process(curb[1], frb[1], krb[1], vrb[1], 1);
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(curb[1], frb[1]);
+      load_kv(curb[1].blk, krb[1], vrb[1]);
+      // a slot's phase row is rewritten only after its entry's reads of it (the
+      // same wave's LDS operations complete in order)
+      put_phase(1, curb[1].start);
+    }
+    if (nk & 1) process(curb[0], frb[0], krb[0], vrb[0], 0);
   }
 
   // ---- merge the four waves ------------------------------------------------------

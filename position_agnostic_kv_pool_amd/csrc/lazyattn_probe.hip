@@ -8,6 +8,9 @@
 //    on another), so the matrix pipes stay busy; 2 * 32 * 32 * 16 flops each.
 //  - lazyattn_probe_hbm_read: a grid-stride streaming read of n 16-byte words,
 //    folded into one value per thread (so no load is dropped).
+//  - lazyattn_probe_gather_read: work-groups read whole chunks (chunk_bytes, a
+//    multiple of 4 KiB) at caller-given offsets, four in flight each: the access
+//    pattern of a paged KV pool whose blocks sit at scattered positions.
 //
 // Each thread stores its result to its own slot of `sink` (vector stores).
 #include <hip/hip_runtime.h>
@@ -58,6 +61,27 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const uint4* src, size_t 
   sink[tid] = static_cast<float>(x & 0xffu);
 }
 
+// Work-group b reads chunks 4b .. 4b + 3, then 4(b + gridDim.x) .., of the offset
+// list, four chunks in flight at a time; each chunk is read 4 KiB at a time, 16
+// bytes per thread.
+__global__ __launch_bounds__(256) void gather_read_kernel(const uint4* base, const int64_t* offsets, int n_chunks,
+                                                          int chunk_units, float* sink) {
+  uint32_t x = 0;
+  for (int c = 4 * blockIdx.x; c < n_chunks; c += 4 * gridDim.x) {
+    const uint4* p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = base + offsets[min(c + j, n_chunks - 1)] / 16;
+    for (int u = 0; u < chunk_units; ++u) {
+      uint4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = p[j][u * 256 + threadIdx.x];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+  }
+  sink[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = static_cast<float>(x & 0xffu);
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,6 +98,18 @@ int lazyattn_probe_mfma_bf16(int num_wg, int iters, float* sink, hipStream_t str
 int lazyattn_probe_hbm_read(const void* src, size_t n, int num_wg, float* sink, hipStream_t stream) {
   if (num_wg < 1 || !src || !sink) return static_cast<int>(hipErrorInvalidValue);
   hipLaunchKernelGGL(hbm_read_kernel, dim3(num_wg), dim3(256), 0, stream, static_cast<const uint4*>(src), n, sink);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Reads n_chunks chunks of chunk_bytes (a multiple of 4096) at byte offsets
+// offsets[i] (device int64, multiples of 16) from base (device).  sink: device
+// float [num_wg * 256].
+int lazyattn_probe_gather_read(const void* base, const int64_t* offsets, int n_chunks, int chunk_bytes, int num_wg,
+                               float* sink, hipStream_t stream) {
+  if (num_wg < 1 || n_chunks < 0 || chunk_bytes < 4096 || chunk_bytes % 4096 != 0 || !base || !offsets || !sink)
+    return static_cast<int>(hipErrorInvalidValue);
+  hipLaunchKernelGGL(gather_read_kernel, dim3(num_wg), dim3(256), 0, stream, static_cast<const uint4*>(base), offsets,
+                     n_chunks, chunk_bytes / 4096, sink);
   return static_cast<int>(hipGetLastError());
 }
 
