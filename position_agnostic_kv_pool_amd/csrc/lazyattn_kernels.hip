@@ -776,7 +776,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 // and M = max_s m_s.  Each split's output is stored already divided by its own
 // sum, in fp16 (a relative rounding of 2^-11, under the bf16 rounding of the
 // result), which halves the partial traffic.  One 16-lane group per (row,
-// head), 8 channels (16 bytes) per lane.  Splits are taken four at a time with
+// head), 8 channels (16 bytes) per lane.  Splits are taken CH at a time with
 // their loads issued together (nothing is read past the last split); M is the
 // running maximum, and what was summed before
 // a chunk raised it is rescaled (the order is fixed: reproducible bit for
@@ -784,6 +784,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 // weighs 0, and its output, which may never have been written, is dropped by a
 // select.
 // ---------------------------------------------------------------------------
+// CH = splits whose loads are issued together: 16 for calls of more than 4 splits
+// (one memory round trip for up to 16), else 4 (fewer registers for the
+// bandwidth-bound merges of few splits)
+template <int CH>
 __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, const float* ml_part, uint16_t* out,
                                                     int rows, int splits) {
   const int idx = blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -791,11 +795,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, cons
   if (idx >= rows) return;
   float M = kNegInf, lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < splits; s0 += 4) {
-    float2 ml[4];
-    uint4 o[4];
+  for (int s0 = 0; s0 < splits; s0 += CH) {
+    float2 ml[CH];
+    uint4 o[CH];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < CH; ++j) {
       // splits is the same for every thread: past the last split nothing is read
       ml[j] = make_float2(kNegInf, 0.f);
       o[j] = make_uint4(0u, 0u, 0u, 0u);
@@ -805,10 +809,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, cons
         o[j] = *reinterpret_cast<const uint4*>(o_part + row * kPD + 8 * c);
       }
     }
-    bool live[4];
+    bool live[CH];
     float mc = kNegInf;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < CH; ++j) {
       live[j] = (s0 + j < splits) && (ml[j].x != kNegInf);
       mc = fmaxf(mc, live[j] ? ml[j].x : kNegInf);
     }
@@ -818,7 +822,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, cons
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] *= f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < CH; ++j) {
       const float w = live[j] ? __builtin_amdgcn_exp2f(ml[j].x - Mn) * ml[j].y : 0.f;
       lsum += w;
       const uint32_t ow[4] = {o[j].x, o[j].y, o[j].z, o[j].w};
@@ -871,7 +875,7 @@ struct DecodeArgs {
 
 constexpr int kOS = kPD + 4;  // LDS row stride (floats) of the wave-merge buffer
 constexpr int kTab = 2048;    // table entries staged in LDS at a time (in the merge buffer's space)
-static_assert((3 * kTab + 1) * 4 <= 4 * 16 * kOS * 4, "the staged table fits the wave-merge buffer");
+static_assert(4 * kTab * 4 <= 4 * 16 * kOS * 4, "the staged table fits the wave-merge buffer");
 constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
 template <int PE, int NT, int KV8>
@@ -1035,8 +1039,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   // has to drain the other's.
   //
   // The split's table is staged in LDS by the whole work-group, up to kTab
-  // entries at a time: the logical start of every entry and of the one after
-  // the chunk, the block ids and (framed pools) the frame starts.  An entry's
+  // entries at a time: each entry's logical start and end (the next entry's
+  // start, or L), block id and (framed pools) frame start.  An entry's
   // fields are then LDS reads, which complete in order: no wait for them
   // involves the K/V loads in flight (table words read with scalar loads would
   // share a counter with the LDS reads and return out of order; read with
@@ -1046,8 +1050,9 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   EntryInfo curb[2];
   int frb[2];
   const int wv = __builtin_amdgcn_readfirstlane(wave);          // wave-uniform, so the loop branches are scalar
-  uint32_t* tst = reinterpret_cast<uint32_t*>(o_s);             // [kTab + 1] logical starts (o_s is free until the merge)
-  uint32_t* tbk = tst + kTab + 1;                                // [kTab] block ids
+  uint32_t* tst = reinterpret_cast<uint32_t*>(o_s);             // [kTab] logical starts (o_s is free until the merge)
+  uint32_t* ten = tst + kTab;                                    // [kTab] logical ends
+  uint32_t* tbk = ten + kTab;                                    // [kTab] block ids
   int32_t* tfr = reinterpret_cast<int32_t*>(tbk + kTab);         // [kTab] frame starts
   const int32_t* frow_v = A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0);
   int nk = 0, kl = 0;                                            // this wave's entries in the chunk; next to load
@@ -1055,7 +1060,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     const int li = wv + 4 * min(kl, nk - 1);
     inf.blk = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tbk[li])));
     inf.start = __builtin_amdgcn_readfirstlane(static_cast<int>(tst[li]));
-    inf.len = __builtin_amdgcn_readfirstlane(static_cast<int>(tst[li + 1])) - inf.start;
+    inf.len = __builtin_amdgcn_readfirstlane(static_cast<int>(ten[li])) - inf.start;
     fr = (PE == kPeFramed) ? __builtin_amdgcn_readfirstlane(tfr[li]) : 0;
     ++kl;
   };
@@ -1221,16 +1226,13 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   for (int c0 = 0; c0 < n_split; c0 += kTab) {
     const int cn = min(kTab, n_split - c0);
     if (c0 > 0) __syncthreads();                     // every wave is done with the previous chunk
-    for (int i = tid; i <= cn; i += 256) {
+    for (int i = tid; i < cn; i += 256) {
       const int ei = e_begin + c0 + i;
-      if (i < cn) {
-        const uint64_t w = trow[ei];
-        tst[i] = word_start(w);
-        tbk[i] = word_block(w);
-        if (PE == kPeFramed) tfr[i] = frow_v[ei];
-      } else {
-        tst[i] = (ei < ne) ? reinterpret_cast<const uint32_t*>(trow + ei)[1] : static_cast<uint32_t>(L);
-      }
+      const uint64_t w = trow[ei];
+      tst[i] = word_start(w);
+      ten[i] = (ei + 1 < ne) ? reinterpret_cast<const uint32_t*>(trow + ei + 1)[1] : static_cast<uint32_t>(L);
+      tbk[i] = word_block(w);
+      if (PE == kPeFramed) tfr[i] = frow_v[ei];
     }
     __syncthreads();
     nk = max(0, (cn - wv + 3) >> 2);
@@ -1601,8 +1603,12 @@ static size_t decode_lds_bytes(int nt) {
 static lazyattn_status merge_launch(int rows_total, int splits, const void* workspace, void* out, hipStream_t stream) {
   const uint16_t* o_part = static_cast<const uint16_t*>(workspace);
   const float* ml_part = reinterpret_cast<const float*>(o_part + static_cast<size_t>(splits) * rows_total * kPD);
-  hipLaunchKernelGGL(merge_kernel, dim3((rows_total + 15) / 16), dim3(256), 0, stream, o_part, ml_part,
-                     static_cast<uint16_t*>(out), rows_total, splits);
+  if (splits > 4)
+    hipLaunchKernelGGL(merge_kernel<16>, dim3((rows_total + 15) / 16), dim3(256), 0, stream, o_part, ml_part,
+                       static_cast<uint16_t*>(out), rows_total, splits);
+  else
+    hipLaunchKernelGGL(merge_kernel<4>, dim3((rows_total + 15) / 16), dim3(256), 0, stream, o_part, ml_part,
+                       static_cast<uint16_t*>(out), rows_total, splits);
   return launched();
 }
 
