@@ -360,8 +360,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   // K: lane l holds channel pair l of the 8 key rows (4 B each); V: lane l holds
   // keys 8 (l % 2) .. + 7 of channels 64 part + 32 cc + l / 2, cc = 0, 1
   const int E_own = ws >> 1, part = ws & 1;
+  // this lane's channel-pair frequency (turns per position), read once
+  const double rev_l = (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) ? A.rope.rev[lane] : 0.0;
   float2 r1 = make_float2(1.f, 0.f);               // R(1) at this lane's pair
-  if (PE == LAZYATTN_PE_ROPE) r1 = unit_phase(1, A.rope.rev[lane]);
+  if (PE == LAZYATTN_PE_ROPE) r1 = unit_phase(1, rev_l);
   // The phases of a lane's 8 consecutive key rows: R(a + 1) = R(a) R(1), then
   // R(a + k + 1) = 2 cos(f) R(a + k) - R(a + k - 1), one fused multiply-add per
   // component instead of a complex product.  The rounding of 2 cos(f) shifts the
@@ -492,6 +494,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   float m_ref[NT] = {0.f};                           // reference per row (raw score units)
   f32x16 negm[NT];
 
+  // Turn (RoPE, frames) or convert (FP8) staged key row k; called between QK
+  // products so that the work hides under them
+  auto stage_row = [&](int k, float2& ph, float2& pq) __attribute__((always_inline)) {
+    if (PE == LAZYATTN_PE_ROPE) {
+      kr[k] = KV8 ? key_fp8(k, ph) : rotate_pair(kr[k], ph);
+      if (k < 7) next_phase(k, ph, pq);
+    } else if (KV8) {
+      kr[k] = key_fp8(k, ph);                 // framed: turned by ph; else converted
+    } else if (PE == kPeFramed) {
+      kr[k] = rotate_pair(kr[k], ph);
+    }
+    if (k == 3 && KV8) convert_v8();
+    // keep the row's work between the products around it (the compiler would
+    // otherwise sink it to the LDS write)
+    asm volatile("" : "+v"(kr[k]));
+  };
+
   // One pass over the key tiles.  maxpass: scores only, folded into the exact
   // row maximum mx[].  Otherwise P.V with the reference m_ref (taken from the
   // first tile when `fresh`).
@@ -510,7 +529,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       }
       load_kv(blk);
       if (PE == LAZYATTN_PE_ROPE) {
-        float2 ph = unit_phase_turns(st - p0 + 8 * part, A.rope.rev[lane]), pq;
+        float2 ph = unit_phase_turns(st - p0 + 8 * part, rev_l), pq;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           kr[k] = KV8 ? key_fp8(k, ph) : rotate_pair(kr[k], ph);
@@ -523,7 +542,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       if (KV8) convert_v8();
       if (PE == kPeFramed) {
         // every row of the entry turns by the same R(F - p0)
-        const float2 ph = unit_phase_turns(__builtin_amdgcn_readlane(fv0, E_own) - p0, A.rope.rev[lane]);
+        const float2 ph = unit_phase_turns(__builtin_amdgcn_readlane(fv0, E_own) - p0, rev_l);
 #pragma unroll
         for (int k = 0; k < 8; ++k) kr[k] = KV8 ? key_fp8(k, ph) : rotate_pair(kr[k], ph);
       }
@@ -540,14 +559,25 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       int nblk, nst, nln;
       entry_of(wv1, i + 1, E_own, nblk, nst, nln);
       const uint16_t* kb = Ks[i & 1];
+      int st[4], ln[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        int b_unused;
+        entry_of(wv0, i, x, b_unused, st[x], ln[x]);
+      }
+      // every key of the tile is a whole block's and visible to every row
+      const bool full = (ln[0] == kBlock) && (ln[1] == kBlock) && (ln[2] == kBlock) && (ln[3] == kBlock) &&
+                        (st[3] + kBlock - 1 <= p0);
+      float2 ph = make_float2(1.f, 0.f), pq = ph;
+      if (PE == LAZYATTN_PE_ROPE) ph = unit_phase_turns(nst - p0 + 8 * part, rev_l);
+      if (PE == kPeFramed) ph = unit_phase_turns(__builtin_amdgcn_readlane(fv1, E_own) - p0, rev_l);
+      uint64_t wv3;
+      int fv3;
       f32x16 S[2][NT];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) S[tau][nt] = negm[nt];
-      float2 ph = make_float2(1.f, 0.f), pq = ph;
-      if (PE == LAZYATTN_PE_ROPE) ph = unit_phase_turns(nst - p0 + 8 * part, A.rope.rev[lane]);
-      if (PE == kPeFramed) ph = unit_phase_turns(__builtin_amdgcn_readlane(fv1, E_own) - p0, A.rope.rev[lane]);
       // K~ operands are read one k-step ahead of their products
       bf16x8 ak[2][2];
 #pragma unroll
@@ -564,37 +594,20 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) S[tau][nt] = mfma32x32x16(ak[kk & 1][tau], qf[8 * nt + kk], S[tau][nt]);
-        if (PE == LAZYATTN_PE_ROPE) {
-          kr[kk] = KV8 ? key_fp8(kk, ph) : rotate_pair(kr[kk], ph);
-          if (kk < 7) next_phase(kk, ph, pq);
-        } else if (KV8) {
-          kr[kk] = key_fp8(kk, ph);                 // framed: turned by ph; else converted
-        } else if (PE == kPeFramed) {
-          kr[kk] = rotate_pair(kr[kk], ph);
-        }
-        if (kk == 3 && KV8) convert_v8();
-        // keep this row's rotation between this k-step's products (the compiler
-        // would otherwise sink it to the LDS write after the loop)
-        asm volatile("" : "+v"(kr[kk]));
+        stage_row(kk, ph, pq);
       }
       // rare: only entries shorter than a block need their padding zeroed
       if (__builtin_expect(nln < kBlock, 0)) mask_v(nln);
       stage_write((i + 1) & 1);
-      // loads of tile i + 2, words of tile i + 3
+      // words of tile i + 3, then the loads of tile i + 2 (in this order, the
+      // copies of the word registers at the end of the tile wait for the word
+      // load only, not for the K/V loads issued after it)
       int lblk, lst, lln;
       entry_of(wv2, i + 2, E_own, lblk, lst, lln);
+      wv3 = load_words(i + 3);
+      fv3 = load_frames(i + 3);
       load_kv(lblk);
-      const uint64_t wv3 = load_words(i + 3);
-      const int fv3 = load_frames(i + 3);
 
-      int st[4], ln[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        int b_unused;
-        entry_of(wv0, i, x, b_unused, st[x], ln[x]);
-      }
-      const bool full = (ln[0] == kBlock) && (ln[1] == kBlock) && (ln[2] == kBlock) && (ln[3] == kBlock) &&
-                        (st[3] + kBlock - 1 <= p0);
       // register r of half tau: key row 8 h + (r % 8) of entry 2 tau + r / 8
       if (PE == LAZYATTN_PE_ALIBI) {
 #pragma unroll
@@ -875,14 +888,15 @@ struct DecodeArgs {
 
 constexpr int kOS = kPD + 4;  // LDS row stride (floats) of the wave-merge buffer
 constexpr int kTab = 2048;    // table entries staged in LDS at a time (in the merge buffer's space)
+constexpr int kRing = 2;      // entries of a decode wave in registers: one processed, the rest in flight
 static_assert(4 * kTab * 4 <= 4 * 16 * kOS * 4, "the staged table fits the wave-merge buffer");
 constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
 template <int PE, int NT, int KV8>
 __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) float dsm[];
-  float2* bsh = reinterpret_cast<float2*>(dsm);             // [4 waves][2][64]
-  float* ml_s = dsm + 4 * 2 * 64 * 2;                         // [4][NT*16][2]
+  float2* bsh = reinterpret_cast<float2*>(dsm);             // [4 waves][kRing][64]
+  float* ml_s = dsm + 4 * kRing * 64 * 2;                     // [4][NT*16][2]
   float* o_s = ml_s + 4 * NT * 16 * 2;                        // [4][Gw][kOS] (NT * 16 rows reserved)
   float2* rtab = reinterpret_cast<float2*>(o_s + 4 * NT * 16 * kOS);  // [16][64] R(n), RoPE only
 
@@ -1030,13 +1044,13 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   };
 
   // Entries are processed in the wave-uniform order e_begin + wave + 4k, k = 0, 1,
-  // ...  Two ring slots hold the K/V of the entry being processed and of the next
-  // one (in flight); a slot is refilled with the entry after next as soon as its
-  // entry is done, so its loads have a whole entry's time to land and no
-  // registers are copied.  Past the wave's last entry a slot reloads that entry
-  // (its block is already in L2, and the result is never used): every refill then
-  // issues the same loads on every path, so the wait for one slot's data never
-  // has to drain the other's.
+  // ...  kRing ring slots hold the K/V of the entry being processed and of the
+  // next kRing - 1 (in flight); a slot is refilled with the entry kRing places
+  // on as soon as its entry is done, so its loads have kRing - 1 entries' time
+  // to land and no registers are copied.  Past the wave's last entry a slot
+  // reloads that entry (its block is already in L2, and the result is never
+  // used): every refill then issues the same loads on every path, so the wait
+  // for one slot's data never has to drain the others'.
   //
   // The split's table is staged in LDS by the whole work-group, up to kTab
   // entries at a time: each entry's logical start and end (the next entry's
@@ -1045,10 +1059,10 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   // involves the K/V loads in flight (table words read with scalar loads would
   // share a counter with the LDS reads and return out of order; read with
   // vector loads, they would share the K/V loads' counter).
-  uint4 krb[2][4];
-  uint2 vrb[2][8];
-  EntryInfo curb[2];
-  int frb[2];
+  uint4 krb[kRing][4];
+  uint2 vrb[kRing][8];
+  EntryInfo curb[kRing];
+  int frb[kRing];
   const int wv = __builtin_amdgcn_readfirstlane(wave);          // wave-uniform, so the loop branches are scalar
   uint32_t* tst = reinterpret_cast<uint32_t*>(o_s);             // [kTab] logical starts (o_s is free until the merge)
   uint32_t* ten = tst + kTab;                                    // [kTab] logical ends
@@ -1069,7 +1083,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   // rotation reads it without an LDS round trip on its own path
   auto put_phase = [&](int sl, int start) {
     if (PE == LAZYATTN_PE_ROPE) {
-      bsh[(wave * 2 + sl) * 64 + lane] = unit_phase_turns(start - p, my_rev);
+      bsh[(wave * kRing + sl) * 64 + lane] = unit_phase_turns(start - p, my_rev);
       __builtin_amdgcn_wave_barrier();
     }
   };
@@ -1093,7 +1107,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
 
       // ---- framed pool: turn the query to this entry's frame, R(p - F) q ----------
       if (PE == kPeFramed && (!q_set || fr != q_frame)) {
-        float2* bw = bsh + (wave * 2 + (q_turns & 1)) * 64;
+        float2* bw = bsh + (wave * kRing + (q_turns & 1)) * 64;
         bw[lane] = unit_phase_turns(p - fr, my_rev);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -1120,7 +1134,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       bf16x8 ka[4];
       if (PE == LAZYATTN_PE_ROPE) {
         // R(S - p) at pair l, written by lane l when the slot was loaded
-        const float2* bw = bsh + (wave * 2 + sl) * 64;
+        const float2* bw = bsh + (wave * kRing + sl) * 64;
         if (KV8) {
           // the lane's 32 codes are in k[0..1]
   #pragma unroll
@@ -1239,30 +1253,31 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     kl = 0;
     if (nk == 0) continue;
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
+    for (int sl = 0; sl < kRing; ++sl) {
       fetch(curb[sl], frb[sl]);
       load_kv(curb[sl].blk, krb[sl], vrb[sl]);
       put_phase(sl, curb[sl].start);
     }
-    // Slot 0 always runs before slot 1 and the pair loop has one exit, after slot
-    // 1's refill: on every path into a slot's processing the other slot's loads
-    // are the newer ones, so the wait for this slot's data leaves them in flight.
-    const int npair = nk >> 1;
-    for (int it = 0; it < npair; ++it) {
-      process(curb[0], frb[0], krb[0], vrb[0], 0);
-      __builtin_amdgcn_sched_barrier(0);
-      fetch(curb[0], frb[0]);
-      load_kv(curb[0].blk, krb[0], vrb[0]);
-      put_phase(0, curb[0].start);
-      process(curb[1], frb[1], krb[1], vrb[1], 1);
-      __builtin_amdgcn_sched_barrier(0);
-      fetch(curb[1], frb[1]);
-      load_kv(curb[1].blk, krb[1], vrb[1]);
-      // a slot's phase row is rewritten only after its entry's reads of it (the
-      // same wave's LDS operations complete in order)
-      put_phase(1, curb[1].start);
+    // The slots run in order and the group loop has one exit, after the last
+    // slot's refill: on every path into a slot's processing the other slots'
+    // loads are the newer ones, so the wait for this slot's data leaves them in
+    // flight.  A slot's phase row is rewritten only after its entry's reads of
+    // it (the same wave's LDS operations complete in order).
+    const int ngrp = nk / kRing;
+    for (int it = 0; it < ngrp; ++it) {
+#pragma unroll
+      for (int sl = 0; sl < kRing; ++sl) {
+        process(curb[sl], frb[sl], krb[sl], vrb[sl], sl);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(curb[sl], frb[sl]);
+        load_kv(curb[sl].blk, krb[sl], vrb[sl]);
+        put_phase(sl, curb[sl].start);
+      }
     }
-    if (nk & 1) process(curb[0], frb[0], krb[0], vrb[0], 0);
+    const int rem = nk - ngrp * kRing;
+#pragma unroll
+    for (int sl = 0; sl + 1 < kRing; ++sl)
+      if (rem > sl) process(curb[sl], frb[sl], krb[sl], vrb[sl], sl);
   }
 
   // ---- merge the four waves ------------------------------------------------------
@@ -1591,7 +1606,7 @@ static lazyattn_status check_batch(const lazyattn_batch* b) {
 constexpr size_t kDecodeLdsFloor = 56 * 1024;
 
 static size_t decode_lds_bytes(int nt) {
-  const size_t need = (4 * 2 * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(nt) * 16 * kOS + 16 * 64 * 2) *
+  const size_t need = (4 * kRing * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(nt) * 16 * kOS + 16 * 64 * 2) *
                       sizeof(float);
   return need > kDecodeLdsFloor ? need : kDecodeLdsFloor;
 }
