@@ -162,6 +162,14 @@ def med(v):
     return v[len(v) // 2]
 
 
+def require_finite(torch, what, *outs):
+    """Every timed call's output must be finite: NaN or inf there would mean the call
+    read pool slots its setup never wrote, so it did not time the real workload."""
+    for o in outs:
+        if not bool(torch.isfinite(o.float()).all()):
+            raise RuntimeError(f"{what}: non-finite output; the benchmark's inputs are not set up")
+
+
 def pct(v):
     v = sorted(v)
     return [v[len(v) // 10], v[len(v) // 2], v[(9 * len(v)) // 10]]
@@ -267,6 +275,7 @@ def bench_headline(torch, args, W, staging, _abi):
     st_none = timer.steps(fns_none, max(5, args.steps // 2), cold=True)
     warm = timer.span(lambda: call.run(pools), max(5, args.steps // 2))
     warm_none = timer.span(lambda: call_none.run(pools), max(5, args.steps // 2))
+    require_finite(torch, "70B prefill", call.out, call_none.out)
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
     pre = dict(ms=sum(step_ms) / len(step_ms), step_ms=step_ms, kern_ms=kern_ms, flops=flops, splits=call.splits,
                none_kern_ms=[x[0] for x in st_none], warm_ms=warm, warm_none_ms=warm_none,
@@ -291,6 +300,7 @@ def bench_headline(torch, args, W, staging, _abi):
         cold = timer.steps(fns, n, cold=True, arg=True)
         warm = timer.steps([lambda i, cs=cs: (cs[i].run(pools), cs[i].run(pools), cs[i].run(pools))], n,
                            cold=False, arg=True)
+        require_finite(torch, f"70B decode ({tag})", *[c.out for c in cs])
         dec[tag] = dict(cold_att=[x[0] for x in cold], cold_merge=[x[1] for x in cold],
                         warm_step=[x[0] / 3.0 for x in warm])
     print(f"# headline decode: {sum(dec['rope']['cold_att']) / n * 1e3:.1f} us attention per step (cold)",
@@ -433,6 +443,7 @@ def bench_llama8b_prefill(torch, args, W, staging, _abi):
         res[tag] = dict(cold_att=med([x[0] for x in cold]), cold_step=med([sum(x) for x in cold]),
                         warm_att=med([timer.span(lambda c=c, p=p: c.attend(p), n) for _ in range(3)]),
                         warm_step=med([timer.span(lambda c=c, p=p: c.run(p), n) for _ in range(3)]))
+        require_finite(torch, f"8B prefill ({tag})", c.out)
     del fpools, pools8
     mat = staging.MaterializedPrefill(s, pb, "cuda")
     mat.run(pools)
@@ -516,6 +527,8 @@ def bench_llama8b_decode(torch, args, W, staging, _abi, n_steps: int):
                  fp8=timer.span(lambda: c8.run(pools8), 3), fp8f=timer.span(lambda: c8f.run(fpools8), 3))
         if step < 0:
             continue
+        if step in (0, n_steps - 1):
+            require_finite(torch, f"8B decode step {step}", call.out, cn.out, cf.out, c8.out, c8f.out)
         if step % 64 == 63:
             print(f"# 8B decode step {step + 1}/{n_steps}", file=sys.stderr, flush=True)
         for k in acc:
@@ -603,6 +616,7 @@ def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
             tp = med([timer.span(lambda: pc.run(pools), 10) for _ in range(3)])
             td = med([timer.span(lambda: dc.run(pools), 10) for _ in range(3)])
             tm = med([timer.span(lambda: mixed(pc, dc, pools), 10) for _ in range(3)])
+            require_finite(torch, f"MQA stress skew {skew} ({pe})", pc.out, dc.out)
             row[pe] = {"prefill_us": round(tp * 1e3, 2), "prefill_TFLOPs": round(flops / (tp * 1e-3) / 1e12, 1),
                        "decode_us": round(td * 1e3, 2),
                        "decode_GBps_unique": round(by["unique"] / (td * 1e-3) / 1e9, 1),

@@ -980,7 +980,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + 256 * q, i = idx >> 6, l = idx & 63;
       const int pair = KV8 ? 16 * (l >> 4) + i : 16 * (i >> 2) + 4 * (l >> 4) + (i & 3);   // c0(i / 4) / 2 + i % 4
-      rtab[idx] = unit_phase(l & 15, A.rope.rev[pair]);
+      rtab[idx] = unit_phase_turns(l & 15, A.rope.rev[pair]);
     }
     __syncthreads();
   }
@@ -1080,10 +1080,28 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   };
   // RoPE: R(S - p) of a slot's entry at pair l, formed by lane l into the slot's
   // LDS row as soon as the entry's loads are issued, so that the entry's
-  // rotation reads it without an LDS round trip on its own path
+  // rotation reads it without an LDS round trip on its own path.  A wave's
+  // entries are four apart: when the next one starts 64 positions after the
+  // previous (four whole blocks on), its phase is the previous one times
+  // R(64), for at most 32 steps in a row (rounding then adds at most ~1e-5 to
+  // a unit phase, far under the bf16 rounding of the rotated key); otherwise
+  // it is formed afresh from the angle reduced in fp64.
+  float2 ph_prev = make_float2(1.f, 0.f), r64 = make_float2(1.f, 0.f);
+  int st_prev = 0, ph_run = 32;
+  if (PE == LAZYATTN_PE_ROPE) r64 = unit_phase(4 * kBlock, my_rev);
   auto put_phase = [&](int sl, int start) {
     if (PE == LAZYATTN_PE_ROPE) {
-      bsh[(wave * kRing + sl) * 64 + lane] = unit_phase_turns(start - p, my_rev);
+      float2 ph;
+      if (start == st_prev + 4 * kBlock && ph_run < 32) {
+        ph = cmul(ph_prev, r64);
+        ++ph_run;
+      } else {
+        ph = unit_phase_turns(start - p, my_rev);
+        ph_run = 0;
+      }
+      ph_prev = ph;
+      st_prev = start;
+      bsh[(wave * kRing + sl) * 64 + lane] = ph;
       __builtin_amdgcn_wave_barrier();
     }
   };

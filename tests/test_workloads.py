@@ -153,3 +153,23 @@ def test_decode_step_bookkeeping():
         assert d["slots"][0] == b * 16 + row
     hist = wl.tokens_before_step(5)
     assert hist["slots"].size == 3 * (q.q_len + 5)
+
+
+def test_tokens_before_every_step_cover_each_step_token():
+    # before step s: each decode request's suffix and steps 0..s-1, the same
+    # values and slots as decode_step writes; s may be the number of decode steps
+    # (every token written), where no decode step remains
+    n = 6
+    wl = W.build_workload(W.spec(3, requests=[3], n_decode=n))
+    for s in (0, 1, n - 1, n, n + 3):
+        hist = wl.tokens_before_step(s)
+        q_len = wl.requests[0].q_len
+        assert hist["slots"].size == 3 * (q_len + min(s, n))
+        assert np.unique(hist["slots"]).size == hist["slots"].size
+        for step in range(min(s, n)):
+            d = wl.decode_step(step)
+            for r in range(3):
+                i = int(np.flatnonzero(hist["slots"] == d["slots"][r])[0])
+                np.testing.assert_array_equal(hist["k_new"][i], d["k_new"][r])
+                np.testing.assert_array_equal(hist["v_new"][i], d["v_new"][r])
+    assert wl.decode_step(n) is None

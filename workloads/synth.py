@@ -475,8 +475,10 @@ class Workload:
 
     def tokens_before_step(self, step: int) -> Optional[dict]:
         """Every new token of the decode requests written before decode step ``step``:
-        their prefill suffix and decode steps 0..step-1, as one batch of (k, v, slots)."""
-        reqs = self.decode_requests(step)
+        their prefill suffix and their decode steps 0..step-1 (a request with fewer
+        decode steps contributes all of its own; ``step`` may be the number of decode
+        steps, i.e. every token written), as one batch of (k, v, slots)."""
+        reqs = [q for q in self.requests if q.n_decode > 0]
         ks, vs, slots, fidx = [], [], [], []
         for q in reqs:
             if q.q_len > 0:
@@ -487,7 +489,7 @@ class Workload:
                     b, row = self.new_token_slot(q, i)
                     slots.append(b * self.B + row)
                     fidx.append(i)
-            for s in range(step):
+            for s in range(min(step, q.n_decode)):
                 rk = self._phase_rng(5, q.index, 1 + s)
                 ks.append(self._values(rk, (1, self.Hkv, self.D)))
                 vs.append(self._values(rk, (1, self.Hkv, self.D)))
