@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "lazyattn_pack_entries": (I32, [P, P, I64, P]),
             "lazyattn_validate_tables": (I32, [CP, P, I32, I32, P, P, I64, P, P]),
             "lazyattn_prefill_splits": (I32, [CP, I32, I32, I32]),
+            "lazyattn_prefill_splits_balanced": (I32, [CP, I32, I32, I32, I64]),
             "lazyattn_decode_splits": (I32, [CP, I32, I32]),
             "lazyattn_prefill_workspace_size": (SZ, [CP, I32, I32, I32, I32, I32]),
             "lazyattn_decode_workspace_size": (SZ, [CP, I32, I32, I32]),
@@ -209,6 +210,10 @@ def validate_tables(cfg: Config, tables: np.ndarray, num_entries: np.ndarray, ct
 
 def prefill_splits(cfg: Config, num_reqs: int, max_q_len: int, max_entries: int) -> int:
     return lib().lazyattn_prefill_splits(ctypes.byref(cfg), num_reqs, max_q_len, max_entries)
+
+
+def prefill_splits_balanced(cfg: Config, num_reqs: int, max_q_len: int, max_entries: int, total_entries: int) -> int:
+    return lib().lazyattn_prefill_splits_balanced(ctypes.byref(cfg), num_reqs, max_q_len, max_entries, total_entries)
 
 
 def decode_splits(cfg: Config, num_reqs: int, max_entries: int) -> int:

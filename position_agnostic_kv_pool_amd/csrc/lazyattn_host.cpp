@@ -219,6 +219,18 @@ int32_t lazyattn_prefill_splits(const lazyattn_config* cfg, int32_t num_reqs, in
   return choose_prefill_splits(cfg, num_reqs, max_q_len, max_entries);
 }
 
+int32_t lazyattn_prefill_splits_balanced(const lazyattn_config* cfg, int32_t num_reqs, int32_t max_q_len,
+                                         int32_t max_entries, int64_t total_entries) {
+  if (check_config(cfg) != LAZYATTN_OK) return 0;
+  int s = choose_prefill_splits(cfg, num_reqs, max_q_len, max_entries);
+  if (num_reqs < 1 || total_entries < 1 || max_entries < 1 || cfg->dtype != LAZYATTN_BF16) return s;
+  // ceil(longest / mean): the longest request's share per work-group comes down to about the mean's
+  const long long imb = (static_cast<long long>(max_entries) * num_reqs + total_entries - 1) / total_entries;
+  const long long cap = std::max(1, max_entries / 64);   // at least 16 key tiles per split
+  const long long want = std::min<long long>(imb, cap);
+  return static_cast<int32_t>(std::max<long long>(s, std::min<long long>(want, 64)));
+}
+
 int32_t lazyattn_decode_splits(const lazyattn_config* cfg, int32_t num_reqs, int32_t max_entries) {
   if (check_config(cfg) != LAZYATTN_OK) return 0;
   return choose_decode_splits(cfg, num_reqs, max_entries);

@@ -7,6 +7,8 @@ host codec.  No attention arithmetic happens here.
 """
 from __future__ import annotations
 
+from typing import Optional
+
 import numpy as np
 import torch
 
@@ -143,8 +145,10 @@ def append_tokens(cfg, pools: DevicePools, inputs: dict, dtype: str, device="cud
 class PrefillCall:
     """Device inputs and output/workspace buffers of one prefill call."""
 
-    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None,
-                 framed: bool = False):
+    def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: Optional[int] = None,
+                 block_permutation=None, framed: bool = False):
+        """num_splits: None = chosen here from the batch's table lengths (known on the host) with
+        lazyattn_prefill_splits_balanced; 0 = the library's own heuristic; > 0 = that many."""
         self.cfg = cfg
         self.tables = DeviceTables.from_inputs(inputs, device, block_permutation, framed)
         self.q = to_device(inputs["q"], spec.dtype, device)
@@ -152,8 +156,11 @@ class PrefillCall:
         self.total_q = int(inputs["total_q"])
         self.max_q_len = int(inputs["max_q_len"])
         self.out = torch.empty_like(self.q)
-        self.num_splits = num_splits
         R = len(inputs["ctx_lens"])
+        if num_splits is None:
+            num_splits = _abi.prefill_splits_balanced(cfg, R, self.max_q_len, self.tables.batch.max_entries,
+                                                      int(np.sum(inputs["num_entries"], dtype=np.int64)))
+        self.num_splits = num_splits
         self.splits = num_splits if num_splits > 0 else \
             _abi.prefill_splits(cfg, R, self.max_q_len, self.tables.batch.max_entries)
         ws = _abi.prefill_workspace_size(cfg, R, self.total_q, self.max_q_len, self.tables.batch.max_entries,

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _abi.lib().lazyattn_abi_version() == 5
+    assert _abi.lib().lazyattn_abi_version() == 6
     for s in range(5):
         assert len(_abi.status_string(s)) > 0
     assert _abi.status_string(99) == "unknown status"
@@ -252,3 +252,21 @@ def test_config_frequency_table_checks():
     assert not check(_cfg(inv_freq=np.full(64, -1.0)))
     assert not check(_cfg(inv_freq=np.full(64, np.inf)))
     assert not check(_cfg(inv_freq=np.full(64, np.nan)))
+
+
+def test_balanced_prefill_splits():
+    c = _cfg(num_q_heads=32, num_kv_heads=1)
+    # equal lengths: the plain heuristic (one 128-token query tile per request gives 512 work-groups)
+    assert _abi.prefill_splits_balanced(c, 32, 128, 651, 32 * 651) == _abi.prefill_splits(c, 32, 128, 651) == 1
+    # the longest request 2.2x the mean: three splits bring its share per work-group to the mean's
+    assert _abi.prefill_splits_balanced(c, 32, 128, 1445, 20832) == 3
+    assert _abi.prefill_splits_balanced(c, 32, 128, 969, 16000) == 2
+    # never fewer than the plain heuristic (8B shape: too few work-groups, 2 splits)
+    c8 = _cfg(num_q_heads=32, num_kv_heads=8)
+    assert _abi.prefill_splits_balanced(c8, 16, 64, 260, 16 * 260) == _abi.prefill_splits(c8, 16, 64, 260) == 2
+    # at most one split per 64 entries of the longest request, and at most 64
+    assert _abi.prefill_splits_balanced(c, 100, 4096, 100, 100) == 1
+    assert _abi.prefill_splits_balanced(c, 1000, 4096, 100000, 100000) == 64
+    # no lengths given, or an invalid config
+    assert _abi.prefill_splits_balanced(c, 32, 128, 1445, 0) == _abi.prefill_splits(c, 32, 128, 1445)
+    assert _abi.prefill_splits_balanced(_cfg(num_q_heads=3, num_kv_heads=2), 1, 1, 1, 1) == 0
