@@ -246,6 +246,41 @@ class Timer:
         t.cuda.synchronize()
         return [[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(fns))] for i in range(n)]
 
+    def rounds(self, variants, n, cold=True, arg=False):
+        """n rounds; each times one step of every variant (a list of functions, as for
+        steps()), in an order rotated by one place per round, each step cold as in steps().
+        Variants compared this way see the same clocks and temperatures on average, so
+        their ratios carry no drift over the run.  Returns, per variant, its per-step
+        lists of per-function ms."""
+        t = self.torch
+        k = len(variants)
+        ev = [[[t.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n)]
+              for fns in variants]
+        t.cuda.synchronize()
+        self.busy()
+        for i in range(n):
+            for j in range(k):
+                v = (i + j) % k
+                if cold:
+                    self.flush(i)
+                ev[v][i][0].record()
+                for m, fn in enumerate(variants[v]):
+                    fn(i) if arg else fn()
+                    ev[v][i][m + 1].record()
+        t.cuda.synchronize()
+        return [[[e[i][m].elapsed_time(e[i][m + 1]) for m in range(len(fns))] for i in range(n)]
+                for e, fns in zip(ev, variants)]
+
+    def span_rounds(self, fns, n, reps=3):
+        """Median ms per call of each function over reps rounds of back-to-back spans of n
+        calls, the functions' order rotated by one place per round."""
+        out = [[] for _ in fns]
+        for r in range(reps):
+            for j in range(len(fns)):
+                v = (r + j) % len(fns)
+                out[v].append(self.span(fns[v], n))
+        return [med(x) for x in out]
+
 
 # ---------------------------------------------------------------------------
 # the headline: Llama-3.1-70B 32k chunk prefill, then its decode steps
@@ -272,13 +307,15 @@ def bench_headline(torch, args, W, staging, _abi):
     step_ms = [sum(x) for x in st]
     kern_ms = [x[0] for x in st]
     print(f"# headline prefill: {sum(step_ms) / len(step_ms) * 1e3:.1f} us/step (cold)", file=sys.stderr, flush=True)
-    st_none = timer.steps(fns_none, max(5, args.steps // 2), cold=True)
-    warm = timer.span(lambda: call.run(pools), max(5, args.steps // 2))
-    warm_none = timer.span(lambda: call_none.run(pools), max(5, args.steps // 2))
+    # RoPE against the rotation-free control: alternating cold steps, then alternating warm spans
+    st_rope, st_none = timer.rounds([fns, fns_none], max(6, args.steps // 2), cold=True)
+    warm, warm_none = timer.span_rounds([lambda: call.run(pools), lambda: call_none.run(pools)],
+                                        max(3, args.steps // 4))
     require_finite(torch, "70B prefill", call.out, call_none.out)
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
     pre = dict(ms=sum(step_ms) / len(step_ms), step_ms=step_ms, kern_ms=kern_ms, flops=flops, splits=call.splits,
-               none_kern_ms=[x[0] for x in st_none], warm_ms=warm, warm_none_ms=warm_none,
+               rope_kern_ms=[x[0] for x in st_rope], none_kern_ms=[x[0] for x in st_none],
+               warm_ms=warm, warm_none_ms=warm_none,
                seq_len=int(max(pb["ctx_lens"])), R=len(pb["ctx_lens"]))
     del call, call_none
 
@@ -294,15 +331,17 @@ def bench_headline(torch, args, W, staging, _abi):
     torch.cuda.synchronize()
     for c in calls[:3]:
         c.run(pools)
+    # every step cold, the RoPE kernel and the rotation-free control in alternating order;
+    # then warm (three back-to-back calls of the step), alternating the same way
     dec = {}
-    for tag, cs in (("rope", calls), ("none", calls_none)):
-        fns = [lambda i, cs=cs: cs[i].attend(pools), lambda i, cs=cs: cs[i].merge()]
-        cold = timer.steps(fns, n, cold=True, arg=True)
-        warm = timer.steps([lambda i, cs=cs: (cs[i].run(pools), cs[i].run(pools), cs[i].run(pools))], n,
-                           cold=False, arg=True)
+    variants = [[lambda i, cs=cs: cs[i].attend(pools), lambda i, cs=cs: cs[i].merge()] for cs in (calls, calls_none)]
+    cold = timer.rounds(variants, n, cold=True, arg=True)
+    warm = timer.rounds([[lambda i, cs=cs: (cs[i].run(pools), cs[i].run(pools), cs[i].run(pools))]
+                         for cs in (calls, calls_none)], n, cold=False, arg=True)
+    for v, (tag, cs) in enumerate((("rope", calls), ("none", calls_none))):
         require_finite(torch, f"70B decode ({tag})", *[c.out for c in cs])
-        dec[tag] = dict(cold_att=[x[0] for x in cold], cold_merge=[x[1] for x in cold],
-                        warm_step=[x[0] / 3.0 for x in warm])
+        dec[tag] = dict(cold_att=[x[0] for x in cold[v]], cold_merge=[x[1] for x in cold[v]],
+                        warm_step=[x[0] / 3.0 for x in warm[v]])
     print(f"# headline decode: {sum(dec['rope']['cold_att']) / n * 1e3:.1f} us attention per step (cold)",
           file=sys.stderr, flush=True)
     # decode step 0's own chunk list (each entry's K and V chunk of every KV head, in the
@@ -357,8 +396,12 @@ def headline_json(h, args):
                 "launch_us_warm_back_to_back": round(pre["warm_ms"] * 1e3, 2),
                 "note": "achieved = algorithmic FLOPs / median cold launch (the kernel's own events)"}
     none_med = med(pre["none_kern_ms"])
-    rope_overhead = {"prefill_rope_us_cold": round(k_med * 1e3, 2), "prefill_norotation_us_cold": round(none_med * 1e3, 2),
-                     "prefill_overhead_cold": round(k_med / none_med - 1.0, 4),
+    rope_med = med(pre["rope_kern_ms"])
+    rope_overhead = {"what": "RoPE kernel against the rotation-free control on the same inputs, timed in "
+                             "alternating order (medians)",
+                     "prefill_rope_us_cold": round(rope_med * 1e3, 2),
+                     "prefill_norotation_us_cold": round(none_med * 1e3, 2),
+                     "prefill_overhead_cold": round(rope_med / none_med - 1.0, 4),
                      "prefill_rope_us_warm": round(pre["warm_ms"] * 1e3, 2),
                      "prefill_norotation_us_warm": round(pre["warm_none_ms"] * 1e3, 2),
                      "prefill_overhead_warm": round(pre["warm_ms"] / pre["warm_none_ms"] - 1.0, 4),
@@ -436,13 +479,15 @@ def bench_llama8b_prefill(torch, args, W, staging, _abi):
     timer.span(lambda: call.attend(pools), 200)        # clocks settle
     n = 20
     res = {}
-    for tag, c, p in (("rope", call, pools), ("none", call_none, pools), ("framed", call_framed, fpools),
-                      ("fp8", call8, pools8)):
-        fns = [lambda c=c, p=p: c.attend(p)] + ([c.merge] if c.splits > 1 else [])
-        cold = timer.steps(fns, n, cold=True)
-        res[tag] = dict(cold_att=med([x[0] for x in cold]), cold_step=med([sum(x) for x in cold]),
-                        warm_att=med([timer.span(lambda c=c, p=p: c.attend(p), n) for _ in range(3)]),
-                        warm_step=med([timer.span(lambda c=c, p=p: c.run(p), n) for _ in range(3)]))
+    # the four variants in alternating order (cold steps, then warm spans)
+    cases = (("rope", call, pools), ("none", call_none, pools), ("framed", call_framed, fpools), ("fp8", call8, pools8))
+    cold = timer.rounds([[lambda c=c, p=p: c.attend(p)] + ([c.merge] if c.splits > 1 else []) for _, c, p in cases],
+                        n, cold=True)
+    warm_att = timer.span_rounds([lambda c=c, p=p: c.attend(p) for _, c, p in cases], n)
+    warm_step = timer.span_rounds([lambda c=c, p=p: c.run(p) for _, c, p in cases], n)
+    for v, (tag, c, p) in enumerate(cases):
+        res[tag] = dict(cold_att=med([x[0] for x in cold[v]]), cold_step=med([sum(x) for x in cold[v]]),
+                        warm_att=warm_att[v], warm_step=warm_step[v])
         require_finite(torch, f"8B prefill ({tag})", c.out)
     del fpools, pools8
     mat = staging.MaterializedPrefill(s, pb, "cuda")
@@ -520,8 +565,9 @@ def bench_llama8b_decode(torch, args, W, staging, _abi, n_steps: int):
         c8 = staging.DecodeCall(cfg8, s, d, "cuda")
         c8f = staging.DecodeCall(cfg8, s, d, "cuda", framed=True)
         splits = call.splits
-        cold = timer.steps([lambda: call.run(pools)], 1, cold=True)[0][0]
-        cold_none = timer.steps([lambda: cn.run(pools)], 1, cold=True)[0][0]
+        pair = timer.rounds([[lambda: call.run(pools)], [lambda: cn.run(pools)]], 2, cold=True)
+        cold = med([x[0] for x in pair[0]])
+        cold_none = med([x[0] for x in pair[1]])
         t = dict(cold=cold, cold_none=cold_none, warm=timer.span(lambda: call.run(pools), 3),
                  none=timer.span(lambda: cn.run(pools), 3), framed=timer.span(lambda: cf.run(fpools), 3),
                  fp8=timer.span(lambda: c8.run(pools8), 3), fp8f=timer.span(lambda: c8f.run(fpools8), 3))
@@ -606,17 +652,22 @@ def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
         flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
         by = decode_bytes(d, wl)
         row = {}
-        for pe in ("rope", "alibi", "none"):
+        pes = ("rope", "alibi", "none")
+        pcs, dcs = {}, {}
+        for pe in pes:
             c = staging.config_for(s, pe=pe)
-            pc = staging.PrefillCall(c, s, pb, "cuda")
-            dc = staging.DecodeCall(c, s, d, "cuda")
-            pc.run(pools)
-            dc.run(pools)
-            mixed(pc, dc, pools)
-            tp = med([timer.span(lambda: pc.run(pools), 10) for _ in range(3)])
-            td = med([timer.span(lambda: dc.run(pools), 10) for _ in range(3)])
-            tm = med([timer.span(lambda: mixed(pc, dc, pools), 10) for _ in range(3)])
-            require_finite(torch, f"MQA stress skew {skew} ({pe})", pc.out, dc.out)
+            pcs[pe] = staging.PrefillCall(c, s, pb, "cuda")
+            dcs[pe] = staging.DecodeCall(c, s, d, "cuda")
+            pcs[pe].run(pools)
+            dcs[pe].run(pools)
+            mixed(pcs[pe], dcs[pe], pools)
+        # the three encodings in alternating order: prefill, decode, mixed step
+        tps = timer.span_rounds([lambda pc=pcs[pe]: pc.run(pools) for pe in pes], 10)
+        tds = timer.span_rounds([lambda dc=dcs[pe]: dc.run(pools) for pe in pes], 10)
+        tms = timer.span_rounds([lambda pe=pe: mixed(pcs[pe], dcs[pe], pools) for pe in pes], 10)
+        for v, pe in enumerate(pes):
+            tp, td, tm = tps[v], tds[v], tms[v]
+            require_finite(torch, f"MQA stress skew {skew} ({pe})", pcs[pe].out, dcs[pe].out)
             row[pe] = {"prefill_us": round(tp * 1e3, 2), "prefill_TFLOPs": round(flops / (tp * 1e-3) / 1e12, 1),
                        "decode_us": round(td * 1e3, 2),
                        "decode_GBps_unique": round(by["unique"] / (td * 1e-3) / 1e9, 1),
