@@ -325,13 +325,27 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     slope[nt] = (PE == LAZYATTN_PE_ALIBI) ? alibi_slope(A.alibi, head[nt], Hq) * kLog2e : 0.0f;
   }
 
+  // Where a tile's staging work goes.  Without per-row work on the staged keys
+  // (no rotation, no FP8 conversion) the QK products leave issue slots free,
+  // and the staging is spread among them (the rotation-free and ALiBi kernels
+  // run 3-8 % faster than with it after the products).  Otherwise those slots
+  // hold the rotation, and the staging stays between the QK and P.V phases,
+  // where it measured fastest.
+  constexpr bool kStageEarly = !KV8 && (PE == LAZYATTN_PE_NONE || PE == LAZYATTN_PE_ALIBI);
+
   // ---- table words: lanes x = 0..4 (mod 8) hold word e0 + x of a tile ------------
+  // Where the staging work is spread among the QK products (kStageEarly) every
+  // lane loads, at an index clamped into the table, so that the load is not
+  // predicated (no branch), and entry_of ignores the words past the table's
+  // end; otherwise a lane past the end holds the sentinel start L (and the
+  // compiler predicates the load).  Nearest-first: tiles past the last (j >= T)
+  // lie below e_begin.
   const uint64_t sentinel = static_cast<uint64_t>(static_cast<uint32_t>(L)) << 32;   // start = L
   auto load_words = [&](int j) -> uint64_t {
     const int x = lane & 7;
     const int e = tile_e0(j) + x;
-    // nearest-first: tiles past the last (j >= T) lie below e_begin
     const uint64_t w = trow[kNearestFirst ? max(min(e, ne - 1), 0) : min(e, ne - 1)];
+    if (kStageEarly) return w;
     return (x < 5 && e < ne && (!kNearestFirst || e >= e_begin)) ? w : sentinel;
   };
   // entry x of the tile whose words are in wv: (block, start, length); past the
@@ -340,8 +354,9 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     const uint32_t lo_w = static_cast<uint32_t>(wv), hi_w = static_cast<uint32_t>(wv >> 32);
     const int b = __builtin_amdgcn_readlane(static_cast<int>(lo_w), x);
     const int s0 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x);
-    const int s1 = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x + 1);
+    const int s1w = __builtin_amdgcn_readlane(static_cast<int>(hi_w), x + 1);
     const int e = tile_e0(j) + x;
+    const int s1 = (!kStageEarly || e + 1 < ne) ? s1w : L;   // the next entry's start, or the context's end
     const bool valid = e < e_stop && (!kNearestFirst || e >= e_begin);
     blk = valid ? b : 0;
     st = valid ? s0 : L;
@@ -388,15 +403,24 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   uint2 kx = make_uint2(0, 0), vx = make_uint2(0, 0);
   // entries past the split's end (length 0) read block 0: their keys are
   // masked out of the scores and their V rows zeroed when staged
-  auto load_kv = [&](int blk) {
+  auto load_k = [&](int blk) {
     const size_t base = static_cast<size_t>(static_cast<uint32_t>(blk)) * Hkv + kvh;
     if (KV8) {
       const uint8_t* kc = reinterpret_cast<const uint8_t*>(A.kpool) + base * kChunk8;
-      const uint8_t* vc = reinterpret_cast<const uint8_t*>(A.vpool) + base * kChunk8;
       const uint16_t* kp = reinterpret_cast<const uint16_t*>(kc + 8 * part * kPD) + lane;
 #pragma unroll
       for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
       kx = *reinterpret_cast<const uint2*>(kc + 16 * kPD + 8 * part);
+    } else {
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(A.kpool + base * (kBlock * kPD) + 8 * part * kPD) + lane;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
+    }
+  };
+  auto load_v = [&](int blk) {
+    const size_t base = static_cast<size_t>(static_cast<uint32_t>(blk)) * Hkv + kvh;
+    if (KV8) {
+      const uint8_t* vc = reinterpret_cast<const uint8_t*>(A.vpool) + base * kChunk8;
       const uint8_t* vp = vc + (64 * part + (lane >> 1)) * kBlock + 8 * (lane & 1);
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -405,13 +429,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       }
       vx = *reinterpret_cast<const uint2*>(vc + 16 * kPD + 8 * (lane & 1));
     } else {
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(A.kpool + base * (kBlock * kPD) + 8 * part * kPD) + lane;
       const uint16_t* vp = A.vpool + base * (kPD * kBlock) + (64 * part + (lane >> 1)) * kBlock + 8 * (lane & 1);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) vr[cc] = *reinterpret_cast<const uint4*>(vp + 32 * cc * kBlock);
     }
+  };
+  auto load_kv = [&](int blk) {
+    load_k(blk);
+    load_v(blk);
   };
   // FP8: the staged key row k (its codes, times 2^exponent) as bf16, turned by ph
   // for RoPE; V codes times their tokens' 2^exponent as bf16.  Exact but for
@@ -450,14 +475,20 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       vr[cc] = make_uint4(vr[cc].x & keep[0], vr[cc].y & keep[1], vr[cc].z & keep[2], vr[cc].w & keep[3]);
   };
   // write the staged K~ and V into LDS buffer b
-  auto stage_write = [&](int b) {
+  auto stage_write_k = [&](int b) {
     uint32_t* kdst = reinterpret_cast<uint32_t*>(Ks[b]) + lane;
-    uint16_t* vdst = Vs[b] + E_own * kVEs + (lane & 1) * kVH;
 #pragma unroll
     for (int k = 0; k < 8; ++k) kdst[krow_of(E_own, 8 * part + k) * (kKS / 2)] = kr[k];
+  };
+  auto stage_write_v = [&](int b) {
+    uint16_t* vdst = Vs[b] + E_own * kVEs + (lane & 1) * kVH;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
       *reinterpret_cast<uint4*>(&vdst[(64 * part + 32 * cc + (lane >> 1)) * 8]) = vr[cc];
+  };
+  auto stage_write = [&](int b) {
+    stage_write_k(b);
+    stage_write_v(b);
   };
 
   // ---- query: rotated by R(m), scaled by scale*log2(e), rounded to bf16 -----------
@@ -596,17 +627,29 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
           for (int nt = 0; nt < NT; ++nt) S[tau][nt] = mfma32x32x16(ak[kk & 1][tau], qf[8 * nt + kk], S[tau][nt]);
         stage_row(kk, ph, pq);
       }
-      // rare: only entries shorter than a block need their padding zeroed
-      if (__builtin_expect(nln < kBlock, 0)) mask_v(nln);
-      stage_write((i + 1) & 1);
-      // words of tile i + 3, then the loads of tile i + 2 (in this order, the
-      // copies of the word registers at the end of the tile wait for the word
-      // load only, not for the K/V loads issued after it)
+      // Staging of the next tiles, then the words of tile i + 3 before the loads
+      // of tile i + 2 (in this order, the copies of the word registers at the
+      // end of the tile wait for the word load only, not for the K/V loads
+      // issued after it).
       int lblk, lst, lln;
-      entry_of(wv2, i + 2, E_own, lblk, lst, lln);
-      wv3 = load_words(i + 3);
-      fv3 = load_frames(i + 3);
-      load_kv(lblk);
+      if constexpr (kStageEarly) {
+        // K~ of tile i + 1 (never masked: the scores of padded keys are) and the
+        // K loads here, V at the P.V products: no branch separates this work
+        // from the QK products, so that the scheduler spreads it among them
+        stage_write_k((i + 1) & 1);
+        entry_of(wv2, i + 2, E_own, lblk, lst, lln);
+        wv3 = load_words(i + 3);
+        fv3 = load_frames(i + 3);
+        load_k(lblk);
+      } else {
+        // rare: only entries shorter than a block need their padding zeroed
+        if (__builtin_expect(nln < kBlock, 0)) mask_v(nln);
+        stage_write((i + 1) & 1);
+        entry_of(wv2, i + 2, E_own, lblk, lst, lln);
+        wv3 = load_words(i + 3);
+        fv3 = load_frames(i + 3);
+        load_kv(lblk);
+      }
 
       // register r of half tau: key row 8 h + (r % 8) of entry 2 tau + r / 8
       if (PE == LAZYATTN_PE_ALIBI) {
@@ -620,17 +663,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
               S[tau][nt][rr] -= slope[nt] * static_cast<float>(p_row[nt] - t);
             }
       }
-      if (!full) {
+      // rare: a tile with padded or invisible keys, or a staged entry shorter
+      // than a block (its V padding is zeroed: the pool may hold anything there)
+      if (__builtin_expect(!full || (kStageEarly && nln < kBlock), 0)) {
+        if (kStageEarly && nln < kBlock) mask_v(nln);
+        if (!full) {
 #pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
+          for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const int E = 2 * tau + (rr >> 3), kr_ = 8 * h + (rr & 7);
-            const int t = st[E] + kr_;
-            const bool live = kr_ < ln[E];
+            for (int rr = 0; rr < 16; ++rr) {
+              const int E = 2 * tau + (rr >> 3), kr_ = 8 * h + (rr & 7);
+              const int t = st[E] + kr_;
+              const bool live = kr_ < ln[E];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) S[tau][nt][rr] = (live && t <= p_row[nt]) ? S[tau][nt][rr] : kNegInf;
-          }
+              for (int nt = 0; nt < NT; ++nt) S[tau][nt][rr] = (live && t <= p_row[nt]) ? S[tau][nt][rr] : kNegInf;
+            }
+        }
       }
       if (maxpass || (fresh && i == 0)) {
         // row maximum of this tile (lanes c and c + 32 hold the two key halves)
@@ -653,6 +701,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
             for (int rr = 0; rr < 16; ++rr) negm[nt][rr] = -mr;
           }
         }
+      }
+      if constexpr (kStageEarly) {
+        // V of tile i + 1, then the V loads of tile i + 2
+        stage_write_v((i + 1) & 1);
+        load_v(lblk);
       }
       if (!maxpass) {
         // P^T operands (weights of keys 8 h .. 8 h + 7 of entry 2 tau + ks) and
