@@ -70,6 +70,7 @@ class Batch(ctypes.Structure):
         ("num_entries", ctypes.c_void_p),
         ("ctx_lens", ctypes.c_void_p),
         ("frame_starts", ctypes.c_void_p),
+        ("req_order", ctypes.c_void_p),
     ]
 
 
@@ -248,9 +249,10 @@ def _stream(stream) -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_batch(tables, num_entries, ctx_lens, frame_starts=None) -> Batch:
+def make_batch(tables, num_entries, ctx_lens, frame_starts=None, req_order=None) -> Batch:
     """Batch over device tensors: tables int64/uint64 [R][E] words, num_entries/ctx_lens int32 [R],
-    optional frame_starts int32 [R][E] (keys stored in document-local frames)."""
+    optional frame_starts int32 [R][E] (keys stored in document-local frames) and req_order
+    int32 [R] (the order in which prefill work-groups take the requests)."""
     b = Batch()
     b.num_reqs = int(num_entries.shape[0])
     b.max_entries = int(tables.shape[1]) if tables.dim() == 2 else 0
@@ -258,7 +260,8 @@ def make_batch(tables, num_entries, ctx_lens, frame_starts=None) -> Batch:
     b.num_entries = _ptr(num_entries)
     b.ctx_lens = _ptr(ctx_lens)
     b.frame_starts = _ptr(frame_starts) if frame_starts is not None else None
-    b._keep = (tables, num_entries, ctx_lens, frame_starts)
+    b.req_order = _ptr(req_order) if req_order is not None else None
+    b._keep = (tables, num_entries, ctx_lens, frame_starts, req_order)
     return b
 
 

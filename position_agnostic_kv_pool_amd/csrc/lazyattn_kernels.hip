@@ -219,11 +219,13 @@ struct PrefillArgs {
   const int32_t* n_ent;
   const int32_t* ctx;
   const int32_t* frames;         // [R][max_entries] frame starts (document-local frames) or NULL
+  const int32_t* order;          // [R] the order in which work-groups take the requests, or NULL
   const float* alibi;
   uint16_t* out;
   uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
   float* ml_part;                // and (m, l) [splits][rows][Hq][2]
   int32_t Hq, Hkv, G, max_entries, total_q, m_q, eps, splits;
+  int32_t n_qt;                  // query tiles per request (the grid's x extent is n_qt * splits)
   int32_t exact;                 // nonzero: always take the two-pass exact-maximum route
   float scale_log2;
   RopeRev rope;
@@ -259,8 +261,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   const int wave = tid >> 6, lane = tid & 63;
   const int ws = __builtin_amdgcn_readfirstlane(wave);
   const int c = lane & 31, h = lane >> 5;
-  const int qt = blockIdx.x, r = blockIdx.y;
-  const int kvh = blockIdx.z % A.Hkv, split = blockIdx.z / A.Hkv;
+  // grid (query tile and split, request, KV head), the query tile fastest: the
+  // work-groups of one request follow each other, in the given request order
+  const int qt = blockIdx.x % A.n_qt, split = blockIdx.x / A.n_qt;
+  const int kvh = blockIdx.z;
+  int r = blockIdx.y;
+  if (A.order) {
+    const int o = A.order[r];
+    r = (o >= 0 && o < static_cast<int>(gridDim.y)) ? o : r;
+  }
   const int q0 = A.cu_q[r];
   const int q_len = A.cu_q[r + 1] - q0;
   const int m0 = qt * A.m_q;
@@ -1732,18 +1741,19 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   const size_t need = lazyattn_prefill_workspace_size(cfg, R, total_q, max_q_len, batch->max_entries, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return LAZYATTN_EWORKSPACE;
   const int m_q = prefill_positions_per_tile(G);
-  const long long gx = (max_q_len + m_q - 1) / m_q;
-  const long long gz = static_cast<long long>(Hkv) * splits;
-  if (R > 65535 || gz > 65535 || gx > 0x7fffffff) return LAZYATTN_EUNSUPPORTED;
+  const long long n_qt = (max_q_len + m_q - 1) / m_q;
+  const long long gx = n_qt * splits;
+  if (R > 65535 || Hkv > 65535 || gx > 0x7fffffff) return LAZYATTN_EUNSUPPORTED;
   uint16_t* o_part = splits > 1 ? static_cast<uint16_t*>(workspace) : nullptr;
   float* ml_part = splits > 1 ? reinterpret_cast<float*>(o_part + static_cast<size_t>(splits) * total_q * Hq * kPD)
                               : nullptr;
   PrefillArgs a{static_cast<const uint16_t*>(q), cu_q_lens, static_cast<const uint16_t*>(k_pool),
                 static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
-                batch->frame_starts, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, Hq, Hkv, G, batch->max_entries,
-                total_q, m_q, prefill_entries_per_split(batch->max_entries, splits), splits,
+                batch->frame_starts, batch->req_order, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part,
+                ml_part, Hq, Hkv, G, batch->max_entries, total_q, m_q,
+                prefill_entries_per_split(batch->max_entries, splits), splits, static_cast<int32_t>(n_qt),
                 (cfg->flags & LAZYATTN_FLAG_EXACT_MAX) ? 1 : 0, scale * kLog2e, rope};
-  const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(gz));
+  const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(Hkv));
   const dim3 block(kPrefillThreads);
   if (fp8) {
     switch (framed ? kPeFramed : cfg->pe) {

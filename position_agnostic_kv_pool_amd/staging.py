@@ -108,7 +108,7 @@ class DeviceTables:
 
     def __init__(self, table_blocks: np.ndarray, table_starts: np.ndarray, num_entries: np.ndarray,
                  ctx_lens: np.ndarray, device="cuda", block_permutation: np.ndarray = None,
-                 frame_starts: np.ndarray = None):
+                 frame_starts: np.ndarray = None, req_order: np.ndarray = None):
         blocks = table_blocks if block_permutation is None else \
             block_permutation[table_blocks.astype(np.int64)].astype(np.uint32)
         self.words_host = _abi.pack_entries(blocks, table_starts)
@@ -117,12 +117,21 @@ class DeviceTables:
         self.ctx_lens = torch.from_numpy(np.ascontiguousarray(ctx_lens, dtype=np.int32)).to(device)
         self.frame_starts = None if frame_starts is None else \
             torch.from_numpy(np.ascontiguousarray(frame_starts, dtype=np.int32)).to(device)
-        self.batch = _abi.make_batch(self.tables, self.num_entries, self.ctx_lens, self.frame_starts)
+        self.req_order = None if req_order is None else \
+            torch.from_numpy(np.ascontiguousarray(req_order, dtype=np.int32)).to(device)
+        self.batch = _abi.make_batch(self.tables, self.num_entries, self.ctx_lens, self.frame_starts,
+                                     self.req_order)
 
     @classmethod
-    def from_inputs(cls, inputs: dict, device="cuda", block_permutation=None, framed=False):
+    def from_inputs(cls, inputs: dict, device="cuda", block_permutation=None, framed=False, req_order=None):
         return cls(inputs["table_blocks"], inputs["table_starts"], inputs["num_entries"], inputs["ctx_lens"],
-                   device, block_permutation, inputs["frame_starts"] if framed else None)
+                   device, block_permutation, inputs["frame_starts"] if framed else None, req_order)
+
+
+def longest_first(num_entries: np.ndarray) -> np.ndarray:
+    """Request order with the longest tables first (ties in batch order): prefill work-groups
+    taking the requests in this order leave the short ones to fill the end of the launch."""
+    return np.argsort(-np.asarray(num_entries, dtype=np.int64), kind="stable").astype(np.int32)
 
 
 def append_tokens(cfg, pools: DevicePools, inputs: dict, dtype: str, device="cuda", block_permutation=None):
@@ -146,11 +155,16 @@ class PrefillCall:
     """Device inputs and output/workspace buffers of one prefill call."""
 
     def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: Optional[int] = None,
-                 block_permutation=None, framed: bool = False):
+                 block_permutation=None, framed: bool = False, req_order="longest_first"):
         """num_splits: None = chosen here from the batch's table lengths (known on the host) with
-        lazyattn_prefill_splits_balanced; 0 = the library's own heuristic; > 0 = that many."""
+        lazyattn_prefill_splits_balanced; 0 = the library's own heuristic; > 0 = that many.
+        req_order: the order in which the work-groups take the requests: "longest_first"
+        (longest table first), None (batch order) or an int32 array; the results are the same."""
         self.cfg = cfg
-        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation, framed)
+        order = longest_first(inputs["num_entries"]) if isinstance(req_order, str) else req_order
+        if isinstance(req_order, str) and req_order != "longest_first":
+            raise ValueError(f"unknown request order {req_order!r}")
+        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation, framed, order)
         self.q = to_device(inputs["q"], spec.dtype, device)
         self.cu_q = torch.from_numpy(inputs["cu_q_lens"].astype(np.int32)).to(device)
         self.total_q = int(inputs["total_q"])

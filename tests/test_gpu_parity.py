@@ -362,6 +362,32 @@ def test_prefill_split_count_invariance_and_empty_splits():
         assert mx <= 4e-3 and mn <= 2e-4
 
 
+def test_prefill_request_order_is_bit_identical():
+    say("prefill: requests taken longest first, reversed, in batch order, or through an out-of-range entry agree bit for bit")
+    wl = W.build_workload(W.spec(5, skew=0.0, requests=[12, 1]))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pb = wl.prefill_batch()
+    R = len(pb["ctx_lens"])
+    pools = staging.DevicePools(wl, DEV)
+    staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+    lf = staging.longest_first(pb["num_entries"])
+    assert sorted(lf.tolist()) == list(range(R)) and np.all(np.diff(pb["num_entries"][lf]) <= 0)
+    odd = np.arange(R, dtype=np.int32)
+    odd[1] = R + 5                                    # stands for its own index, 1
+    orders = [None, "longest_first", np.arange(R, dtype=np.int32)[::-1].copy(), odd]
+    for splits in (1, 3):
+        outs = []
+        for order in orders:
+            call = staging.PrefillCall(cfg, s, pb, DEV, splits, req_order=order)
+            outs.append(call.run(pools).clone())
+        sync()
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0])
+    mx, _ = diff_stats(gpu_f64(outs[0]), run_prefill(wl, num_splits=3, pools=pools, pb=pb)[1])
+    assert mx == 0.0
+
+
 # ---------------------------------------------------------------------------
 # rotation-free and ALiBi instantiations on the same inputs
 # ---------------------------------------------------------------------------
