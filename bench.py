@@ -554,7 +554,8 @@ def bench_llama8b_decode(torch, args, W, staging, _abi, n_steps: int):
     staging.append_tokens(cfg8, fpools8, allt, s.dtype, "cuda")
     torch.cuda.synchronize()
     timer = Timer(torch)
-    acc = {k: 0.0 for k in ("cold", "cold_none", "warm", "none", "framed", "fp8", "fp8f")}
+    acc = {k: 0.0 for k in ("cold", "cold_none", "cold_runs", "warm", "none", "runs", "framed", "fp8", "fp8f",
+                            "plan_ms")}
     tot = {"logical": 0, "unique": 0, "kv_logical": 0}
     splits = 0
     for step in range(-2, n_steps):          # two untimed warm-up rounds on step 0's inputs
@@ -564,17 +565,22 @@ def bench_llama8b_decode(torch, args, W, staging, _abi, n_steps: int):
         cf = staging.DecodeCall(cfg, s, d, "cuda", framed=True)
         c8 = staging.DecodeCall(cfg8, s, d, "cuda")
         c8f = staging.DecodeCall(cfg8, s, d, "cuda", framed=True)
+        t0 = time.perf_counter()
+        cr = staging.RunDecodeCall(cfg, s, d, pools.num_blocks, "cuda")     # host plan + its upload
+        plan_ms = (time.perf_counter() - t0) * 1e3
         splits = call.splits
-        pair = timer.rounds([[lambda: call.run(pools)], [lambda: cn.run(pools)]], 2, cold=True)
-        cold = med([x[0] for x in pair[0]])
-        cold_none = med([x[0] for x in pair[1]])
-        t = dict(cold=cold, cold_none=cold_none, warm=timer.span(lambda: call.run(pools), 3),
-                 none=timer.span(lambda: cn.run(pools), 3), framed=timer.span(lambda: cf.run(fpools), 3),
-                 fp8=timer.span(lambda: c8.run(pools8), 3), fp8f=timer.span(lambda: c8f.run(fpools8), 3))
+        trio = timer.rounds([[lambda: call.run(pools)], [lambda: cn.run(pools)], [lambda: cr.run(pools)]], 2,
+                            cold=True)
+        cold, cold_none, cold_runs = (med([x[0] for x in v]) for v in trio)
+        t = dict(cold=cold, cold_none=cold_none, cold_runs=cold_runs, warm=timer.span(lambda: call.run(pools), 3),
+                 none=timer.span(lambda: cn.run(pools), 3), runs=timer.span(lambda: cr.run(pools), 3),
+                 framed=timer.span(lambda: cf.run(fpools), 3),
+                 fp8=timer.span(lambda: c8.run(pools8), 3), fp8f=timer.span(lambda: c8f.run(fpools8), 3),
+                 plan_ms=plan_ms)
         if step < 0:
             continue
         if step in (0, n_steps - 1):
-            require_finite(torch, f"8B decode step {step}", call.out, cn.out, cf.out, c8.out, c8f.out)
+            require_finite(torch, f"8B decode step {step}", call.out, cn.out, cf.out, c8.out, c8f.out, cr.out)
         if step % 64 == 63:
             print(f"# 8B decode step {step + 1}/{n_steps}", file=sys.stderr, flush=True)
         for k in acc:
@@ -609,6 +615,15 @@ def bench_llama8b_decode(torch, args, W, staging, _abi, n_steps: int):
         "document_frames_overhead_warm": round(a["framed"] / a["none"] - 1.0, 4),
         "fp8_pool_us_warm": round(a["fp8"] * 1e3, 2),
         "fp8_framed_pool_us_warm": round(a["fp8f"] * 1e3, 2),
+        "shared_run_decode": {
+            "what": "lazyattn_decode_runs: the tables cut into runs shared by several requests, each run read "
+                    "once per group of up to 4 requests (G = 4), partials merged per request; the plan is built "
+                    "on the host for every step (plan_host_ms, outside the timed region)",
+            "us_per_step_cold": round(a["cold_runs"] * 1e3, 2), "us_per_step_warm": round(a["runs"] * 1e3, 2),
+            "speedup_vs_per_request_cold": round(a["cold"] / a["cold_runs"], 3),
+            "unique_GBps": round(kv_unique / (a["cold_runs"] * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(kv_unique / (a["cold_runs"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "plan_host_ms_per_step": round(a["plan_ms"], 2)},
     }
     del pools, fpools, pools8, fpools8
     torch.cuda.empty_cache()
@@ -689,6 +704,57 @@ def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
 # ---------------------------------------------------------------------------
 # measured peaks, pool hit ratios, CPU baseline
 # ---------------------------------------------------------------------------
+def bench_tp8_share(torch, W, staging, _abi, n_decode: int = 8) -> dict:
+    """One GPU's share of the Llama-3.1-70B layer under 8-way tensor parallelism over KV heads
+    (Hq 8, Hkv 1, G 8) at the same 32k contexts: the 2048-token chunk and the first decode steps,
+    every step cold.  No exchange is needed between the shares."""
+    import dataclasses
+    sp = dataclasses.replace(W.spec(4, n_decode=n_decode), num_q_heads=8, num_kv_heads=1,
+                             name="llama70b-32k-tp8-share")
+    wl = W.build_workload(sp)
+    s = wl.spec
+    pools = staging.DevicePools(wl, "cuda")
+    pb = wl.prefill_batch()
+    cfg = staging.config_for(s)
+    staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
+    call = staging.PrefillCall(cfg, s, pb, "cuda")
+    timer = Timer(torch)
+    for _ in range(2):
+        call.run(pools)
+    st = timer.steps([lambda: call.attend(pools)] + ([call.merge] if call.splits > 1 else []), 10, cold=True)
+    require_finite(torch, "TP-8 share prefill", call.out)
+    flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
+    att, step = med([x[0] for x in st]), med([sum(x) for x in st])
+    allt = wl.tokens_before_step(n_decode)
+    staging.append_tokens(cfg, pools, allt, s.dtype, "cuda")
+    steps = [wl.decode_step(i) for i in range(n_decode)]
+    calls = [staging.DecodeCall(cfg, s, d, "cuda") for d in steps]
+    by = [decode_bytes(d, wl) for d in steps]
+    for c in calls[:2]:
+        c.run(pools)
+    cold = timer.steps([lambda i: calls[i].attend(pools), lambda i: calls[i].merge()], n_decode, cold=True, arg=True)
+    require_finite(torch, "TP-8 share decode", *[c.out for c in calls])
+    d_att = sum(x[0] for x in cold) / n_decode
+    d_mrg = sum(x[1] for x in cold) / n_decode
+    uniq = sum(b["unique"] for b in by) / n_decode
+    timer.release()
+    out = {
+        "workload": "one GPU's share of the Llama-3.1-70B layer under 8-way tensor parallelism over KV heads: "
+                    "Hq 8, Hkv 1, the same 4 x 32k contexts, 2048-token chunk, then decode steps "
+                    f"0..{n_decode - 1}; cold",
+        "prefill": {"attention_us_cold": round(att * 1e3, 2), "step_us_cold": round(step * 1e3, 2),
+                    "key_splits": call.splits, "TFLOPs_attention": round(flops / (att * 1e-3) / 1e12, 2),
+                    "frac_of_peak": round(flops / (att * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "decode": {"us_per_step_cold": round((d_att + d_mrg) * 1e3, 2),
+                   "attention_us_cold": round(d_att * 1e3, 2), "merge_us_cold": round(d_mrg * 1e3, 2),
+                   "splits": calls[0].splits, "GBps_unique": round(uniq / (d_att * 1e-3) / 1e9, 1),
+                   "frac_of_peak": round(uniq / (d_att * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    del calls, call, pools
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_peaks(torch) -> dict:
     out = {}
     L = probe_lib()
@@ -848,7 +914,7 @@ def main() -> int:
     ap.add_argument("--decode8b-steps", type=int, default=256)
     ap.add_argument("--no-extras", action="store_true", help="headline only (8B and MQA extras, peaks skipped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["llama8b", "mqa", "peaks"], help="run one extra alone (profiling)")
+    ap.add_argument("--only", choices=["llama8b", "mqa", "peaks", "tp8"], help="run one extra alone (profiling)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     args = ap.parse_args()
@@ -880,6 +946,8 @@ def main() -> int:
                    "llama8b_decode": bench_llama8b_decode(torch, args, W, staging, _abi, args.decode8b_steps)}
         elif args.only == "mqa":
             res = {"mqa_mixed": bench_mqa_mixed(torch, W, staging, _abi)}
+        elif args.only == "tp8":
+            res = {"llama70b_tp8_share": bench_tp8_share(torch, W, staging, _abi)}
         else:
             res = {"measured_peaks": measured_peaks(torch)}
         print(json.dumps(res), flush=True)
@@ -899,6 +967,8 @@ def main() -> int:
         print("# 8B decode done", file=sys.stderr, flush=True)
         out["mqa_mixed"] = bench_mqa_mixed(torch, W, staging, _abi)
         print("# MQA mixed done", file=sys.stderr, flush=True)
+        out["llama70b_tp8_share"] = bench_tp8_share(torch, W, staging, _abi)
+        print("# 70B TP-8 share done", file=sys.stderr, flush=True)
         out["pool_hit_ratio"] = hit_ratio_study(W, _abi)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(h)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LAZYATTN_ABI_VERSION 7
+#define LAZYATTN_ABI_VERSION 8
 
 typedef enum {
   LAZYATTN_OK = 0,
@@ -285,6 +285,87 @@ lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const
 lazyattn_status lazyattn_decode_noalloc(const lazyattn_config* cfg, const void* q, const void* k_pool,
                                         const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
                                         int32_t num_splits, void* out, hipStream_t stream);
+
+/* ---- decode over shared runs ----------------------------------------------
+ * A pool block holds content only, so one physical copy of a document serves
+ * every request that holds it, at whatever position (gist.science, Technical
+ * Summary > Methodology: purely content-based cache; shd-paper.top, Abstract:
+ * one physical KV copy shared by many logical requests).  lazyattn_decode
+ * reads such a block once per request that holds it; these two calls read it
+ * about once per batch.
+ *
+ * lazyattn_decode_runs_plan (host) cuts the tables into runs: maximal
+ * sequences of entries, (block, valid length) each, that follow one another in
+ * the same order wherever they occur (typically a shared document); all but a
+ * run's last entry are whole blocks.  Every entry of every request lies in
+ * exactly one occurrence of one run.  A run held more than once is cut into
+ * work items of at most 64 entries and at most 16 / G occurrences (G =
+ * Hq / Hkv; the query rows of one 16-row MFMA tile), listed so that
+ * round-robin dispatch puts the items of one run piece on one XCD, where their
+ * reads of the same blocks meet in its L2.  The entries of runs held once are
+ * gathered per request into items of at most 128 entries and one occurrence.
+ *
+ * lazyattn_decode_runs attends each item once per KV head.  An item's entries
+ * carry key offsets o from a base s of the item (a shared run's first key; 0
+ * for a request's own entries), and each occurrence an offset p - s, p the
+ * request's query position: the key rows are turned by R(o) and the query of
+ * each occurrence by R(p - s).  Since R(t - p) = R(o) R(s - p) for the key at
+ * t = s + o, the scores are the per-request ones (gist.science, Technical
+ * Summary > Mathematical Equivalence).  Each occurrence and head gets a
+ * partial (o / l in fp16, m, l), and a second kernel merges each request's
+ * partials by log-sum-exp in occurrence order.  Results equal
+ * lazyattn_decode's up to rounding (the query is rounded to bf16 after its
+ * turn; the summation order differs). */
+#define LAZYATTN_RUN_ITEM_INTS 4
+typedef struct {
+  int32_t num_items;              /* work items; a multiple of 8, padded with empty items */
+  int32_t num_words;              /* item entries */
+  int32_t num_refs;               /* occurrences over all items = partial slots */
+  const int32_t* items;           /* device [num_items][LAZYATTN_RUN_ITEM_INTS]: {first word,
+                                     entries (0: an empty item), first occurrence, occurrences} */
+  const uint64_t* words;          /* device [num_words] item entries: physical block in bits
+                                     31..0, key offset o in bits 58..32, valid length in 63..59 */
+  const int32_t* refs;            /* device [num_refs][2] {request, p - s} */
+  const int32_t* req_ref_begin;   /* device [R + 1]: request r's occurrences are */
+  const int32_t* req_refs;        /* device [num_refs]: req_refs[req_ref_begin[r] .. req_ref_begin[r+1]) */
+} lazyattn_run_plan;
+
+/* Build the plan on the host from host copies of a decode batch's tables
+ * (the layout of lazyattn_batch; tables are checked as by
+ * lazyattn_validate_tables, EINVAL on a violation).  Writes the needed sizes
+ * to *num_items, *num_words and *num_refs in every case (with zero
+ * capacities, that is all it does) and fills the host arrays
+ *  items_h [capacity_items][LAZYATTN_RUN_ITEM_INTS], words_h [capacity_words],
+ *  refs_h [capacity_refs][2], req_ref_begin_h [num_reqs + 1], req_refs_h [capacity_refs]
+ * only when every capacity suffices (else LAZYATTN_EWORKSPACE, arrays
+ * untouched); the caller copies them to the device for lazyattn_decode_runs.
+ * The plan depends on the tables only, not on the pool's contents.
+ * LAZYATTN_EUNSUPPORTED unless dtype is bf16 and G <= 16, and for a request
+ * entry starting at 2^27 or later.  A request with no
+ * entries has no occurrence; its output rows become zero. */
+lazyattn_status lazyattn_decode_runs_plan(const lazyattn_config* cfg, const uint64_t* tables_h, int32_t num_reqs,
+                                          int32_t max_entries, const int32_t* num_entries_h,
+                                          const int32_t* ctx_lens_h, int64_t num_blocks, int32_t capacity_items,
+                                          int32_t capacity_words, int32_t capacity_refs, int32_t* items_h,
+                                          uint64_t* words_h, int32_t* refs_h, int32_t* req_ref_begin_h,
+                                          int32_t* req_refs_h, int32_t* num_items, int32_t* num_words,
+                                          int32_t* num_refs);
+
+/* Bytes of workspace lazyattn_decode_runs needs: the partials of num_refs
+ * occurrences; 0 for an invalid config. */
+size_t lazyattn_decode_runs_workspace_size(const lazyattn_config* cfg, int32_t num_refs);
+
+/* One decode step over a plan (see above): q, out device [num_reqs][Hq][D] as
+ * for lazyattn_decode, the pool content-only (plain or FP8), workspace >=
+ * lazyattn_decode_runs_workspace_size bytes.  Launches the attention kernel
+ * (num_items x Hkv work-groups) and the merge kernel on `stream`.  The plan's
+ * arrays must describe this batch: an item or occurrence outside the pool or
+ * the batch is not detected here (lazyattn_decode_runs_plan builds valid ones).
+ * EUNSUPPORTED as for the plan; EWORKSPACE for a short workspace. */
+lazyattn_status lazyattn_decode_runs(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                     const void* v_pool, int64_t num_blocks, int32_t num_reqs,
+                                     const lazyattn_run_plan* plan, void* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
 
 /* The attention kernel of lazyattn_prefill / lazyattn_decode alone (same
  * arguments).  With one split it writes `out` directly; with S > 1 splits

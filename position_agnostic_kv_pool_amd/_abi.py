@@ -74,6 +74,23 @@ class Batch(ctypes.Structure):
     ]
 
 
+RUN_ITEM_INTS = 4
+
+
+class RunPlan(ctypes.Structure):
+    """lazyattn_run_plan: the device arrays of a shared-run decode plan."""
+    _fields_ = [
+        ("num_items", ctypes.c_int32),
+        ("num_words", ctypes.c_int32),
+        ("num_refs", ctypes.c_int32),
+        ("items", ctypes.c_void_p),
+        ("words", ctypes.c_void_p),
+        ("refs", ctypes.c_void_p),
+        ("req_ref_begin", ctypes.c_void_p),
+        ("req_refs", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -104,6 +121,10 @@ def lib() -> ctypes.CDLL:
             "lazyattn_prefill": (I32, [CP, P, P, I32, I32, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_decode": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_decode_noalloc": (I32, [CP, P, P, P, I64, BP, I32, P, P]),
+            "lazyattn_decode_runs_plan": (I32, [CP, P, I32, I32, P, P, I64, I32, I32, I32, P, P, P, P, P,
+                                                ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+            "lazyattn_decode_runs_workspace_size": (SZ, [CP, I32]),
+            "lazyattn_decode_runs": (I32, [CP, P, P, P, I64, I32, ctypes.POINTER(RunPlan), P, P, SZ, P]),
             "lazyattn_prefill_attend": (I32, [CP, P, P, I32, I32, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_decode_attend": (I32, [CP, P, P, P, I64, BP, I32, P, P, SZ, P]),
             "lazyattn_merge_splits": (I32, [CP, I32, I32, P, SZ, P, P]),
@@ -281,6 +302,60 @@ def decode(cfg: Config, q, k_pool, v_pool, num_blocks: int, batch: Batch, out, w
                                ctypes.byref(batch), int(num_splits), _ptr(out), _ptr(workspace), ws_bytes,
                                _stream(stream))
     _check(st, "lazyattn_decode")
+
+
+def decode_runs_plan(cfg: Config, tables: np.ndarray, num_entries: np.ndarray, ctx_lens: np.ndarray,
+                     num_blocks: int) -> dict:
+    """Host plan of a shared-run decode (lazyattn_decode_runs_plan) from host copies of the batch:
+    numpy arrays items [n][RUN_ITEM_INTS], words, refs [m][2], req_ref_begin [R+1], req_refs [m]."""
+    t = np.ascontiguousarray(tables, dtype=np.uint64)
+    ne = np.ascontiguousarray(num_entries, dtype=np.int32)
+    cl = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    R, E = int(ne.shape[0]), (int(t.shape[1]) if t.ndim == 2 else 0)
+    ni, nw, nr = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    L = lib()
+    st = L.lazyattn_decode_runs_plan(ctypes.byref(cfg), t.ctypes.data, R, E, ne.ctypes.data, cl.ctypes.data,
+                                     int(num_blocks), 0, 0, 0, None, None, None, None, None,
+                                     ctypes.byref(ni), ctypes.byref(nw), ctypes.byref(nr))
+    if st != EWORKSPACE and st != OK:
+        _check(st, "lazyattn_decode_runs_plan")
+    items = np.zeros((max(ni.value, 1), RUN_ITEM_INTS), dtype=np.int32)
+    words = np.zeros(max(nw.value, 1), dtype=np.uint64)
+    refs = np.zeros((max(nr.value, 1), 2), dtype=np.int32)
+    begin = np.zeros(R + 1, dtype=np.int32)
+    rrefs = np.zeros(max(nr.value, 1), dtype=np.int32)
+    st = L.lazyattn_decode_runs_plan(ctypes.byref(cfg), t.ctypes.data, R, E, ne.ctypes.data, cl.ctypes.data,
+                                     int(num_blocks), items.shape[0], words.shape[0], refs.shape[0],
+                                     items.ctypes.data, words.ctypes.data, refs.ctypes.data, begin.ctypes.data,
+                                     rrefs.ctypes.data, ctypes.byref(ni), ctypes.byref(nw), ctypes.byref(nr))
+    _check(st, "lazyattn_decode_runs_plan")
+    return dict(items=items[:ni.value], words=words[:nw.value], refs=refs[:nr.value], req_ref_begin=begin,
+                req_refs=rrefs[:nr.value])
+
+
+def decode_runs_workspace_size(cfg: Config, num_refs: int) -> int:
+    return lib().lazyattn_decode_runs_workspace_size(ctypes.byref(cfg), int(num_refs))
+
+
+def make_run_plan(items, words, refs, req_ref_begin, req_refs) -> RunPlan:
+    """RunPlan over device int32/uint32 tensors (kept alive by the struct)."""
+    p = RunPlan()
+    p.num_items = int(items.shape[0])
+    p.num_words = int(words.shape[0])
+    p.num_refs = int(refs.shape[0])
+    p.items, p.words, p.refs = _ptr(items), _ptr(words), _ptr(refs)
+    p.req_ref_begin, p.req_refs = _ptr(req_ref_begin), _ptr(req_refs)
+    p._keep = (items, words, refs, req_ref_begin, req_refs)
+    return p
+
+
+def decode_runs(cfg: Config, q, k_pool, v_pool, num_blocks: int, num_reqs: int, plan: RunPlan, out, workspace=None,
+                stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().lazyattn_decode_runs(ctypes.byref(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), int(num_blocks),
+                                    int(num_reqs), ctypes.byref(plan), _ptr(out), _ptr(workspace), ws_bytes,
+                                    _stream(stream))
+    _check(st, "lazyattn_decode_runs")
 
 
 def decode_noalloc(cfg: Config, q, k_pool, v_pool, num_blocks: int, batch: Batch, out, num_splits: int = 0,

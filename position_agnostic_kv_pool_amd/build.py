@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblazyattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["lazyattn_kernels.hip", "lazyattn_host.cpp", "lazyattn_pool.cpp"]
+SOURCES = ["lazyattn_kernels.hip", "lazyattn_host.cpp", "lazyattn_pool.cpp", "lazyattn_runs.cpp"]
 # peak probes for the benchmark (MFMA issue rate, HBM streaming read): a library of their own
 PROBE_LIB_PATH = os.path.join(PKG, "liblazyattn_probe.so")
 PROBE_SOURCES = ["lazyattn_probe.hip"]

@@ -862,12 +862,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 // CH = splits whose loads are issued together: 16 for calls of more than 4 splits
 // (one memory round trip for up to 16), else 4 (fewer registers for the
 // bandwidth-bound merges of few splits)
+// List mode (list_begin != NULL, shared-run decode): output row idx = r Hq + h
+// merges the partials of request r's occurrences, rows list[i] Hq + h for i in
+// list_begin[r] .. list_begin[r + 1], in that order.
 template <int CH>
 __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, const float* ml_part, uint16_t* out,
-                                                    int rows, int splits) {
+                                                    int rows, int splits, const int32_t* list_begin,
+                                                    const int32_t* list, int Hq) {
   const int idx = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;                  // channels 8c .. 8c + 7
   if (idx >= rows) return;
+  int l0 = 0, hh = 0;
+  if (list_begin) {
+    const int rq = idx / Hq;
+    hh = idx - rq * Hq;
+    l0 = list_begin[rq];
+    splits = list_begin[rq + 1] - l0;
+  }
   float M = kNegInf, lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += CH) {
@@ -875,11 +886,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, cons
     uint4 o[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      // splits is the same for every thread: past the last split nothing is read
+      // past the last split (the row's last occurrence) nothing is read
       ml[j] = make_float2(kNegInf, 0.f);
       o[j] = make_uint4(0u, 0u, 0u, 0u);
       if (s0 + j < splits) {
-        const size_t row = static_cast<size_t>(s0 + j) * rows + idx;
+        const size_t row = list_begin ? static_cast<size_t>(list[l0 + s0 + j]) * Hq + hh
+                                      : static_cast<size_t>(s0 + j) * rows + idx;
         ml[j] = *reinterpret_cast<const float2*>(ml_part + row * 2);
         o[j] = *reinterpret_cast<const uint4*>(o_part + row * kPD + 8 * c);
       }
@@ -946,6 +958,11 @@ struct DecodeArgs {
   int32_t halves;                // 2: groups of 17..32 heads, one work-group per 16-head half
   float scale_log2;
   RopeRev rope;
+  // shared-run decode (items != NULL): work-group (item, KV head) instead of
+  // (split, KV head, request); partials go to the occurrence's slot
+  const int32_t* items;          // [n_items][4] {first word, entries, first occurrence, occurrences}
+  const uint64_t* words;         // item entries: block, key offset (bits 58..32), length (63..59)
+  const int32_t* refs;           // [n_refs][2] {request, p - s}
 };
 
 constexpr int kOS = kPD + 4;  // LDS row stride (floats) of the wave-merge buffer
@@ -954,7 +971,7 @@ constexpr int kRing = 2;      // entries of a decode wave in registers: one proc
 static_assert(4 * kTab * 4 <= 4 * 16 * kOS * 4, "the staged table fits the wave-merge buffer");
 constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
-template <int PE, int NT, int KV8>
+template <int PE, int NT, int KV8, int RUNS>
 __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) float dsm[];
   float2* bsh = reinterpret_cast<float2*>(dsm);             // [4 waves][kRing][64]
@@ -971,7 +988,20 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   // block hits that XCD's L2: ids 16 j + i and 16 j + 8 + i (i < 8) are the
   // two halves of work item 8 j + i = (split, kvh, request), split fastest.
   int split, kvh, r, half = 0;
-  if (A.halves == 1) {
+  // shared-run item: its words, entries, last entry's length, occurrences
+  int run_w0 = 0, run_n = 0, run_ref0 = 0, run_nref = 0;
+  constexpr bool runs = RUNS != 0;
+  if (runs) {
+    const int32_t* it = A.items + static_cast<size_t>(blockIdx.x) * 4;
+    run_w0 = it[0];
+    run_n = it[1];
+    run_ref0 = it[2];
+    run_nref = it[3];
+    if (run_n == 0) return;                          // a padding item
+    split = 0;
+    kvh = blockIdx.y;
+    r = 0;
+  } else if (A.halves == 1) {
     split = blockIdx.x;
     kvh = blockIdx.y;
     r = blockIdx.z;
@@ -986,16 +1016,19 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     r = rest / Hkv;
   }
   const int hb = 16 * half;                          // first head column of this work-group
-  const int Gw = min(16 * NT, G - hb);               // its head columns
-  const int L = A.ctx[r];
-  const int p = L - 1;
-  const int ne = A.n_ent[r];
-  const uint64_t* trow = A.tables + static_cast<size_t>(r) * A.max_entries;
-  const int e_begin = split * A.eps;
-  const int e_end = min(ne, e_begin + A.eps);
+  // its head columns; a shared-run item's columns are (occurrence, head) pairs
+  const int Gw = runs ? min(16 * NT, run_nref * G) : min(16 * NT, G - hb);
+  // key positions are relative to the query (p) or, for a shared-run item, to
+  // its first key (the queries carry the rest of the turn)
+  const int L = runs ? 0 : A.ctx[r];
+  const int p = runs ? 0 : L - 1;
+  const int ne = runs ? run_n : A.n_ent[r];
+  const uint64_t* trow = A.tables + (runs ? 0 : static_cast<size_t>(r) * A.max_entries);
+  const int e_begin = runs ? 0 : split * A.eps;
+  const int e_end = runs ? run_n : min(ne, e_begin + A.eps);
   // a split past the request's last entry leaves only an empty (m, l) = (-inf, 0),
   // which the merge skips without reading its output
-  if (A.splits > 1 && e_begin >= ne) {
+  if (!runs && A.splits > 1 && e_begin >= ne) {
     if (tid < Gw) {
       const size_t prow = static_cast<size_t>(split) * A.R * Hq + static_cast<size_t>(r) * Hq + kvh * G + hb + tid;
       *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(kNegInf, 0.f);
@@ -1012,24 +1045,44 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   // query fragments: lane (g, n) holds head column nt*16+n, channels c0(s) + 0..7,
   // scaled by scale*log2(e) and rounded to bf16
   // (framed pool: the raw fragments are kept, and qb is formed per frame)
+  // (shared-run item: column = (occurrence j, head gg) with j = col / G; its
+  // query is request refs[j]'s, turned by R(p - s) at every pair when RoPE)
   bf16x8 qb[NT][4];
   uint4 qraw[NT][4];
   float slope[NT];
+  int pcol[NT];                                       // the query's position, relative as the keys'
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = nt * 16 + n;
     const bool ok = col < Gw;
-    const int h = kvh * G + hb + (ok ? col : 0);
+    int h = kvh * G + hb + (ok ? col : 0), rq = r;
+    int turn = 0;
+    pcol[nt] = p;
+    if (runs) {
+      const int j = ok ? col / G : 0;
+      h = kvh * G + (ok ? col - j * G : 0);
+      rq = A.refs[2 * (run_ref0 + j)];
+      turn = A.refs[2 * (run_ref0 + j) + 1];
+      pcol[nt] = turn;
+    }
     slope[nt] = (PE == LAZYATTN_PE_ALIBI) ? alibi_slope(A.alibi, h, Hq) * kLog2e : 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 raw = make_uint4(0, 0, 0, 0);
-      if (ok) raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(r) * Hq + h) * kPD + c0(s));
+      if (ok) raw = *reinterpret_cast<const uint4*>(A.q + (static_cast<size_t>(rq) * Hq + h) * kPD + c0(s));
       qraw[nt][s] = raw;
       uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        w4[jj] = pack_bf16x2(bf_lo(w4[jj]) * A.scale_log2, bf_hi(w4[jj]) * A.scale_log2);
+      for (int jj = 0; jj < 4; ++jj) {
+        float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
+        if (PE == LAZYATTN_PE_ROPE && runs) {
+          const float2 ph = unit_phase_turns(turn, A.rope.rev[c0(s) / 2 + jj]);
+          const float y0 = x0 * ph.x - x1 * ph.y, y1 = x0 * ph.y + x1 * ph.x;
+          x0 = y0;
+          x1 = y1;
+        }
+        w4[jj] = pack_bf16x2(x0 * A.scale_log2, x1 * A.scale_log2);
+      }
       qb[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
     }
   }
@@ -1274,7 +1327,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
         for (int j = 0; j < 4; ++j) {
           const int krow = 4 * g + j;
           float x = S[j];
-          if (PE == LAZYATTN_PE_ALIBI) x -= slope[nt] * static_cast<float>(p - (inf.start + krow));
+          if (PE == LAZYATTN_PE_ALIBI) x -= slope[nt] * static_cast<float>(pcol[nt] - (inf.start + krow));
           x = (krow < inf.len) ? x : kNegInf;
           S[j] = x;
           lm = fmaxf(lm, x);
@@ -1322,6 +1375,16 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     if (c0 > 0) __syncthreads();                     // every wave is done with the previous chunk
     for (int i = tid; i < cn; i += 256) {
       const int ei = e_begin + c0 + i;
+      if (runs) {
+        // a shared-run item's entry: its key offsets from the item's base, its block
+        const uint64_t w = A.words[run_w0 + ei];
+        const uint32_t off = static_cast<uint32_t>(w >> 32) & 0x7ffffffu;
+        tst[i] = off;
+        ten[i] = off + static_cast<uint32_t>(w >> 59);
+        tbk[i] = static_cast<uint32_t>(w);
+        if (PE == kPeFramed) tfr[i] = 0;
+        continue;
+      }
       const uint64_t w = trow[ei];
       tst[i] = word_start(w);
       ten[i] = (ei + 1 < ne) ? reinterpret_cast<const uint32_t*>(trow + ei + 1)[1] : static_cast<uint32_t>(L);
@@ -1399,7 +1462,13 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     }
     const int h = kvh * G + hb + col;
     const size_t rowoff = static_cast<size_t>(r) * Hq + h;
-    if (A.splits == 1) {
+    if (runs) {
+      // occurrence j = col / G, head kvh G + col % G: its partial slot
+      const int j = col / G;
+      const size_t prow = static_cast<size_t>(run_ref0 + j) * Hq + kvh * G + (col - j * G);
+      A.o_part[prow * kPD + d] = static_cast<uint16_t>(pack_f16x2(lsum > 0.f ? osum / lsum : 0.f, 0.f) & 0xffffu);
+      if (d == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(M, lsum);
+    } else if (A.splits == 1) {
       const float val = lsum > 0.f ? osum / lsum : 0.f;
       A.out[rowoff * kPD + d] = static_cast<uint16_t>(pack_bf16x2(val, 0.f) & 0xffffu);
     } else {
@@ -1700,10 +1769,10 @@ static lazyattn_status merge_launch(int rows_total, int splits, const void* work
   const float* ml_part = reinterpret_cast<const float*>(o_part + static_cast<size_t>(splits) * rows_total * kPD);
   if (splits > 4)
     hipLaunchKernelGGL(merge_kernel<16>, dim3((rows_total + 15) / 16), dim3(256), 0, stream, o_part, ml_part,
-                       static_cast<uint16_t*>(out), rows_total, splits);
+                       static_cast<uint16_t*>(out), rows_total, splits, nullptr, nullptr, 0);
   else
     hipLaunchKernelGGL(merge_kernel<4>, dim3((rows_total + 15) / 16), dim3(256), 0, stream, o_part, ml_part,
-                       static_cast<uint16_t*>(out), rows_total, splits);
+                       static_cast<uint16_t*>(out), rows_total, splits, nullptr, nullptr, 0);
   return launched();
 }
 
@@ -1774,21 +1843,24 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   return launched();
 }
 
-template <int PEV, int NTV, int KV8>
+template <int PEV, int NTV, int KV8, int RUNS>
 static void launch_decode_one(dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
   if (lds > 65536)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<PEV, NTV, KV8>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<PEV, NTV, KV8, RUNS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  hipLaunchKernelGGL((decode_bf16_kernel<PEV, NTV, KV8>), grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL((decode_bf16_kernel<PEV, NTV, KV8, RUNS>), grid, dim3(256), lds, stream, a);
 }
 
-template <int KV8>
+// RUNS: the shared-run decode (a content-only pool: no framed instantiation)
+template <int KV8, int RUNS>
 static void launch_decode(int pe_sel, dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
   switch (pe_sel) {
-    case kPeFramed: launch_decode_one<kPeFramed, 1, KV8>(grid, lds, stream, a); break;
-    case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 1, KV8>(grid, lds, stream, a); break;
-    case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 1, KV8>(grid, lds, stream, a); break;
-    default: launch_decode_one<LAZYATTN_PE_ALIBI, 1, KV8>(grid, lds, stream, a); break;
+    case kPeFramed:
+      if (!RUNS) launch_decode_one<kPeFramed, 1, KV8, 0>(grid, lds, stream, a);
+      break;
+    case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 1, KV8, RUNS>(grid, lds, stream, a); break;
+    case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 1, KV8, RUNS>(grid, lds, stream, a); break;
+    default: launch_decode_one<LAZYATTN_PE_ALIBI, 1, KV8, RUNS>(grid, lds, stream, a); break;
   }
 }
 
@@ -1840,9 +1912,9 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   const size_t lds = decode_lds_bytes(1);
   const int pe_sel = framed ? kPeFramed : cfg->pe;
   if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3)
-    launch_decode<1>(pe_sel, grid, lds, stream, a);
+    launch_decode<1, 0>(pe_sel, grid, lds, stream, a);
   else
-    launch_decode<0>(pe_sel, grid, lds, stream, a);
+    launch_decode<0, 0>(pe_sel, grid, lds, stream, a);
   *splits_out = splits;
   return launched();
 }
@@ -1917,6 +1989,47 @@ lazyattn_status lazyattn_decode(const lazyattn_config* cfg, const void* q, const
                                      workspace_bytes, stream, &splits);
   if (st != LAZYATTN_OK || splits <= 1) return st;
   return merge_launch(batch->num_reqs * cfg->num_q_heads, splits, workspace, out, stream);
+}
+
+lazyattn_status lazyattn_decode_runs(const lazyattn_config* cfg, const void* q, const void* k_pool,
+                                     const void* v_pool, int64_t num_blocks, int32_t num_reqs,
+                                     const lazyattn_run_plan* plan, void* out, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  lazyattn_status st = check_config(cfg);
+  if (st != LAZYATTN_OK) return st;
+  if (!plan || num_reqs < 0 || num_blocks < 0 || plan->num_items < 0 || plan->num_words < 0 || plan->num_refs < 0)
+    return LAZYATTN_EINVAL;
+  const int Hq = cfg->num_q_heads, Hkv = cfg->num_kv_heads, G = Hq / Hkv;
+  if (cfg->dtype != LAZYATTN_BF16 || G > 16) return LAZYATTN_EUNSUPPORTED;
+  if (num_reqs == 0) return LAZYATTN_OK;
+  if (!q || !k_pool || !v_pool || !out || num_blocks < 1 || !plan->req_ref_begin || plan->num_items % 8 != 0)
+    return LAZYATTN_EINVAL;
+  if (plan->num_items > 0 && (!plan->items || !plan->words || !plan->refs || !plan->req_refs))
+    return LAZYATTN_EINVAL;
+  const size_t need = lazyattn_decode_runs_workspace_size(cfg, plan->num_refs);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return LAZYATTN_EWORKSPACE;
+  if (Hkv > 65535 || static_cast<long long>(num_reqs) * Hq > 0x7fffffffLL - 15) return LAZYATTN_EUNSUPPORTED;
+  uint16_t* o_part = static_cast<uint16_t*>(workspace);
+  float* ml_part = reinterpret_cast<float*>(o_part + static_cast<size_t>(plan->num_refs) * Hq * kPD);
+  if (plan->num_items > 0) {
+    // the per-request arrays are not read for a shared-run item; valid device
+    // pointers stand in for them all the same
+    DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+                 static_cast<const uint16_t*>(v_pool), reinterpret_cast<const uint64_t*>(plan->items),
+                 plan->req_ref_begin, plan->req_ref_begin, nullptr, cfg->alibi_slopes, static_cast<uint16_t*>(out),
+                 o_part, ml_part, num_reqs, Hq, Hkv, G, 1, 1, 1, 1, softmax_scale_of(cfg) * kLog2e,
+                 make_rope_rev(cfg), plan->items, plan->words, plan->refs};
+    const dim3 grid(static_cast<unsigned>(plan->num_items), static_cast<unsigned>(Hkv));
+    if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3)
+      launch_decode<1, 1>(cfg->pe, grid, decode_lds_bytes(1), stream, a);
+    else
+      launch_decode<0, 1>(cfg->pe, grid, decode_lds_bytes(1), stream, a);
+    if ((st = launched()) != LAZYATTN_OK) return st;
+  }
+  const int rows_total = num_reqs * Hq;
+  hipLaunchKernelGGL(merge_kernel<16>, dim3((rows_total + 15) / 16), dim3(256), 0, stream, o_part, ml_part,
+                     static_cast<uint16_t*>(out), rows_total, 0, plan->req_ref_begin, plan->req_refs, Hq);
+  return launched();
 }
 
 lazyattn_status lazyattn_decode_noalloc(const lazyattn_config* cfg, const void* q, const void* k_pool,

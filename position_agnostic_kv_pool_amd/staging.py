@@ -194,6 +194,33 @@ class PrefillCall:
         _abi.merge_splits(self.cfg, self.total_q, self.splits, self.workspace, self.out, stream)
 
 
+class RunDecodeCall:
+    """One decode step over shared runs (lazyattn_decode_runs): the plan is cut from the batch's
+    tables on the host and copied to the device with the queries; num_blocks is the pool's."""
+
+    def __init__(self, cfg, spec, inputs: dict, num_blocks: int, device="cuda", block_permutation=None):
+        self.cfg = cfg
+        blocks = inputs["table_blocks"] if block_permutation is None else \
+            block_permutation[inputs["table_blocks"].astype(np.int64)].astype(np.uint32)
+        words = _abi.pack_entries(blocks, inputs["table_starts"])
+        self.plan_host = _abi.decode_runs_plan(cfg, words, inputs["num_entries"], inputs["ctx_lens"], num_blocks)
+        h = self.plan_host
+        dev = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int64) if v.dtype == np.uint64 else
+                                   np.ascontiguousarray(v)).to(device) for k, v in h.items()}
+        self.plan = _abi.make_run_plan(dev["items"], dev["words"], dev["refs"], dev["req_ref_begin"],
+                                       dev["req_refs"])
+        self.q = to_device(inputs["q"], spec.dtype, device)
+        self.out = torch.empty_like(self.q)
+        self.num_reqs = len(inputs["ctx_lens"])
+        ws = _abi.decode_runs_workspace_size(cfg, h["refs"].shape[0])
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws > 0 else None
+
+    def run(self, pools: DevicePools, stream=None):
+        _abi.decode_runs(self.cfg, self.q, pools.k, pools.v, pools.num_blocks, self.num_reqs, self.plan, self.out,
+                         self.workspace, stream)
+        return self.out
+
+
 class DecodeCall:
     """Device inputs and output/workspace buffers of one decode step."""
 

@@ -267,6 +267,100 @@ def test_parity_llama70b_all_requests_as_benched():
         say(f"70B decode 4 requests step {step} splits {call.splits}: max {mx:.2e} mean {mn:.2e}")
 
 
+# ---------------------------------------------------------------------------
+# shared-run decode (one read of a shared block serves every request holding it)
+# ---------------------------------------------------------------------------
+@pytest.mark.timeout(300)
+def test_decode_runs_llama8b_full_batch():
+    say("shared-run decode: 8B, all 128 requests, steps 0 and 1 (oracle on every 8th request), "
+        "against the per-request decode on all")
+    wl = W.build_workload(W.spec(3, n_decode=2))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    orc = OracleState(wl)
+    reqs = list(range(0, 128, 8))
+    before = wl.tokens_before_step(0)
+    staging.append_tokens(cfg, pools, before, s.dtype, DEV)
+    orc.append(before)
+    for step in (0, 1):
+        d = wl.decode_step(step)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        orc.append(d)
+        call = staging.RunDecodeCall(cfg, s, d, pools.num_blocks, DEV)
+        # the shared documents are read far fewer times than the tables name them
+        assert len(call.plan_host["words"]) < 0.5 * int(np.sum(d["num_entries"]))
+        out = gpu_f64(call.run(pools))
+        ref = orc.decode(d, requests=reqs)
+        mx, mn = assert_parity(out[reqs], np.stack([ref[r] for r in reqs]), "bf16",
+                               f"8B shared-run decode step {step}")
+        say(f"8B shared-run decode step {step}: max {mx:.2e} mean {mn:.2e}")
+        per_req = gpu_f64(staging.DecodeCall(cfg, s, d, DEV).run(pools))
+        dmx, dmn = diff_stats(out, per_req)
+        say(f"  vs per-request decode, all 128: max {dmx:.2e} mean {dmn:.2e}")
+        assert dmx <= 2e-2 and dmn <= 1e-3
+
+
+@pytest.mark.timeout(300)
+def test_decode_runs_encodings_repeats_and_long_context():
+    say("shared-run decode: rotation-free and ALiBi (8B, 16 requests), a request holding another's "
+        "whole table, FP8 pool, and the 70B 32k step 0 (G = 8)")
+    wl = W.build_workload(W.spec(3, requests=[16], n_decode=1))
+    s = wl.spec
+    pools = staging.DevicePools(wl, DEV)
+    orc = OracleState(wl)
+    cfg = staging.config_for(s)
+    before = wl.tokens_before_step(0)
+    staging.append_tokens(cfg, pools, before, s.dtype, DEV)
+    orc.append(before)
+    d = wl.decode_step(0)
+    staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+    orc.append(d)
+    for pe in ("rope", "none", "alibi"):
+        c = staging.config_for(s, pe=pe)
+        out = gpu_f64(staging.RunDecodeCall(c, s, d, pools.num_blocks, DEV).run(pools))
+        ref = orc.decode(d, pe=pe)
+        mx, mn = assert_parity(out, np.stack([ref[r] for r in range(16)]), "bf16", f"8B shared-run decode {pe}")
+        say(f"8B shared-run decode {pe}: max {mx:.2e} mean {mn:.2e}")
+    # request 1 holds request 0's table (the same blocks at the same positions), with its own query
+    d2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+    for key in ("table_blocks", "table_starts"):
+        d2[key][1] = d2[key][0]
+    for key in ("num_entries", "ctx_lens"):
+        d2[key][1] = d2[key][0]
+    call = staging.RunDecodeCall(cfg, s, d2, pools.num_blocks, DEV)
+    out = gpu_f64(call.run(pools))
+    ref = orc.decode(d2, requests=[0, 1, 2])
+    mx, mn = assert_parity(out[:3], np.stack([ref[r] for r in range(3)]), "bf16", "shared-run decode, shared table")
+    say(f"shared-run decode, request 1 = request 0's table: max {mx:.2e} mean {mn:.2e}")
+    # FP8 pool
+    cfg8 = staging.config_for(s, kv_format="fp8")
+    pools8 = staging.WrittenPools(wl, cfg8, DEV)
+    orc8 = OracleFp8State(wl)
+    for inp in (before, d):
+        staging.append_tokens(cfg8, pools8, inp, s.dtype, DEV)
+        orc8.append(inp)
+    out = gpu_f64(staging.RunDecodeCall(cfg8, s, d, pools8.num_blocks, DEV).run(pools8))
+    ref = orc8.decode(d)
+    mx, mn = assert_parity(out, np.stack([ref[r] for r in range(16)]), "bf16", "FP8 shared-run decode")
+    say(f"FP8 8B shared-run decode: max {mx:.2e} mean {mn:.2e}")
+    del pools, pools8
+    # 70B, 4 requests over 32k contexts: long runs cut into pieces of 64 entries
+    wl = W.build_workload(W.spec(4, n_decode=1))
+    s = wl.spec
+    cfg = staging.config_for(s)
+    pools = staging.DevicePools(wl, DEV)
+    orc = OracleState(wl)
+    for inp in (wl.prefill_batch(), wl.decode_step(0)):
+        staging.append_tokens(cfg, pools, inp, s.dtype, DEV)
+        orc.append(inp)
+    d = wl.decode_step(0)
+    out = gpu_f64(staging.RunDecodeCall(cfg, s, d, pools.num_blocks, DEV).run(pools))
+    ref = orc.decode(d)
+    mx, mn = assert_parity(out, np.stack([ref[r] for r in range(4)]), "bf16", "70B shared-run decode")
+    say(f"70B shared-run decode step 0: max {mx:.2e} mean {mn:.2e}")
+
+
 @pytest.mark.parametrize("skew", W.CFG5_SKEWS)
 @pytest.mark.parametrize("pe", W.CFG5_PES)
 def test_parity_mqa_stress(skew, pe):

@@ -17,7 +17,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "position_agnostic_kv_pool_amd", "csrc")
-SOURCES = ["lazyattn_kernels.hip", "lazyattn_host.cpp", "lazyattn_pool.cpp"]
+SOURCES = ["lazyattn_kernels.hip", "lazyattn_host.cpp", "lazyattn_pool.cpp", "lazyattn_runs.cpp"]
 
 
 def _hipcc():
