@@ -305,7 +305,8 @@ lazyattn_status lazyattn_decode_noalloc(const lazyattn_config* cfg, const void* 
  * reads of the same blocks meet in its L2.  The entries of runs held once are
  * gathered per request into items of at most 128 entries and one occurrence.
  *
- * lazyattn_decode_runs attends each item once per KV head.  An item's entries
+ * lazyattn_decode_runs attends each item once per KV head, one wave per item
+ * (items 4 m .. 4 m + 3 form work-group m).  An item's entries
  * carry key offsets o from a base s of the item (a shared run's first key; 0
  * for a request's own entries), and each occurrence an offset p - s, p the
  * request's query position: the key rows are turned by R(o) and the query of
@@ -318,7 +319,7 @@ lazyattn_status lazyattn_decode_noalloc(const lazyattn_config* cfg, const void* 
  * turn; the summation order differs). */
 #define LAZYATTN_RUN_ITEM_INTS 4
 typedef struct {
-  int32_t num_items;              /* work items; a multiple of 8, padded with empty items */
+  int32_t num_items;              /* work items; a multiple of 32, padded with empty items */
   int32_t num_words;              /* item entries */
   int32_t num_refs;               /* occurrences over all items = partial slots */
   const int32_t* items;           /* device [num_items][LAZYATTN_RUN_ITEM_INTS]: {first word,

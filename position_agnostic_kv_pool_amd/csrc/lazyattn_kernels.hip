@@ -992,12 +992,14 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   int run_w0 = 0, run_n = 0, run_ref0 = 0, run_nref = 0;
   constexpr bool runs = RUNS != 0;
   if (runs) {
-    const int32_t* it = A.items + static_cast<size_t>(blockIdx.x) * 4;
+    // one item per wave: items 4 x .. 4 x + 3 of work-group x (an empty item's
+    // wave passes the work-group barrier below, then ends)
+    const int w_item = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + wave);
+    const int32_t* it = A.items + static_cast<size_t>(w_item) * 4;
     run_w0 = it[0];
     run_n = it[1];
     run_ref0 = it[2];
     run_nref = it[3];
-    if (run_n == 0) return;                          // a padding item
     split = 0;
     kvh = blockIdx.y;
     r = 0;
@@ -1061,8 +1063,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     if (runs) {
       const int j = ok ? col / G : 0;
       h = kvh * G + (ok ? col - j * G : 0);
-      rq = A.refs[2 * (run_ref0 + j)];
-      turn = A.refs[2 * (run_ref0 + j) + 1];
+      rq = ok ? A.refs[2 * (run_ref0 + j)] : 0;
+      turn = ok ? A.refs[2 * (run_ref0 + j) + 1] : 0;
       pcol[nt] = turn;
     }
     slope[nt] = (PE == LAZYATTN_PE_ALIBI) ? alibi_slope(A.alibi, h, Hq) * kLog2e : 0.f;
@@ -1185,8 +1187,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   int32_t* tfr = reinterpret_cast<int32_t*>(tbk + kTab);         // [kTab] frame starts
   const int32_t* frow_v = A.frames + (PE == kPeFramed ? static_cast<size_t>(r) * A.max_entries : 0);
   int nk = 0, kl = 0;                                            // this wave's entries in the chunk; next to load
+  // a wave's entries in the staged table: wv, wv + 4, ... (the work-group's
+  // entries), or its own item's rows 0, 1, ... from row (kTab / 4) wv
+  const int tab_base = runs ? wv * (kTab / 4) : wv, tab_step = runs ? 1 : 4;
   auto fetch = [&](EntryInfo& inf, int& fr) {
-    const int li = wv + 4 * min(kl, nk - 1);
+    const int li = tab_base + tab_step * min(kl, nk - 1);
     inf.blk = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tbk[li])));
     inf.start = __builtin_amdgcn_readfirstlane(static_cast<int>(tst[li]));
     inf.len = __builtin_amdgcn_readfirstlane(static_cast<int>(ten[li])) - inf.start;
@@ -1201,13 +1206,15 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   // R(64), for at most 32 steps in a row (rounding then adds at most ~1e-5 to
   // a unit phase, far under the bf16 rounding of the rotated key); otherwise
   // it is formed afresh from the angle reduced in fp64.
+  // (a wave that takes its item's entries in order steps by one block: R(16))
+  const int ph_step = runs ? kBlock : 4 * kBlock;
   float2 ph_prev = make_float2(1.f, 0.f), r64 = make_float2(1.f, 0.f);
   int st_prev = 0, ph_run = 32;
-  if (PE == LAZYATTN_PE_ROPE) r64 = unit_phase(4 * kBlock, my_rev);
+  if (PE == LAZYATTN_PE_ROPE) r64 = unit_phase(ph_step, my_rev);
   auto put_phase = [&](int sl, int start) {
     if (PE == LAZYATTN_PE_ROPE) {
       float2 ph;
-      if (start == st_prev + 4 * kBlock && ph_run < 32) {
+      if (start == st_prev + ph_step && ph_run < 32) {
         ph = cmul(ph_prev, r64);
         ++ph_run;
       } else {
@@ -1369,32 +1376,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       }
   };
 
-  const int n_split = max(0, e_end - e_begin);
-  for (int c0 = 0; c0 < n_split; c0 += kTab) {
-    const int cn = min(kTab, n_split - c0);
-    if (c0 > 0) __syncthreads();                     // every wave is done with the previous chunk
-    for (int i = tid; i < cn; i += 256) {
-      const int ei = e_begin + c0 + i;
-      if (runs) {
-        // a shared-run item's entry: its key offsets from the item's base, its block
-        const uint64_t w = A.words[run_w0 + ei];
-        const uint32_t off = static_cast<uint32_t>(w >> 32) & 0x7ffffffu;
-        tst[i] = off;
-        ten[i] = off + static_cast<uint32_t>(w >> 59);
-        tbk[i] = static_cast<uint32_t>(w);
-        if (PE == kPeFramed) tfr[i] = 0;
-        continue;
-      }
-      const uint64_t w = trow[ei];
-      tst[i] = word_start(w);
-      ten[i] = (ei + 1 < ne) ? reinterpret_cast<const uint32_t*>(trow + ei + 1)[1] : static_cast<uint32_t>(L);
-      tbk[i] = word_block(w);
-      if (PE == kPeFramed) tfr[i] = frow_v[ei];
-    }
-    __syncthreads();
-    nk = max(0, (cn - wv + 3) >> 2);
-    kl = 0;
-    if (nk == 0) continue;
+  // the wave's entries, nk of them from the staged table: kRing in flight
+  auto run_ring = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int sl = 0; sl < kRing; ++sl) {
       fetch(curb[sl], frb[sl]);
@@ -1421,6 +1404,63 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
 #pragma unroll
     for (int sl = 0; sl + 1 < kRing; ++sl)
       if (rem > sl) process(curb[sl], frb[sl], krb[sl], vrb[sl], sl);
+  };
+
+  if (runs) {
+    // ---- shared-run item: one wave, its entries in order, its own partials ----
+    if (run_n == 0) return;
+    for (int i = lane; i < run_n; i += 64) {
+      // an item entry: block, key offset from the item's base (bits 58..32), length
+      const uint64_t w = A.words[run_w0 + i];
+      const uint32_t off = static_cast<uint32_t>(w >> 32) & 0x7ffffffu;
+      tst[tab_base + i] = off;
+      ten[tab_base + i] = off + static_cast<uint32_t>(w >> 59);
+      tbk[tab_base + i] = static_cast<uint32_t>(w);
+      if (PE == kPeFramed) tfr[tab_base + i] = 0;
+    }
+    // only this wave reads these rows: its own LDS writes are ordered before its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    nk = run_n;
+    kl = 0;
+    run_ring();
+    // column (occurrence j, head): o / l in fp16 and (m, l) to the occurrence's slot;
+    // lane (g, n) holds channels 16 dt + 4 g .. + 3 of column n
+    float lt = l_run[0] + __shfl_xor(l_run[0], 16);
+    lt += __shfl_xor(lt, 32);
+    if (n < Gw) {
+      const int j = n / G;
+      const size_t prow = static_cast<size_t>(run_ref0 + j) * Hq + kvh * G + (n - j * G);
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 o = O[dt][0];
+        *reinterpret_cast<uint2*>(A.o_part + prow * kPD + 16 * dt + 4 * g) =
+            make_uint2(pack_f16x2(o[0] * inv, o[1] * inv), pack_f16x2(o[2] * inv, o[3] * inv));
+      }
+      if (g == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(m_run[0], lt);
+    }
+    return;
+  }
+
+  const int n_split = max(0, e_end - e_begin);
+  for (int c0 = 0; c0 < n_split; c0 += kTab) {
+    const int cn = min(kTab, n_split - c0);
+    if (c0 > 0) __syncthreads();                     // every wave is done with the previous chunk
+    for (int i = tid; i < cn; i += 256) {
+      const int ei = e_begin + c0 + i;
+      const uint64_t w = trow[ei];
+      tst[i] = word_start(w);
+      ten[i] = (ei + 1 < ne) ? reinterpret_cast<const uint32_t*>(trow + ei + 1)[1] : static_cast<uint32_t>(L);
+      tbk[i] = word_block(w);
+      if (PE == kPeFramed) tfr[i] = frow_v[ei];
+    }
+    __syncthreads();
+    nk = max(0, (cn - wv + 3) >> 2);
+    kl = 0;
+    if (nk == 0) continue;
+    run_ring();
   }
 
   // ---- merge the four waves ------------------------------------------------------
@@ -1462,13 +1502,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     }
     const int h = kvh * G + hb + col;
     const size_t rowoff = static_cast<size_t>(r) * Hq + h;
-    if (runs) {
-      // occurrence j = col / G, head kvh G + col % G: its partial slot
-      const int j = col / G;
-      const size_t prow = static_cast<size_t>(run_ref0 + j) * Hq + kvh * G + (col - j * G);
-      A.o_part[prow * kPD + d] = static_cast<uint16_t>(pack_f16x2(lsum > 0.f ? osum / lsum : 0.f, 0.f) & 0xffffu);
-      if (d == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(M, lsum);
-    } else if (A.splits == 1) {
+    if (A.splits == 1) {
       const float val = lsum > 0.f ? osum / lsum : 0.f;
       A.out[rowoff * kPD + d] = static_cast<uint16_t>(pack_bf16x2(val, 0.f) & 0xffffu);
     } else {
@@ -2002,7 +2036,7 @@ lazyattn_status lazyattn_decode_runs(const lazyattn_config* cfg, const void* q, 
   const int Hq = cfg->num_q_heads, Hkv = cfg->num_kv_heads, G = Hq / Hkv;
   if (cfg->dtype != LAZYATTN_BF16 || G > 16) return LAZYATTN_EUNSUPPORTED;
   if (num_reqs == 0) return LAZYATTN_OK;
-  if (!q || !k_pool || !v_pool || !out || num_blocks < 1 || !plan->req_ref_begin || plan->num_items % 8 != 0)
+  if (!q || !k_pool || !v_pool || !out || num_blocks < 1 || !plan->req_ref_begin || plan->num_items % 32 != 0)
     return LAZYATTN_EINVAL;
   if (plan->num_items > 0 && (!plan->items || !plan->words || !plan->refs || !plan->req_refs))
     return LAZYATTN_EINVAL;
@@ -2019,7 +2053,7 @@ lazyattn_status lazyattn_decode_runs(const lazyattn_config* cfg, const void* q, 
                  plan->req_ref_begin, plan->req_ref_begin, nullptr, cfg->alibi_slopes, static_cast<uint16_t*>(out),
                  o_part, ml_part, num_reqs, Hq, Hkv, G, 1, 1, 1, 1, softmax_scale_of(cfg) * kLog2e,
                  make_rope_rev(cfg), plan->items, plan->words, plan->refs};
-    const dim3 grid(static_cast<unsigned>(plan->num_items), static_cast<unsigned>(Hkv));
+    const dim3 grid(static_cast<unsigned>(plan->num_items / 4), static_cast<unsigned>(Hkv));
     if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3)
       launch_decode<1, 1>(cfg->pe, grid, decode_lds_bytes(1), stream, a);
     else

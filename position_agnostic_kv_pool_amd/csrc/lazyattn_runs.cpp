@@ -15,7 +15,7 @@ namespace lazyattn {
 namespace {
 
 constexpr int kRunPiece = 64;   // entries per work item over a shared run at most
-constexpr int kOwnPiece = 128;  // entries per work item over one request's unshared entries at most
+constexpr int kOwnPiece = 32;   // entries per work item over one request's unshared entries at most
 constexpr int kXcds = 8;        // round-robin dispatch spreads consecutive work-group ids over 8 XCDs
 
 struct Run {
@@ -154,12 +154,15 @@ static lazyattn_status build_run_items(const lazyattn_config* cfg, const uint64_
       queue[x].push_back(std::move(it));
     }
   }
-  // even out the item counts (work-groups are dealt to XCDs by id, so a longer
-  // queue would need empty items in the others): items past the mean count
-  // move from the back of the longer queues to the shorter ones
+  // A work-group takes four items, one per wave, and work-group m runs on XCD
+  // m % 8: queue x's items 4 k .. 4 k + 3 form work-group 8 k + x.  The queues
+  // are first evened out to a common length, a multiple of 4 (items past it
+  // move from the back of the longer queues to the shorter ones; the rest is
+  // padded with empty items), and each is ordered by size, longest first, so
+  // that the four waves of a work-group carry similar work.
   size_t total = 0;
   for (const auto& q : queue) total += q.size();
-  const size_t per = (total + kXcds - 1) / kXcds;
+  const size_t per = ((total + kXcds - 1) / kXcds + 3) / 4 * 4;
   std::vector<Item> spill;
   for (auto& q : queue)
     while (q.size() > per) {
@@ -171,19 +174,19 @@ static lazyattn_status build_run_items(const lazyattn_config* cfg, const uint64_
       q.push_back(std::move(spill.back()));
       spill.pop_back();
     }
-  // interleave: item id 8 k + x is queue x's k-th item (or an empty one)
-  size_t longest = 0;
-  for (const auto& q : queue) longest = std::max(longest, q.size());
+  for (auto& q : queue)
+    std::stable_sort(q.begin(), q.end(), [](const Item& a, const Item& b) { return a.n_entries > b.n_entries; });
   items.clear();
-  for (size_t k = 0; k < longest; ++k)
-    for (int x = 0; x < kXcds; ++x) {
-      if (k < queue[x].size()) {
-        items.push_back(std::move(queue[x][k]));
-      } else {
-        Item empty{0, 0, {}};
-        items.push_back(std::move(empty));
+  for (size_t k = 0; k < per; k += 4)
+    for (int x = 0; x < kXcds; ++x)
+      for (size_t w = 0; w < 4; ++w) {
+        if (k + w < queue[x].size()) {
+          items.push_back(std::move(queue[x][k + w]));
+        } else {
+          Item empty{0, 0, {}};
+          items.push_back(std::move(empty));
+        }
       }
-    }
   return LAZYATTN_OK;
 }
 

@@ -3,7 +3,7 @@
 The plan must cover every entry of every request exactly once, with the
 positions the kernel will give its keys; these tests rebuild each request's
 table from the plan and compare it with the input, and check the bounds the
-kernel relies on (occurrences per item, entries per item, a multiple of 8
+kernel relies on (occurrences per item, entries per item, a multiple of 32
 items) and the per-request occurrence lists the merge reads.
 """
 import numpy as np
@@ -56,7 +56,7 @@ def _check_plan(cfg, words, ne, ctx, num_blocks):
     begin, rrefs = plan["req_ref_begin"], plan["req_refs"]
     G = cfg.num_q_heads // cfg.num_kv_heads
     R = len(ne)
-    assert items.shape[0] % 8 == 0
+    assert items.shape[0] % 32 == 0
     got = [[] for _ in range(R)]
     seen_refs = set()
     for it in items:
@@ -153,5 +153,5 @@ def test_plan_errors():
     st = _abi.lib().lazyattn_decode_runs_plan(ctypes.byref(_cfg()), words.ctypes.data, 1, words.shape[1],
                                              ne.ctypes.data, ctx.ctypes.data, 4, 0, 0, 0, None, None, None, None,
                                              None, ctypes.byref(ni), ctypes.byref(nw), ctypes.byref(nr))
-    assert st == _abi.EWORKSPACE and ni.value == 8 and nw.value == 2 and nr.value == 1
+    assert st == _abi.EWORKSPACE and ni.value == 32 and nw.value == 2 and nr.value == 1
     assert _abi.decode_runs_workspace_size(_cfg(), 3) == 3 * 32 * (128 * 2 + 8)
