@@ -199,11 +199,12 @@ lazyattn_status lazyattn_validate_tables(const lazyattn_config* cfg, const uint6
 int32_t lazyattn_prefill_splits(const lazyattn_config* cfg, int32_t num_reqs, int32_t max_q_len,
                                 int32_t max_entries);
 /* Split count for a prefill call whose table lengths the caller knows on the
- * host (total_entries = the sum of num_entries over the batch's requests):
- * at least lazyattn_prefill_splits(), and enough that the longest request's
- * share of keys per work-group is about the mean request's, so that a batch of
- * unequal lengths does not wait on its longest request; at most one split per
- * 64 entries of the longest request, and at most 64.  Pass the result as
+ * host (max_entries = the longest request's num_entries, total_entries = their
+ * sum over the batch's requests): at least lazyattn_prefill_splits(), and
+ * ceil(longest / mean - 0.1), enough that the longest request's share of keys
+ * per work-group is about the mean request's, so that a batch of unequal
+ * lengths does not wait on its longest request; at most one split per 64
+ * entries of the longest request, and at most 64.  Pass the result as
  * num_splits (and to the workspace size).  Returns 0 for an invalid config. */
 int32_t lazyattn_prefill_splits_balanced(const lazyattn_config* cfg, int32_t num_reqs, int32_t max_q_len,
                                          int32_t max_entries, int64_t total_entries);

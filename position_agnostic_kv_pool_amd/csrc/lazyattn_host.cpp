@@ -224,8 +224,10 @@ int32_t lazyattn_prefill_splits_balanced(const lazyattn_config* cfg, int32_t num
   if (check_config(cfg) != LAZYATTN_OK) return 0;
   int s = choose_prefill_splits(cfg, num_reqs, max_q_len, max_entries);
   if (num_reqs < 1 || total_entries < 1 || max_entries < 1 || cfg->dtype != LAZYATTN_BF16) return s;
-  // ceil(longest / mean): the longest request's share per work-group comes down to about the mean's
-  const long long imb = (static_cast<long long>(max_entries) * num_reqs + total_entries - 1) / total_entries;
+  // ceil(longest / mean - 0.1): the longest request's share per work-group comes down to about
+  // the mean's (a ratio within 0.1 above a whole number does not take one more split)
+  const long long num = 10LL * max_entries * num_reqs - total_entries, den = 10LL * total_entries;
+  const long long imb = std::max(1LL, (num + den - 1) / den);
   const long long cap = std::max(1, max_entries / 64);   // at least 16 key tiles per split
   const long long want = std::min<long long>(imb, cap);
   return static_cast<int32_t>(std::max<long long>(s, std::min<long long>(want, 64)));

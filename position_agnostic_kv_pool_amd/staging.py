@@ -172,8 +172,9 @@ class PrefillCall:
         self.out = torch.empty_like(self.q)
         R = len(inputs["ctx_lens"])
         if num_splits is None:
-            num_splits = _abi.prefill_splits_balanced(cfg, R, self.max_q_len, self.tables.batch.max_entries,
-                                                      int(np.sum(inputs["num_entries"], dtype=np.int64)))
+            ne = np.asarray(inputs["num_entries"], dtype=np.int64)
+            num_splits = _abi.prefill_splits_balanced(cfg, R, self.max_q_len, int(ne.max(initial=0)),
+                                                      int(ne.sum()))
         self.num_splits = num_splits
         self.splits = num_splits if num_splits > 0 else \
             _abi.prefill_splits(cfg, R, self.max_q_len, self.tables.batch.max_entries)

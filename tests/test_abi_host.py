@@ -261,6 +261,11 @@ def test_balanced_prefill_splits():
     # the longest request 2.2x the mean: three splits bring its share per work-group to the mean's
     assert _abi.prefill_splits_balanced(c, 32, 128, 1445, 20832) == 3
     assert _abi.prefill_splits_balanced(c, 32, 128, 969, 16000) == 2
+    # a ratio just above a whole number takes no extra split (70B: 2176 entries each, a table stride of 2184)
+    c70 = _cfg(num_q_heads=64, num_kv_heads=8)
+    assert _abi.prefill_splits_balanced(c70, 4, 2048, 2184, 4 * 2176) == 1
+    assert _abi.prefill_splits_balanced(c, 32, 128, 1100, 32 * 1000) == 1
+    assert _abi.prefill_splits_balanced(c, 32, 128, 1150, 32 * 1000) == 2
     # never fewer than the plain heuristic (8B shape: too few work-groups, 2 splits)
     c8 = _cfg(num_q_heads=32, num_kv_heads=8)
     assert _abi.prefill_splits_balanced(c8, 16, 64, 260, 16 * 260) == _abi.prefill_splits(c8, 16, 64, 260) == 2

@@ -155,3 +155,27 @@ def test_plan_errors():
                                              None, ctypes.byref(ni), ctypes.byref(nw), ctypes.byref(nr))
     assert st == _abi.EWORKSPACE and ni.value == 32 and nw.value == 2 and nr.value == 1
     assert _abi.decode_runs_workspace_size(_cfg(), 3) == 3 * 32 * (128 * 2 + 8)
+
+
+def test_decode_runs_rejects_bad_arguments_before_launch():
+    import ctypes
+    lib = _abi.lib()
+    P = ctypes.c_void_p(64)
+    plan = _abi.RunPlan()
+    plan.num_items, plan.num_words, plan.num_refs = 32, 4, 2
+    plan.items = plan.words = plan.refs = plan.req_ref_begin = plan.req_refs = 64   # never dereferenced on the host
+    c = _cfg()
+    call = lambda cfg, pl, ws, nws: lib.lazyattn_decode_runs(ctypes.byref(cfg), P, P, P, 8, 2, pl, P, ws, nws, None)
+    need = _abi.decode_runs_workspace_size(c, 2)
+    assert call(c, None, P, need) == _abi.EINVAL                                   # no plan
+    assert call(c, ctypes.byref(plan), None, 0) == _abi.EWORKSPACE                 # no room for the partials
+    assert call(c, ctypes.byref(plan), P, need - 1) == _abi.EWORKSPACE
+    assert call(_cfg(32, 1), ctypes.byref(plan), P, need) == _abi.EUNSUPPORTED      # G = 32
+    odd = _abi.RunPlan()
+    odd.num_items, odd.num_words, odd.num_refs = 8, 4, 2                          # not a multiple of 32
+    odd.items = odd.words = odd.refs = odd.req_ref_begin = odd.req_refs = 64
+    assert call(c, ctypes.byref(odd), P, need) == _abi.EINVAL
+    plan.req_ref_begin = None
+    assert call(c, ctypes.byref(plan), P, need) == _abi.EINVAL
+    empty = _abi.RunPlan()                                                        # no requests: nothing to do
+    assert lib.lazyattn_decode_runs(ctypes.byref(c), P, P, P, 8, 0, ctypes.byref(empty), P, None, 0, None) == _abi.OK
