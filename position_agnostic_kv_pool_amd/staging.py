@@ -156,10 +156,12 @@ class PrefillCall:
 
     def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: Optional[int] = None,
                  block_permutation=None, framed: bool = False, req_order="longest_first"):
-        """num_splits: None = chosen here from the batch's table lengths (known on the host) with
-        lazyattn_prefill_splits_balanced; 0 = the library's own heuristic; > 0 = that many.
-        req_order: the order in which the work-groups take the requests: "longest_first"
-        (longest table first), None (batch order) or an int32 array; the results are the same."""
+        """req_order: the order in which the work-groups take the requests: "longest_first"
+        (longest table first), None (batch order) or an int32 array; the results are the same.
+        num_splits: None = the library's own heuristic when the requests are taken longest first
+        (the short requests then fill the end of the launch: splitting the long ones for balance
+        no longer pays), else chosen from the batch's table lengths (known on the host) with
+        lazyattn_prefill_splits_balanced; 0 = the library's own heuristic; > 0 = that many."""
         self.cfg = cfg
         order = longest_first(inputs["num_entries"]) if isinstance(req_order, str) else req_order
         if isinstance(req_order, str) and req_order != "longest_first":
@@ -171,6 +173,8 @@ class PrefillCall:
         self.max_q_len = int(inputs["max_q_len"])
         self.out = torch.empty_like(self.q)
         R = len(inputs["ctx_lens"])
+        if num_splits is None and isinstance(req_order, str):
+            num_splits = 0
         if num_splits is None:
             ne = np.asarray(inputs["num_entries"], dtype=np.int64)
             num_splits = _abi.prefill_splits_balanced(cfg, R, self.max_q_len, int(ne.max(initial=0)),
