@@ -317,7 +317,8 @@ lazyattn_status lazyattn_decode_noalloc(const lazyattn_config* cfg, const void* 
  * partial (o / l in fp16, m, l), and a second kernel merges each request's
  * partials by log-sum-exp in occurrence order.  Results equal
  * lazyattn_decode's up to rounding (the query is rounded to bf16 after its
- * turn; the summation order differs). */
+ * turn; the summation order differs).  The partials are IEEE half, so every
+ * value must satisfy |v| <= 65504, as for a split lazyattn_decode call. */
 #define LAZYATTN_RUN_ITEM_INTS 4
 typedef struct {
   int32_t num_items;              /* work items; a multiple of 32, padded with empty items */
