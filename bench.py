@@ -295,10 +295,18 @@ def bench_headline(torch, args, W, staging, _abi):
     staging.append_tokens(cfg, pools, pb, s.dtype, "cuda")
     call = staging.PrefillCall(cfg, s, pb, "cuda")
     call_none = staging.PrefillCall(cfg_none, s, pb, "cuda")
+    # the same RoPE call with the keys turned inside the attention kernel (the library
+    # turns them once first for this chunk of 64 query tiles per request and KV head)
+    call_fused = staging.PrefillCall(staging.config_for(s, keys="fused"), s, pb, "cuda")
+    keys_once = _abi.prefill_workspace_size(cfg, len(pb["ctx_lens"]), call.total_q, call.max_q_len,
+                                            call.tables.batch.max_entries, call.num_splits) > \
+        _abi.prefill_workspace_size(call_fused.cfg, len(pb["ctx_lens"]), call.total_q, call.max_q_len,
+                                    call.tables.batch.max_entries, call.num_splits)
     torch.cuda.synchronize()
     timer = Timer(torch)
     fns = [lambda: call.attend(pools)] + ([call.merge] if call.splits > 1 else [])
     fns_none = [lambda: call_none.attend(pools)] + ([call_none.merge] if call_none.splits > 1 else [])
+    fns_fused = [lambda: call_fused.attend(pools)] + ([call_fused.merge] if call_fused.splits > 1 else [])
     for _ in range(args.warmup):
         call.run(pools)
     torch.cuda.synchronize()
@@ -307,17 +315,19 @@ def bench_headline(torch, args, W, staging, _abi):
     step_ms = [sum(x) for x in st]
     kern_ms = [x[0] for x in st]
     print(f"# headline prefill: {sum(step_ms) / len(step_ms) * 1e3:.1f} us/step (cold)", file=sys.stderr, flush=True)
-    # RoPE against the rotation-free control: alternating cold steps, then alternating warm spans
-    st_rope, st_none = timer.rounds([fns, fns_none], max(6, args.steps // 2), cold=True)
+    # RoPE against the rotation-free control (and the keys turned in the attention
+    # kernel): alternating cold steps, then alternating warm spans
+    st_rope, st_none, st_fused = timer.rounds([fns, fns_none, fns_fused], max(6, args.steps // 2), cold=True)
     warm, warm_none = timer.span_rounds([lambda: call.run(pools), lambda: call_none.run(pools)],
                                         max(3, args.steps // 4))
-    require_finite(torch, "70B prefill", call.out, call_none.out)
+    require_finite(torch, "70B prefill", call.out, call_none.out, call_fused.out)
     flops = prefill_flops(pb, s.head_dim, s.num_q_heads)
     pre = dict(ms=sum(step_ms) / len(step_ms), step_ms=step_ms, kern_ms=kern_ms, flops=flops, splits=call.splits,
                rope_kern_ms=[x[0] for x in st_rope], none_kern_ms=[x[0] for x in st_none],
+               fused_kern_ms=[x[0] for x in st_fused], keys_once=keys_once,
                warm_ms=warm, warm_none_ms=warm_none,
                seq_len=int(max(pb["ctx_lens"])), R=len(pb["ctx_lens"]))
-    del call, call_none
+    del call, call_none, call_fused
 
     # decode steps 0..n-1: every step's token is appended first (setup); a step's call
     # reads only its own context (ctx_lens, num_entries), so later tokens are invisible to it
@@ -390,18 +400,26 @@ def headline_json(h, args):
     roofline = {"bound": "mfma", "achieved": round(kernel_tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": read_counter_summary(COUNTERS["prefill70b"]),
-                "kernel": "prefill_bf16_kernel<ROPE>", "flops_per_launch": flops,
+                "kernel": ("turn_keys_kernel + prefill_bf16_kernel<KEYS_TURNED>" if pre["keys_once"]
+                           else "prefill_bf16_kernel<ROPE>"),
+                "flops_per_launch": flops,
                 "launch_us_median_cold": round(k_med * 1e3, 2),
                 "launch_us_p10_p50_p90_cold": [round(x * 1e3, 2) for x in pct(pre["kern_ms"])],
                 "launch_us_warm_back_to_back": round(pre["warm_ms"] * 1e3, 2),
-                "note": "achieved = algorithmic FLOPs / median cold launch (the kernel's own events)"}
+                "note": "achieved = algorithmic FLOPs / median cold launch (events around the call's kernels: "
+                        "with the keys turned once, the key-turning kernel and the attention kernel together)"}
     none_med = med(pre["none_kern_ms"])
     rope_med = med(pre["rope_kern_ms"])
-    rope_overhead = {"what": "RoPE kernel against the rotation-free control on the same inputs, timed in "
-                             "alternating order (medians)",
+    fused_med = med(pre["fused_kern_ms"])
+    rope_overhead = {"what": "RoPE kernel(s) against the rotation-free control on the same inputs, timed in "
+                             "alternating order (medians); keys turned once first (the library's choice for "
+                             "this chunk) and, beside it, turned inside the attention kernel",
+                     "prefill_keys": "turned once" if pre["keys_once"] else "turned in the attention kernel",
                      "prefill_rope_us_cold": round(rope_med * 1e3, 2),
                      "prefill_norotation_us_cold": round(none_med * 1e3, 2),
                      "prefill_overhead_cold": round(rope_med / none_med - 1.0, 4),
+                     "prefill_keys_in_kernel_us_cold": round(fused_med * 1e3, 2),
+                     "prefill_keys_in_kernel_overhead_cold": round(fused_med / none_med - 1.0, 4),
                      "prefill_rope_us_warm": round(pre["warm_ms"] * 1e3, 2),
                      "prefill_norotation_us_warm": round(pre["warm_none_ms"] * 1e3, 2),
                      "prefill_overhead_warm": round(pre["warm_ms"] / pre["warm_none_ms"] - 1.0, 4),
@@ -676,8 +694,12 @@ def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
             pcs[pe].run(pools)
             dcs[pe].run(pools)
             mixed(pcs[pe], dcs[pe], pools)
+        # RoPE with the keys turned inside the attention kernel (the library turns them
+        # once first for these 16 query tiles per request)
+        pc_fused = staging.PrefillCall(staging.config_for(s, keys="fused"), s, pb, "cuda")
+        pc_fused.run(pools)
         # the three encodings in alternating order: prefill, decode, mixed step
-        tps = timer.span_rounds([lambda pc=pcs[pe]: pc.run(pools) for pe in pes], 10)
+        tps = timer.span_rounds([lambda pc=pcs[pe]: pc.run(pools) for pe in pes] + [lambda: pc_fused.run(pools)], 10)
         tds = timer.span_rounds([lambda dc=dcs[pe]: dc.run(pools) for pe in pes], 10)
         tms = timer.span_rounds([lambda pe=pe: mixed(pcs[pe], dcs[pe], pools) for pe in pes], 10)
         for v, pe in enumerate(pes):
@@ -690,13 +712,16 @@ def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
                        "mixed_step_us": round(tm * 1e3, 2),
                        "overlap_gain": round((tp + td) / tm, 3)}
         row["prefill_rope_overhead"] = round(row["rope"]["prefill_us"] / row["none"]["prefill_us"] - 1.0, 4)
+        require_finite(torch, f"MQA stress skew {skew} (rope, keys in the kernel)", pc_fused.out)
+        row["prefill_rope_keys_in_kernel_us"] = round(tps[len(pes)] * 1e3, 2)
+        row["prefill_rope_keys_in_kernel_overhead"] = round(tps[len(pes)] / tps[pes.index("none")] - 1.0, 4)
         row["decode_rope_overhead"] = round(row["rope"]["decode_us"] / row["none"]["decode_us"] - 1.0, 4)
         row["mixed_rope_overhead"] = round(row["rope"]["mixed_step_us"] / row["none"]["mixed_step_us"] - 1.0, 4)
         row["decode_GB_unique"] = round(by["unique"] / 1e9, 4)
         row["decode_GB_logical"] = round(by["logical"] / 1e9, 4)
         row["prefill_GFLOP"] = round(flops / 1e9, 1)
         out[f"skew{skew}"] = row
-        del pools
+        del pools, pc_fused
         torch.cuda.empty_cache()
     return out
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LAZYATTN_ABI_VERSION 8
+#define LAZYATTN_ABI_VERSION 9
 
 typedef enum {
   LAZYATTN_OK = 0,
@@ -83,6 +83,24 @@ typedef enum { LAZYATTN_PE_ROPE = 0, LAZYATTN_PE_NONE = 1, LAZYATTN_PE_ALIBI = 2
  * tile and redoing only when a later score outgrows it; same results up to
  * rounding, for validation. */
 #define LAZYATTN_FLAG_EXACT_MAX 1
+
+/* Where the bf16 prefill turns the keys of a content-only pool (pe ROPE, plain
+ * pool, no frame_starts).  The pages rotate each staged key tile inside the
+ * attention kernel (gist.science, Technical Implementation > Prefilling), so a
+ * chunk of many query tiles turns the same key once per query tile.  With
+ * KEYS_ONCE the call first turns every key of every request once, by
+ * R(t - c_r) with c_r = ctx_lens[r] - q_len_r (the position of the request's
+ * first new token), into the workspace, then attends with the queries turned
+ * by R(m - c_r) and no rotation in the attention kernel; the pool itself is
+ * never written.  KEYS_FUSED keeps the rotation inside the attention kernel.
+ * With neither flag the library turns the keys once when a request spans at
+ * least LAZYATTN_KEYS_ONCE_TILES query tiles of 256 rows (ceil(max_q_len /
+ * floor(256 / G)) >= 8), where it measured faster.  Both flags set:
+ * LAZYATTN_EINVAL.  The two routes give the same result up to rounding; other
+ * encodings, FP8 pools, framed batches and the decode ignore both flags. */
+#define LAZYATTN_FLAG_KEYS_FUSED 2
+#define LAZYATTN_FLAG_KEYS_ONCE 4
+#define LAZYATTN_KEYS_ONCE_TILES 8
 
 /* Pool formats (lazyattn_config.kv_format).
  *
@@ -221,8 +239,14 @@ int32_t lazyattn_decode_splits(const lazyattn_config* cfg, int32_t num_reqs, int
  * IEEE half, so a call with S > 1 requires |v| <= 65504 for every value it
  * reads (a larger value overflows its partial and the merged output is not
  * finite); with S = 1 the output is written as bf16 directly and no such limit
- * applies.  The workspace needs no initialisation; calls that may run
- * concurrently must not share one. */
+ * applies.  A prefill call that turns the keys once (LAZYATTN_FLAG_KEYS_ONCE,
+ * or the library's choice without a flag) also holds the turned keys there,
+ * after the partials rounded up to 256 bytes: num_reqs * max_entries blocks
+ * in the pool's K layout ([Hkv][16][D] bf16 each, entry e of request r at
+ * block r * max_entries + e), num_reqs * max_entries * Hkv * 4096 bytes; the
+ * size counts them whenever the route would be taken for these sizes (a framed
+ * batch, which does not take it, needs less).  The workspace needs no
+ * initialisation; calls that may run concurrently must not share one. */
 size_t lazyattn_prefill_workspace_size(const lazyattn_config* cfg, int32_t num_reqs, int32_t total_q,
                                        int32_t max_q_len, int32_t max_entries, int32_t num_splits);
 size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_reqs,
@@ -245,8 +269,10 @@ size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_re
  *  out        device [total_q][Hq][D]
  *  workspace  device, >= lazyattn_prefill_workspace_size(...) bytes (may be
  *             NULL when that size is 0).
- *  Launches the attention kernel and, when the key range is split, the merge
- *  kernel (lazyattn_prefill_attend followed by lazyattn_merge_splits). */
+ *  Launches the key-turning kernel when the keys are turned once (see
+ *  LAZYATTN_FLAG_KEYS_ONCE), the attention kernel and, when the key range is
+ *  split, the merge kernel (lazyattn_prefill_attend followed by
+ *  lazyattn_merge_splits). */
 lazyattn_status lazyattn_prefill(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
                                  int32_t total_q, int32_t max_q_len, const void* k_pool,
                                  const void* v_pool, int64_t num_blocks, const lazyattn_batch* batch,
@@ -371,7 +397,8 @@ lazyattn_status lazyattn_decode_runs(const lazyattn_config* cfg, const void* q, 
                                      size_t workspace_bytes, hipStream_t stream);
 
 /* The attention kernel of lazyattn_prefill / lazyattn_decode alone (same
- * arguments).  With one split it writes `out` directly; with S > 1 splits
+ * arguments; for a prefill that turns the keys once, the key-turning kernel
+ * and then the attention kernel).  With one split it writes `out` directly; with S > 1 splits
  * (see lazyattn_prefill_splits / lazyattn_decode_splits for num_splits 0) it
  * writes partials to `workspace` and leaves `out` untouched until
  * lazyattn_merge_splits runs on the same stream.  For callers that schedule

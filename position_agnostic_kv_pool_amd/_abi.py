@@ -20,6 +20,10 @@ LIB_PATH = os.environ.get("LAZYATTN_LIBRARY") or os.path.join(_PKG, "liblazyattn
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 FLAG_EXACT_MAX = 1          # LAZYATTN_FLAG_EXACT_MAX
+FLAG_KEYS_FUSED = 2         # LAZYATTN_FLAG_KEYS_FUSED: the prefill turns keys inside the attention kernel
+FLAG_KEYS_ONCE = 4          # LAZYATTN_FLAG_KEYS_ONCE: the prefill turns each key once first
+KEYS_ONCE_TILES = 8         # LAZYATTN_KEYS_ONCE_TILES
+_KEYS = {None: 0, "auto": 0, "fused": FLAG_KEYS_FUSED, "once": FLAG_KEYS_ONCE}
 F32, BF16 = 0, 1
 PE_ROPE, PE_NONE, PE_ALIBI = 0, 1, 2
 _PE = {"rope": PE_ROPE, "none": PE_NONE, "alibi": PE_ALIBI}
@@ -166,16 +170,18 @@ def _check(status: int, where: str):
 def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str = "bf16", pe: str = "rope",
                 rope_theta: float = 10000.0, softmax_scale: float = 0.0, alibi_slopes=None,
                 block_size: int = 16, exact_max: bool = False, inv_freq: np.ndarray = None,
-                kv_format: str = "plain") -> Config:
+                kv_format: str = "plain", keys: str = None) -> Config:
     """inv_freq: optional host float64 [head_dim/2] RoPE frequency table (kept alive by the config);
-    kv_format "plain" or "fp8" (e4m3 chunks of FP8_CHUNK_BYTES per block and KV head)."""
+    kv_format "plain" or "fp8" (e4m3 chunks of FP8_CHUNK_BYTES per block and KV head);
+    keys: where the RoPE prefill turns the keys, "fused" (in the attention kernel), "once" (one
+    pass over each request's keys first) or None / "auto" (the library's choice)."""
     c = Config()
     c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size = num_q_heads, num_kv_heads, head_dim, block_size
     c.dtype = _DT[dtype] if isinstance(dtype, str) else int(dtype)
     c.pe = _PE[pe] if isinstance(pe, str) else int(pe)
     c.rope_theta = float(rope_theta)
     c.softmax_scale = float(softmax_scale)
-    c.flags = FLAG_EXACT_MAX if exact_max else 0
+    c.flags = (FLAG_EXACT_MAX if exact_max else 0) | _KEYS[keys]
     c.alibi_slopes = _ptr(alibi_slopes) if alibi_slopes is not None else None
     f = None
     if inv_freq is not None:

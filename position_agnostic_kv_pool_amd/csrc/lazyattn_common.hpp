@@ -43,6 +43,12 @@ int prefill_positions_per_tile(int group);
 int choose_prefill_splits(const lazyattn_config* cfg, int num_reqs, int max_q_len, int max_entries);
 int choose_decode_splits(const lazyattn_config* cfg, int num_reqs, int max_entries);
 int prefill_entries_per_split(int max_entries, int splits);
+// The prefill's key-turning route (LAZYATTN_FLAG_KEYS_ONCE) and its workspace:
+// split partials first, then the turned keys from a 256-byte boundary
+bool prefill_keys_once(const lazyattn_config* cfg, int max_q_len);
+size_t prefill_partials_bytes(const lazyattn_config* cfg, int total_q, int splits);
+size_t prefill_turned_keys_offset(size_t partials_bytes);
+size_t prefill_turned_keys_bytes(const lazyattn_config* cfg, int num_reqs, int max_entries);
 int decode_entries_per_split(int max_entries, int splits);
 // decode work-groups per (request, KV head, split): 2 for groups of more than 16 heads
 int decode_halves(int group);

@@ -16,7 +16,9 @@ lazyattn_status check_config(const lazyattn_config* cfg) {
   if (!cfg) return LAZYATTN_EINVAL;
   if (cfg->num_q_heads < 1 || cfg->num_kv_heads < 1) return LAZYATTN_EINVAL;
   if (cfg->num_q_heads % cfg->num_kv_heads != 0) return LAZYATTN_EINVAL;
-  if ((cfg->flags & ~LAZYATTN_FLAG_EXACT_MAX) != 0) return LAZYATTN_EINVAL;
+  constexpr int32_t known = LAZYATTN_FLAG_EXACT_MAX | LAZYATTN_FLAG_KEYS_FUSED | LAZYATTN_FLAG_KEYS_ONCE;
+  if ((cfg->flags & ~known) != 0) return LAZYATTN_EINVAL;
+  if ((cfg->flags & LAZYATTN_FLAG_KEYS_FUSED) && (cfg->flags & LAZYATTN_FLAG_KEYS_ONCE)) return LAZYATTN_EINVAL;
   if (cfg->dtype != LAZYATTN_F32 && cfg->dtype != LAZYATTN_BF16) return LAZYATTN_EINVAL;
   if (cfg->pe != LAZYATTN_PE_ROPE && cfg->pe != LAZYATTN_PE_NONE && cfg->pe != LAZYATTN_PE_ALIBI)
     return LAZYATTN_EINVAL;
@@ -76,6 +78,32 @@ int choose_prefill_splits(const lazyattn_config* cfg, int num_reqs, int max_q_le
   // keep at least 16 key tiles (64 entries) per split
   s = std::min(s, std::max(1, max_entries / 64));
   return std::max(1, std::min(s, 64));
+}
+
+// The bf16 prefill over a plain content-only pool turns every key once before
+// attending when asked to, or by default when a request spans at least
+// LAZYATTN_KEYS_ONCE_TILES query tiles: each key is then staged by that many
+// work-groups, and turning it in each of them costs more vector work than one
+// pass that reads and writes the keys once.
+bool prefill_keys_once(const lazyattn_config* cfg, int max_q_len) {
+  if (cfg->dtype != LAZYATTN_BF16 || cfg->pe != LAZYATTN_PE_ROPE || cfg->kv_format != LAZYATTN_KV_PLAIN) return false;
+  if (cfg->flags & LAZYATTN_FLAG_KEYS_FUSED) return false;
+  if (cfg->flags & LAZYATTN_FLAG_KEYS_ONCE) return true;
+  const int group = cfg->num_q_heads / cfg->num_kv_heads;
+  return ceil_div(std::max(1, max_q_len), prefill_positions_per_tile(group)) >= LAZYATTN_KEYS_ONCE_TILES;
+}
+
+size_t prefill_partials_bytes(const lazyattn_config* cfg, int total_q, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(total_q) * cfg->num_q_heads;
+  return static_cast<size_t>(splits) * rows * (static_cast<size_t>(cfg->head_dim) * sizeof(uint16_t) + 2 * sizeof(float));
+}
+
+size_t prefill_turned_keys_offset(size_t partials_bytes) { return (partials_bytes + 255) / 256 * 256; }
+
+size_t prefill_turned_keys_bytes(const lazyattn_config* cfg, int num_reqs, int max_entries) {
+  return static_cast<size_t>(num_reqs) * static_cast<size_t>(std::max(0, max_entries)) * cfg->num_kv_heads * kBlock *
+         cfg->head_dim * sizeof(uint16_t);
 }
 
 int decode_halves(int group) { return group > 16 ? 2 : 1; }
@@ -243,9 +271,9 @@ size_t lazyattn_prefill_workspace_size(const lazyattn_config* cfg, int32_t num_r
   if (check_config(cfg) != LAZYATTN_OK || num_reqs < 0 || total_q < 0) return 0;
   if (cfg->dtype != LAZYATTN_BF16) return 0;  // the fp32 path never splits
   int s = num_splits > 0 ? num_splits : choose_prefill_splits(cfg, num_reqs, max_q_len, max_entries);
-  if (s <= 1) return 0;
-  const size_t rows = static_cast<size_t>(total_q) * cfg->num_q_heads;
-  return static_cast<size_t>(s) * rows * (static_cast<size_t>(cfg->head_dim) * sizeof(uint16_t) + 2 * sizeof(float));
+  const size_t part = prefill_partials_bytes(cfg, total_q, s);
+  if (!prefill_keys_once(cfg, max_q_len) || num_reqs == 0) return part;
+  return prefill_turned_keys_offset(part) + prefill_turned_keys_bytes(cfg, num_reqs, max_entries);
 }
 
 size_t lazyattn_decode_workspace_size(const lazyattn_config* cfg, int32_t num_reqs,

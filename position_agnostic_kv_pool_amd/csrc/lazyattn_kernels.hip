@@ -224,6 +224,7 @@ struct PrefillArgs {
   uint16_t* out;
   uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
   float* ml_part;                // and (m, l) [splits][rows][Hq][2]
+  const uint16_t* kturned;       // keys turned once (kPeKeysTurned): block r * max_entries + e = entry e of request r
   int32_t Hq, Hkv, G, max_entries, total_q, m_q, eps, splits;
   int32_t n_qt;                  // query tiles per request (the grid's x extent is n_qt * splits)
   int32_t exact;                 // nonzero: always take the two-pass exact-maximum route
@@ -235,6 +236,11 @@ constexpr int kPD = 128;                 // head dim of the bf16 kernels
 // Kernel instantiation for RoPE over a pool in document-local frames: a key
 // row at logical position t is stored as R(t - F) k, F its entry's frame start
 constexpr int kPeFramed = 3;
+// Kernel instantiation for RoPE over keys already turned once per request by
+// R(t - c), c = the request's first new position (turn_keys_kernel): the
+// attention kernel turns only the queries, by R(m - c), and stages the keys
+// as the rotation-free kernel does
+constexpr int kPeKeysTurned = 4;
 constexpr int kPrefillThreads = 512;    // threads per prefill work-group
 constexpr int kKS = kPD + 8;             // K~ row stride in bf16 (272 B: conflict-free 16 B reads)
 // V of one entry in LDS: two planes [token half][channel][8 tokens], so that an
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   const int m0 = qt * A.m_q;
   if (m0 >= q_len) return;
   const int L = A.ctx[r];
-  const int ne = A.n_ent[r];
+  const int ne = min(A.n_ent[r], A.max_entries);
   const int p0 = L - q_len + m0;                      // position of the tile's first row
   const int mq = min(A.m_q, q_len - m0);
   const int p_last = p0 + mq - 1;
@@ -340,7 +346,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   // run 3-8 % faster than with it after the products).  Otherwise those slots
   // hold the rotation, and the staging stays between the QK and P.V phases,
   // where it measured fastest.
-  constexpr bool kStageEarly = !KV8 && (PE == LAZYATTN_PE_NONE || PE == LAZYATTN_PE_ALIBI);
+  constexpr bool kTurned = PE == kPeKeysTurned;
+  constexpr bool kStageEarly = !KV8 && (PE == LAZYATTN_PE_NONE || PE == LAZYATTN_PE_ALIBI || kTurned);
 
   // ---- table words: lanes x = 0..4 (mod 8) hold word e0 + x of a tile ------------
   // Where the staging work is spread among the QK products (kStageEarly) every
@@ -370,6 +377,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     blk = valid ? b : 0;
     st = valid ? s0 : L;
     ln = valid ? s1 - s0 : 0;
+  };
+  // where the keys of entry x of tile j are read: the pool block, or (keys
+  // turned once) the request's own turned copy of the entry, the split's first
+  // entry standing in past the split's end
+  auto k_index = [&](int j, int x, int blk) -> uint32_t {
+    if constexpr (!kTurned) return static_cast<uint32_t>(blk);
+    const int e = tile_e0(j) + x;
+    return static_cast<uint32_t>(r) * static_cast<uint32_t>(A.max_entries) +
+           static_cast<uint32_t>(e < e_stop ? e : e_begin);
   };
 
   // frame starts (framed pool): lanes x = 0..3 (mod 8) hold entry e0 + x of a tile
@@ -412,8 +428,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   uint2 kx = make_uint2(0, 0), vx = make_uint2(0, 0);
   // entries past the split's end (length 0) read block 0: their keys are
   // masked out of the scores and their V rows zeroed when staged
-  auto load_k = [&](int blk) {
-    const size_t base = static_cast<size_t>(static_cast<uint32_t>(blk)) * Hkv + kvh;
+  auto load_k = [&](uint32_t kb) {
+    const size_t base = static_cast<size_t>(kb) * Hkv + kvh;
     if (KV8) {
       const uint8_t* kc = reinterpret_cast<const uint8_t*>(A.kpool) + base * kChunk8;
       const uint16_t* kp = reinterpret_cast<const uint16_t*>(kc + 8 * part * kPD) + lane;
@@ -421,7 +437,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
       kx = *reinterpret_cast<const uint2*>(kc + 16 * kPD + 8 * part);
     } else {
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(A.kpool + base * (kBlock * kPD) + 8 * part * kPD) + lane;
+      const uint16_t* ksrc = kTurned ? A.kturned : A.kpool;
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(ksrc + base * (kBlock * kPD) + 8 * part * kPD) + lane;
 #pragma unroll
       for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
     }
@@ -443,8 +460,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       for (int cc = 0; cc < 2; ++cc) vr[cc] = *reinterpret_cast<const uint4*>(vp + 32 * cc * kBlock);
     }
   };
-  auto load_kv = [&](int blk) {
-    load_k(blk);
+  auto load_kv = [&](uint32_t kb, int blk) {
+    load_k(kb);
     load_v(blk);
   };
   // FP8: the staged key row k (its codes, times 2^exponent) as bf16, turned by ph
@@ -500,7 +517,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     stage_write_v(b);
   };
 
-  // ---- query: rotated by R(m), scaled by scale*log2(e), rounded to bf16 -----------
+  // ---- query: rotated by R(m - p0) (R(m - c) for keys turned once), scaled by ----
+  // ---- scale*log2(e), rounded to bf16 --------------------------------------------
   // B operand of k-step kk: channels 16 kk + 8 h .. + 7 of the row
   bf16x8 qf[8 * NT];
 #pragma unroll
@@ -515,8 +533,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         float x0 = bf_lo(w4[jj]), x1 = bf_hi(w4[jj]);
-        if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) {
-          const float2 ph = unit_phase_turns_small(p_row[nt] - p0, A.rope.rev[8 * kk + 4 * h + jj]);
+        if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed || kTurned) {
+          // R(m - p0) against keys turned by R(t - p0); R(m - c) against keys turned once
+          const float2 ph = kTurned ? unit_phase_turns(p_row[nt] - (L - q_len), A.rope.rev[8 * kk + 4 * h + jj])
+                                    : unit_phase_turns_small(p_row[nt] - p0, A.rope.rev[8 * kk + 4 * h + jj]);
           const float y0 = x0 * ph.x - x1 * ph.y;
           const float y1 = x0 * ph.y + x1 * ph.x;
           x0 = y0;
@@ -561,13 +581,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     {
       int blk, st, ln;
       entry_of(wv0, 0, E_own, blk, st, ln);
+      const uint32_t kb0 = k_index(0, E_own, blk);
       int fv0 = 0;
       if (PE == kPeFramed) {
         fv0 = load_frames(0);
         fv1 = load_frames(1);
         fv2 = load_frames(2);
       }
-      load_kv(blk);
+      load_kv(kb0, blk);
       if (PE == LAZYATTN_PE_ROPE) {
         float2 ph = unit_phase_turns(st - p0 + 8 * part, rev_l), pq;
 #pragma unroll
@@ -589,7 +610,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       if (ln < kBlock) mask_v(ln);
       stage_write(0);
       entry_of(wv1, 1, E_own, blk, st, ln);
-      load_kv(blk);
+      load_kv(k_index(1, E_own, blk), blk);
     }
     __syncthreads();
     for (int i = 0; i < T; ++i) {
@@ -649,7 +670,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         entry_of(wv2, i + 2, E_own, lblk, lst, lln);
         wv3 = load_words(i + 3);
         fv3 = load_frames(i + 3);
-        load_k(lblk);
+        load_k(k_index(i + 2, E_own, lblk));
       } else {
         // rare: only entries shorter than a block need their padding zeroed
         if (__builtin_expect(nln < kBlock, 0)) mask_v(nln);
@@ -657,7 +678,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
         entry_of(wv2, i + 2, E_own, lblk, lst, lln);
         wv3 = load_words(i + 3);
         fv3 = load_frames(i + 3);
-        load_kv(lblk);
+        load_kv(k_index(i + 2, E_own, lblk), lblk);
       }
 
       // register r of half tau: key row 8 h + (r % 8) of entry 2 tau + r / 8
@@ -1546,6 +1567,49 @@ __global__ __launch_bounds__(256) void materialize_kernel(const uint16_t* kpool,
   reinterpret_cast<uint4*>(dv + db)[tid] = reinterpret_cast<const uint4*>(vpool + sb)[tid];
 }
 
+// Keys turned once for the prefill (LAZYATTN_FLAG_KEYS_ONCE).  Wave w of
+// work-group (x, r) takes entry e = 4 x + w of request r and writes every KV
+// head's 16 key rows, each turned by R(t - c) (t its position, c = the
+// request's first new position), to block r * max_entries + e of `out`, in
+// the pool's K layout.  Lane l moves 16 bytes of rows l / 16 + 4 i
+// (i = 0..3), channels 8 (l % 16) .. + 7, i.e. four channel pairs: its 16
+// phases are formed once per entry (angle reduced in double) and serve every
+// head.  Rows past the entry's length are turned too; the attention kernel
+// masks their scores.
+__global__ __launch_bounds__(256) void turn_keys_kernel(const uint16_t* kpool, const uint64_t* tables,
+                                                        const int32_t* n_ent, const int32_t* ctx,
+                                                        const int32_t* cu_q, int max_entries, int Hkv,
+                                                        uint16_t* out, RopeRev rope) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = blockIdx.y;
+  const int e = 4 * static_cast<int>(blockIdx.x) + wave;
+  if (e >= min(n_ent[r], max_entries)) return;
+  const uint64_t w = tables[static_cast<size_t>(r) * max_entries + e];
+  const int c = ctx[r] - (cu_q[r + 1] - cu_q[r]);
+  const int n0 = static_cast<int>(word_start(w)) - c + (lane >> 4);
+  const int j0 = 4 * (lane & 15);
+  float2 ph[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ph[i][q] = unit_phase_turns(n0 + 4 * i, rope.rev[j0 + q]);
+  const int off = (lane >> 4) * kPD + 8 * (lane & 15);
+  const uint16_t* src = kpool + static_cast<size_t>(word_block(w)) * Hkv * (kBlock * kPD) + off;
+  uint16_t* dst = out + (static_cast<size_t>(r) * max_entries + e) * Hkv * (kBlock * kPD) + off;
+#pragma unroll 2
+  for (int kvh = 0; kvh < Hkv; ++kvh) {
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(src + kvh * (kBlock * kPD) + 4 * i * kPD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 t = make_uint4(rotate_pair(v[i].x, ph[i][0]), rotate_pair(v[i].y, ph[i][1]),
+                                 rotate_pair(v[i].z, ph[i][2]), rotate_pair(v[i].w, ph[i][3]));
+      *reinterpret_cast<uint4*>(dst + kvh * (kBlock * kPD) + 4 * i * kPD) = t;
+    }
+  }
+}
+
 // One work-group per (query row of a request, request): lane l rotates
 // channel pair l of every head of that token by R(p).
 __global__ __launch_bounds__(64) void rotate_queries_kernel(const uint16_t* q, const int32_t* cu_q,
@@ -1841,7 +1905,12 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
 
   if (G > 256) return LAZYATTN_EUNSUPPORTED;
   const int splits = num_splits > 0 ? num_splits : choose_prefill_splits(cfg, R, max_q_len, batch->max_entries);
-  const size_t need = lazyattn_prefill_workspace_size(cfg, R, total_q, max_q_len, batch->max_entries, splits);
+  // keys turned once (plain content-only pool, RoPE): after the partials in the workspace
+  const bool once = !framed && !fp8 && prefill_keys_once(cfg, max_q_len);
+  const size_t part_bytes = prefill_partials_bytes(cfg, total_q, splits);
+  const size_t need = once ? prefill_turned_keys_offset(part_bytes) +
+                                 prefill_turned_keys_bytes(cfg, R, batch->max_entries)
+                           : part_bytes;
   if (need > 0 && (!workspace || workspace_bytes < need)) return LAZYATTN_EWORKSPACE;
   const int m_q = prefill_positions_per_tile(G);
   const long long n_qt = (max_q_len + m_q - 1) / m_q;
@@ -1853,12 +1922,22 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
   PrefillArgs a{static_cast<const uint16_t*>(q), cu_q_lens, static_cast<const uint16_t*>(k_pool),
                 static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
                 batch->frame_starts, batch->req_order, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part,
-                ml_part, Hq, Hkv, G, batch->max_entries, total_q, m_q,
+                ml_part,
+                once ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(workspace) +
+                                                         prefill_turned_keys_offset(part_bytes))
+                     : nullptr,
+                Hq, Hkv, G, batch->max_entries, total_q, m_q,
                 prefill_entries_per_split(batch->max_entries, splits), splits, static_cast<int32_t>(n_qt),
                 (cfg->flags & LAZYATTN_FLAG_EXACT_MAX) ? 1 : 0, scale * kLog2e, rope};
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(Hkv));
   const dim3 block(kPrefillThreads);
-  if (fp8) {
+  if (once) {
+    hipLaunchKernelGGL(turn_keys_kernel, dim3((batch->max_entries + 3) / 4, R), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(k_pool), batch->block_tables, batch->num_entries,
+                       batch->ctx_lens, cu_q_lens, batch->max_entries, Hkv, const_cast<uint16_t*>(a.kturned), rope);
+    if ((st = launched()) != LAZYATTN_OK) return st;
+    hipLaunchKernelGGL((prefill_bf16_kernel<kPeKeysTurned, 0>), grid, block, 0, stream, a);
+  } else if (fp8) {
     switch (framed ? kPeFramed : cfg->pe) {
       case kPeFramed: hipLaunchKernelGGL((prefill_bf16_kernel<kPeFramed, 1>), grid, block, 0, stream, a); break;
       case LAZYATTN_PE_ROPE: hipLaunchKernelGGL((prefill_bf16_kernel<LAZYATTN_PE_ROPE, 1>), grid, block, 0, stream, a); break;

@@ -27,10 +27,11 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 def config_for(spec, pe: str = None, softmax_scale: float = 0.0, exact_max: bool = False,
-               inv_freq: np.ndarray = None, kv_format: str = "plain") -> _abi.Config:
+               inv_freq: np.ndarray = None, kv_format: str = "plain", keys: str = None) -> _abi.Config:
+    """keys: where the RoPE prefill turns the keys ("fused", "once", or None for the library's choice)."""
     return _abi.make_config(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.dtype,
                             pe or spec.pe, spec.rope_theta, softmax_scale, block_size=spec.block_size,
-                            exact_max=exact_max, inv_freq=inv_freq, kv_format=kv_format)
+                            exact_max=exact_max, inv_freq=inv_freq, kv_format=kv_format, keys=keys)
 
 
 class DevicePools:

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert _abi.lib().lazyattn_abi_version() == 8
+    assert _abi.lib().lazyattn_abi_version() == 9
     for s in range(5):
         assert len(_abi.status_string(s)) > 0
     assert _abi.status_string(99) == "unknown status"
@@ -132,7 +132,11 @@ def test_config_errors():
     assert check(C(rope_theta=0.0, pe="none")) == _abi.OK
     c = C(); c.flags = _abi.FLAG_EXACT_MAX
     assert check(c) == _abi.OK
-    c = C(); c.flags = 2
+    c = C(); c.flags = _abi.FLAG_KEYS_FUSED | _abi.FLAG_EXACT_MAX
+    assert check(c) == _abi.OK
+    c = C(); c.flags = _abi.FLAG_KEYS_FUSED | _abi.FLAG_KEYS_ONCE
+    assert check(c) == _abi.EINVAL
+    c = C(); c.flags = 8
     assert check(c) == _abi.EINVAL
     c = C(); c.dtype = 7
     assert check(c) == _abi.EINVAL
@@ -165,6 +169,53 @@ def test_split_heuristics_and_workspace_sizes():
     assert _abi.decode_splits(_cfg(num_q_heads=32, num_kv_heads=1), 96, 600) == 6
     assert _abi.decode_splits(_cfg(num_q_heads=16, num_kv_heads=1), 96, 300) == 6
     assert _abi.decode_splits(_cfg(num_q_heads=16, num_kv_heads=1), 96, 100) == 3   # 6 capped at 100 / 32
+
+
+def test_keys_once_route_and_its_workspace():
+    """The RoPE prefill turns the keys once when a request spans >= 8 query tiles of 256 rows
+    (or when asked to); its workspace then holds the turned keys after the partials."""
+    turned = lambda R, E, hkv: R * E * hkv * 16 * 128 * 2
+    c70 = _cfg(num_q_heads=64, num_kv_heads=8)
+    # the 70B chunk: 2048 positions x 8 heads = 64 query tiles per (request, KV head), 1 split
+    assert _abi.prefill_splits(c70, 4, 2048, 2176) == 1
+    assert _abi.prefill_workspace_size(c70, 4, 8192, 2048, 2176) == turned(4, 2176, 8)
+    # 8 tiles (256 positions x 8 heads) turn once, 7 do not
+    assert _abi.prefill_workspace_size(c70, 4, 1024, 256, 100, 1) == turned(4, 100, 8)
+    assert _abi.prefill_workspace_size(c70, 4, 1024, 224, 100, 1) == 0
+    # split partials first, the turned keys from the next 256-byte boundary
+    part = 3 * 5 * 64 * (128 * 2 + 8)
+    assert _abi.prefill_workspace_size(c70, 1, 5, 256, 300, 3) == (part + 255) // 256 * 256 + turned(1, 300, 8)
+    # the flags force either route; other encodings, FP8 pools and f32 never turn once
+    fused = _abi.make_config(64, 8, 128, pe="rope", rope_theta=5e5, keys="fused")
+    once = _abi.make_config(64, 8, 128, pe="rope", rope_theta=5e5, keys="once")
+    assert _abi.prefill_workspace_size(fused, 4, 8192, 2048, 2176) == 0
+    assert _abi.prefill_workspace_size(once, 2, 10, 5, 7, 1) == turned(2, 7, 8)
+    for kw in (dict(pe="none"), dict(pe="alibi"), dict(kv_format="fp8")):
+        c = _abi.make_config(64, 8, 128, rope_theta=5e5, keys="once", **kw)
+        assert _abi.prefill_workspace_size(c, 2, 10, 5, 7, 1) == 0
+    # MQA (G = 32): 8 positions per tile, so 64 positions make 8 tiles
+    cm = _cfg(num_q_heads=32, num_kv_heads=1)
+    assert _abi.prefill_workspace_size(cm, 2, 128, 64, 40, 1) == turned(2, 40, 1)
+    assert _abi.prefill_workspace_size(cm, 2, 112, 56, 40, 1) == 0
+    # both flags at once is no valid config
+    both = _abi.make_config(64, 8, 128, rope_theta=5e5)
+    both.flags = _abi.FLAG_KEYS_FUSED | _abi.FLAG_KEYS_ONCE
+    assert _abi.lib().lazyattn_prefill_splits(ctypes.byref(both), 1, 1, 1) == 0
+    assert _abi.prefill_workspace_size(both, 1, 1, 1, 1) == 0
+    bad = _abi.make_config(64, 8, 128, rope_theta=5e5)
+    bad.flags = 8
+    assert _abi.lib().lazyattn_prefill_splits(ctypes.byref(bad), 1, 1, 1) == 0
+    # a call on the turned route checks that the workspace holds the turned keys
+    lib = _abi.lib()
+    b = _abi.Batch()
+    b.num_reqs, b.max_entries = 2, 4
+    b.block_tables = b.num_entries = b.ctx_lens = 16   # never dereferenced on the host
+    P = ctypes.c_void_p(64)
+    need = turned(2, 4, 8)
+    assert lib.lazyattn_prefill(ctypes.byref(once), P, P, 2, 1, P, P, 1, ctypes.byref(b), 1, P, P, need - 1,
+                                None) == _abi.EWORKSPACE
+    assert lib.lazyattn_prefill_attend(ctypes.byref(once), P, P, 2, 1, P, P, 1, ctypes.byref(b), 1, P, None, 0,
+                                       None) == _abi.EWORKSPACE
 
 
 def test_gpu_entry_points_reject_bad_arguments_before_launch():

@@ -43,9 +43,9 @@ def sync():
 # ---------------------------------------------------------------------------
 # helpers running one phase on both sides
 # ---------------------------------------------------------------------------
-def run_prefill(wl, num_splits=0, pe=None, block_permutation=None, pools=None, exact_max=False, pb=None):
+def run_prefill(wl, num_splits=0, pe=None, block_permutation=None, pools=None, exact_max=False, pb=None, keys=None):
     s = wl.spec
-    cfg = staging.config_for(s, pe=pe, exact_max=exact_max)
+    cfg = staging.config_for(s, pe=pe, exact_max=exact_max, keys=keys)
     if pb is None:
         pb = wl.prefill_batch()
     if pools is None:
@@ -64,8 +64,10 @@ def sample_tokens(q_len, k, rng):
     return np.array(sorted(pick))
 
 
-def compare_prefill(wl, pb, got, orc, requests=None, token_subset=None, pe=None, label=""):
-    ref = orc.prefill(pb, token_subset=token_subset, requests=requests, pe=pe)
+def compare_prefill(wl, pb, got, orc, requests=None, token_subset=None, pe=None, label="", ref=None):
+    """ref: the oracle's rows from an earlier call with the same arguments (else computed here)."""
+    if ref is None:
+        ref = orc.prefill(pb, token_subset=token_subset, requests=requests, pe=pe)
     cu = pb["cu_q_lens"]
     gs, rs = [], []
     for r, o in ref.items():
@@ -75,7 +77,7 @@ def compare_prefill(wl, pb, got, orc, requests=None, token_subset=None, pe=None,
     g, rr = np.concatenate(gs), np.concatenate(rs)
     mx, mn = assert_parity(g, rr, wl.spec.dtype, label)
     say(f"{label}: max {mx:.2e} mean {mn:.2e} over {g.shape[0]} tokens")
-    return g, rr
+    return g, ref
 
 
 # ---------------------------------------------------------------------------
@@ -238,7 +240,14 @@ def test_parity_llama70b_all_requests_as_benched():
     subset = {0: np.array(sorted(set([0, 1, 31, 32, 33, 1023, 1024, 2046, 2047]) |
                                  set(rng.choice(2048, 6, replace=False).tolist())))}
     subset.update({r: sample_tokens(2048, 6, rng) for r in range(1, 4)})
-    compare_prefill(wl, pb, got, orc, token_subset=subset, label="70B chunk prefill, 4 requests")
+    assert _abi.prefill_workspace_size(cfg, 4, int(pb["total_q"]), int(pb["max_q_len"]), 1, 1) > 0   # keys turned once
+    _, ref = compare_prefill(wl, pb, got, orc, token_subset=subset, label="70B chunk prefill, 4 requests")
+    fused = run_prefill(wl, pools=pools, pb=pb, keys="fused")[1]
+    compare_prefill(wl, pb, fused, orc, token_subset=subset, ref=ref,
+                    label="70B chunk prefill, 4 requests, keys turned in the attention kernel")
+    mx, mn = diff_stats(got, fused)
+    say(f"70B chunk: keys turned once vs in the kernel, every row: max {mx:.2e} mean {mn:.2e}")
+    assert mx <= 2e-2 and mn <= 1e-3
     d0 = wl.decode_step(0)
     staging.append_tokens(cfg, pools, d0, s.dtype, DEV)
     orc.append(d0)
@@ -373,7 +382,11 @@ def test_parity_mqa_stress(skew, pe):
     orc.append(pb)
     rng = np.random.default_rng(1)
     subset = {r: sample_tokens(128, 10, rng) for r in range(len(pb["ctx_lens"]))}
-    compare_prefill(wl, pb, got, orc, token_subset=subset, label=f"MQA prefill {skew}/{pe}")
+    _, ref = compare_prefill(wl, pb, got, orc, token_subset=subset, label=f"MQA prefill {skew}/{pe}")
+    if pe == "rope":   # 16 query tiles per request: the keys were turned once; the fused route too
+        fused = run_prefill(wl, pools=pools, pb=pb, keys="fused")[1]
+        compare_prefill(wl, pb, fused, orc, token_subset=subset, ref=ref,
+                        label=f"MQA prefill {skew}/{pe}, keys turned in the attention kernel")
     for step in range(8):
         d = wl.decode_step(step)
         staging.append_tokens(cfg, pools, d, s.dtype, DEV)
@@ -399,11 +412,13 @@ def test_physical_relocation_is_bit_identical():
     assert np.array_equal(a, b)
 
 
-def test_pool_is_read_only_and_padding_poison_stays_out():
-    say("pools unchanged by prefill and decode; outputs finite despite NaN padding")
+@pytest.mark.parametrize("keys", [None, "fused"])
+def test_pool_is_read_only_and_padding_poison_stays_out(keys):
+    say(f"pools unchanged by prefill (keys {keys or 'turned once: the default here'}) and decode; "
+        "outputs finite despite NaN padding")
     wl = W.build_workload(W.spec(5, requests=[6, 6], skew=1.6))
     s = wl.spec
-    cfg = staging.config_for(s)
+    cfg = staging.config_for(s, keys=keys)
     pools = staging.DevicePools(wl, DEV)
     pb = wl.prefill_batch()
     staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
@@ -454,6 +469,71 @@ def test_prefill_split_count_invariance_and_empty_splits():
     for o in outs[1:]:
         mx, mn = diff_stats(o, outs[0])
         assert mx <= 4e-3 and mn <= 2e-4
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_prefill_keys_once_llama8b_full(num_splits):
+    say("8B prefill full, keys turned once first (forced), splits", num_splits)
+    wl = W.build_workload(W.spec(2))
+    pb, got, pools = run_prefill(wl, num_splits=num_splits, keys="once")
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label=f"8B prefill, keys once, splits={num_splits}")
+    fused = run_prefill(wl, num_splits=num_splits, pools=pools, pb=pb, keys="fused")[1]
+    mx, mn = diff_stats(got, fused)
+    say(f"keys once vs fused: max {mx:.2e} mean {mn:.2e}")
+    assert mx <= 2e-2 and mn <= 1e-3
+
+
+def test_prefill_keys_once_ragged_edges_and_workspace_reuse():
+    say("keys turned once: ragged query tiles, long chunk over few documents, requests without documents, "
+        "a zero-length request, one workspace reused by a smaller call")
+    # 300 positions x 4 heads = 4.7 query tiles; 3 splits over 1..3 documents
+    wl = W.build_workload(W.spec(2, requests=[5], q_len=300, docs=(1, 3)))
+    pb, got, pools = run_prefill(wl, num_splits=3, keys="once")
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="ragged 300-token chunks, keys once, 3 splits")
+    # no documents: each context is the chunk itself; chunks of 1 and 40 tokens
+    for q_len in (1, 40):
+        wl1 = W.build_workload(W.spec(2, requests=[3], docs=(0, 0), q_len=q_len))
+        pb1, got1, _ = run_prefill(wl1, keys="once")
+        orc1 = OracleState(wl1)
+        orc1.append(pb1)
+        compare_prefill(wl1, pb1, got1, orc1, label=f"{q_len}-token contexts without documents, keys once")
+    # a request with no new tokens in the middle of the batch
+    s = wl.spec
+    cfg = staging.config_for(s, keys="once")
+    ins = dict(pb)
+    cu = pb["cu_q_lens"]
+    ins["cu_q_lens"] = np.array([0, 300, 300, 600, 900, 1200], dtype=np.int32)
+    keep = np.r_[cu[0]:cu[1], cu[2]:cu[5]]
+    ins["q"] = pb["q"][keep]
+    ins["total_q"] = 1200
+    ctx = pb["ctx_lens"].copy()
+    ctx[1] -= 300
+    ins["ctx_lens"] = ctx
+    ne = pb["num_entries"].copy()
+    ne[1] = wl.requests[1].n_doc_entries
+    ins["num_entries"] = ne
+    call = staging.PrefillCall(cfg, s, ins, DEV, 2)
+    out = gpu_f64(call.run(pools))
+    ref = orc.prefill(pb)
+    for r, rows in ((0, slice(0, 300)), (2, slice(300, 600)), (4, slice(900, 1200))):
+        assert_parity(out[rows], ref[r], "bf16", f"zero-length request: request {r}")
+    # the same workspace, dirty from the call above, serves a smaller batch
+    small = W.build_workload(W.spec(2, requests=[2], q_len=70, docs=(1, 1)))
+    spb = small.prefill_batch()
+    spools = staging.DevicePools(small, DEV)
+    staging.append_tokens(cfg, spools, spb, s.dtype, DEV)
+    scall = staging.PrefillCall(cfg, s, spb, DEV, 2)
+    need = scall.workspace.numel()
+    assert need <= call.workspace.numel()
+    scall.workspace = call.workspace
+    sout = gpu_f64(scall.run(spools))
+    sorc = OracleState(small)
+    sorc.append(spb)
+    compare_prefill(small, spb, sout, sorc, label="smaller call in a reused workspace, keys once")
 
 
 def test_prefill_request_order_is_bit_identical():
