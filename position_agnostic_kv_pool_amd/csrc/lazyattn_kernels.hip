@@ -181,7 +181,9 @@ __device__ __forceinline__ f32x4 mfma16x16x16(const s16x4& a, const s16x4& b, co
 // tile: lane l loads channel pair l of those 8 key rows (4 B each) and
 // 2 x 16 B of V one iteration ahead, rotates the keys by R(t - p0) (phase
 // R(start - p0 + row) stepped by R(1) per row) between the QK products, and
-// writes K~ and V into the other LDS buffer.  One barrier per tile.  Table words are fetched three tiles ahead
+// writes K~ and V into the other LDS buffer (keys that need no per-row work,
+// in the rotation-free, ALiBi and keys-turned-once kernels, move as two 16-byte
+// pieces of 4 rows per lane instead).  One barrier per tile.  Table words are fetched three tiles ahead
 // and decoded per wave with lane reads.  With the key range split, each
 // split writes its output divided by its own row sum, as IEEE half (so split
 // calls need |V| <= 65504), and fp32 (m, l); the merge kernel combines them.
@@ -397,7 +399,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   };
 
   // ---- staging: wave w handles rows 8 part .. 8 part + 7 of entry E = w / 2 --------
-  // K: lane l holds channel pair l of the 8 key rows (4 B each); V: lane l holds
+  // K: lane l holds channel pair l of the 8 key rows (4 B each; with early
+  // staging, 8 channels of rows l / 16 and l / 16 + 4 instead); V: lane l holds
   // keys 8 (l % 2) .. + 7 of channels 64 part + 32 cc + l / 2, cc = 0, 1
   const int E_own = ws >> 1, part = ws & 1;
   // this lane's channel-pair frequency (turns per position), read once
@@ -436,9 +439,21 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
 #pragma unroll
       for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
       kx = *reinterpret_cast<const uint2*>(kc + 16 * kPD + 8 * part);
-    } else {
+    } else if (kStageEarly) {
+      // no per-row work on these keys: two 16-byte loads, rows 8 part + 4 i + lane / 16
+      // (i = 0, 1), channels 8 (lane % 16) .. + 7, into kr[4 i .. 4 i + 3]
       const uint16_t* ksrc = kTurned ? A.kturned : A.kpool;
-      const uint32_t* kp = reinterpret_cast<const uint32_t*>(ksrc + base * (kBlock * kPD) + 8 * part * kPD) + lane;
+      const uint16_t* kp = ksrc + base * (kBlock * kPD) + (8 * part + (lane >> 4)) * kPD + 8 * (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kp + 4 * i * kPD);
+        kr[4 * i] = v.x;
+        kr[4 * i + 1] = v.y;
+        kr[4 * i + 2] = v.z;
+        kr[4 * i + 3] = v.w;
+      }
+    } else {
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(A.kpool + base * (kBlock * kPD) + 8 * part * kPD) + lane;
 #pragma unroll
       for (int k = 0; k < 8; ++k) kr[k] = kp[k * (kPD / 2)];
     }
@@ -502,9 +517,16 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   };
   // write the staged K~ and V into LDS buffer b
   auto stage_write_k = [&](int b) {
-    uint32_t* kdst = reinterpret_cast<uint32_t*>(Ks[b]) + lane;
+    if constexpr (kStageEarly) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) kdst[krow_of(E_own, 8 * part + k) * (kKS / 2)] = kr[k];
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<uint4*>(&Ks[b][krow_of(E_own, 8 * part + 4 * i + (lane >> 4)) * kKS + 8 * (lane & 15)]) =
+            make_uint4(kr[4 * i], kr[4 * i + 1], kr[4 * i + 2], kr[4 * i + 3]);
+    } else {
+      uint32_t* kdst = reinterpret_cast<uint32_t*>(Ks[b]) + lane;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) kdst[krow_of(E_own, 8 * part + k) * (kKS / 2)] = kr[k];
+    }
   };
   auto stage_write_v = [&](int b) {
     uint16_t* vdst = Vs[b] + E_own * kVEs + (lane & 1) * kVH;
