@@ -241,9 +241,9 @@ int32_t lazyattn_decode_splits(const lazyattn_config* cfg, int32_t num_reqs, int
  * finite); with S = 1 the output is written as bf16 directly and no such limit
  * applies.  A prefill call that turns the keys once (LAZYATTN_FLAG_KEYS_ONCE,
  * or the library's choice without a flag) also holds the turned keys there,
- * after the partials rounded up to 256 bytes: num_reqs * max_entries blocks
- * in the pool's K layout ([Hkv][16][D] bf16 each, entry e of request r at
- * block r * max_entries + e), num_reqs * max_entries * Hkv * 4096 bytes; the
+ * after the partials rounded up to 256 bytes: bf16 [num_reqs][Hkv][max_entries]
+ * chunks of [16][D] (request r's entry e for KV head h at chunk
+ * (r * Hkv + h) * max_entries + e), num_reqs * max_entries * Hkv * 4096 bytes; the
  * size counts them whenever the route would be taken for these sizes (a framed
  * batch, which does not take it, needs less).  The workspace needs no
  * initialisation; calls that may run concurrently must not share one. */

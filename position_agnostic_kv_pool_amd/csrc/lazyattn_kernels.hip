@@ -226,9 +226,10 @@ struct PrefillArgs {
   uint16_t* out;
   uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
   float* ml_part;                // and (m, l) [splits][rows][Hq][2]
-  const uint16_t* kturned;       // keys turned once (kPeKeysTurned): block r * max_entries + e = entry e of request r
+  const uint16_t* kturned;       // keys turned once (kPeKeysTurned): [R][Hkv][max_entries][16][D]
   int32_t Hq, Hkv, G, max_entries, total_q, m_q, eps, splits;
   int32_t n_qt;                  // query tiles per request (the grid's x extent is n_qt * splits)
+  int32_t xcd_units;             // nonzero: the query tiles of one (split, request, KV head) all run on one XCD
   int32_t exact;                 // nonzero: always take the two-pass exact-maximum route
   float scale_log2;
   RopeRev rope;
@@ -271,9 +272,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   const int c = lane & 31, h = lane >> 5;
   // grid (query tile and split, request, KV head), the query tile fastest: the
   // work-groups of one request follow each other, in the given request order
-  const int qt = blockIdx.x % A.n_qt, split = blockIdx.x / A.n_qt;
-  const int kvh = blockIdx.z;
+  int qt = blockIdx.x % A.n_qt, split = blockIdx.x / A.n_qt;
+  int kvh = blockIdx.z;
   int r = blockIdx.y;
+  if (A.xcd_units) {
+    // work-group L of the dispatch order runs on XCD L % 8: give XCD x the units
+    // (split, request, KV head) u = x, x + 8, ... with all query tiles of each,
+    // so that those tiles, which read the same keys, share one L2 (the host sets
+    // this only when the number of units is a multiple of 8)
+    const int L = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int k = L >> 3;
+    const int u = (L & 7) + 8 * (k / A.n_qt);
+    qt = k % A.n_qt;
+    split = u % A.splits;
+    r = (u / A.splits) % static_cast<int>(gridDim.y);
+    kvh = u / (A.splits * static_cast<int>(gridDim.y));
+  }
   if (A.order) {
     const int o = A.order[r];
     r = (o >= 0 && o < static_cast<int>(gridDim.y)) ? o : r;
@@ -380,14 +394,14 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     st = valid ? s0 : L;
     ln = valid ? s1 - s0 : 0;
   };
-  // where the keys of entry x of tile j are read: the pool block, or (keys
-  // turned once) the request's own turned copy of the entry, the split's first
-  // entry standing in past the split's end
-  auto k_index = [&](int j, int x, int blk) -> uint32_t {
-    if constexpr (!kTurned) return static_cast<uint32_t>(blk);
+  // where the keys of entry x of tile j are read, in 4 KiB (16 x D) chunks: the
+  // pool's (block, KV head) chunk, or (keys turned once) the request's own
+  // turned copy of the entry for this KV head, the split's first entry
+  // standing in past the split's end
+  auto k_index = [&](int j, int x, int blk) -> size_t {
+    if constexpr (!kTurned) return static_cast<size_t>(static_cast<uint32_t>(blk)) * Hkv + kvh;
     const int e = tile_e0(j) + x;
-    return static_cast<uint32_t>(r) * static_cast<uint32_t>(A.max_entries) +
-           static_cast<uint32_t>(e < e_stop ? e : e_begin);
+    return (static_cast<size_t>(r) * Hkv + kvh) * A.max_entries + static_cast<size_t>(e < e_stop ? e : e_begin);
   };
 
   // frame starts (framed pool): lanes x = 0..3 (mod 8) hold entry e0 + x of a tile
@@ -431,8 +445,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   uint2 kx = make_uint2(0, 0), vx = make_uint2(0, 0);
   // entries past the split's end (length 0) read block 0: their keys are
   // masked out of the scores and their V rows zeroed when staged
-  auto load_k = [&](uint32_t kb) {
-    const size_t base = static_cast<size_t>(kb) * Hkv + kvh;
+  auto load_k = [&](size_t base) {
     if (KV8) {
       const uint8_t* kc = reinterpret_cast<const uint8_t*>(A.kpool) + base * kChunk8;
       const uint16_t* kp = reinterpret_cast<const uint16_t*>(kc + 8 * part * kPD) + lane;
@@ -475,7 +488,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
       for (int cc = 0; cc < 2; ++cc) vr[cc] = *reinterpret_cast<const uint4*>(vp + 32 * cc * kBlock);
     }
   };
-  auto load_kv = [&](uint32_t kb, int blk) {
+  auto load_kv = [&](size_t kb, int blk) {
     load_k(kb);
     load_v(blk);
   };
@@ -603,7 +616,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
     {
       int blk, st, ln;
       entry_of(wv0, 0, E_own, blk, st, ln);
-      const uint32_t kb0 = k_index(0, E_own, blk);
+      const size_t kb0 = k_index(0, E_own, blk);
       int fv0 = 0;
       if (PE == kPeFramed) {
         fv0 = load_frames(0);
@@ -1592,8 +1605,9 @@ __global__ __launch_bounds__(256) void materialize_kernel(const uint16_t* kpool,
 // Keys turned once for the prefill (LAZYATTN_FLAG_KEYS_ONCE).  Wave w of
 // work-group (x, r) takes entry e = 4 x + w of request r and writes every KV
 // head's 16 key rows, each turned by R(t - c) (t its position, c = the
-// request's first new position), to block r * max_entries + e of `out`, in
-// the pool's K layout.  Lane l moves 16 bytes of rows l / 16 + 4 i
+// request's first new position), to out[r][kvh][e] ([R][Hkv][max_entries]
+// chunks of 16 x D: one request and KV head's keys are contiguous, in table
+// order, as the attention kernel's work-groups read them).  Lane l moves 16 bytes of rows l / 16 + 4 i
 // (i = 0..3), channels 8 (l % 16) .. + 7, i.e. four channel pairs: its 16
 // phases are formed once per entry (angle reduced in double) and serve every
 // head.  Rows past the entry's length are turned too; the attention kernel
@@ -1617,7 +1631,7 @@ __global__ __launch_bounds__(256) void turn_keys_kernel(const uint16_t* kpool, c
     for (int q = 0; q < 4; ++q) ph[i][q] = unit_phase_turns(n0 + 4 * i, rope.rev[j0 + q]);
   const int off = (lane >> 4) * kPD + 8 * (lane & 15);
   const uint16_t* src = kpool + static_cast<size_t>(word_block(w)) * Hkv * (kBlock * kPD) + off;
-  uint16_t* dst = out + (static_cast<size_t>(r) * max_entries + e) * Hkv * (kBlock * kPD) + off;
+  uint16_t* dst = out + (static_cast<size_t>(r) * Hkv * max_entries + e) * (kBlock * kPD) + off;
 #pragma unroll 2
   for (int kvh = 0; kvh < Hkv; ++kvh) {
     uint4 v[4];
@@ -1627,7 +1641,7 @@ __global__ __launch_bounds__(256) void turn_keys_kernel(const uint16_t* kpool, c
     for (int i = 0; i < 4; ++i) {
       const uint4 t = make_uint4(rotate_pair(v[i].x, ph[i][0]), rotate_pair(v[i].y, ph[i][1]),
                                  rotate_pair(v[i].z, ph[i][2]), rotate_pair(v[i].w, ph[i][3]));
-      *reinterpret_cast<uint4*>(dst + kvh * (kBlock * kPD) + 4 * i * kPD) = t;
+      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(kvh) * max_entries * (kBlock * kPD) + 4 * i * kPD) = t;
     }
   }
 }
@@ -1950,6 +1964,7 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
                      : nullptr,
                 Hq, Hkv, G, batch->max_entries, total_q, m_q,
                 prefill_entries_per_split(batch->max_entries, splits), splits, static_cast<int32_t>(n_qt),
+                (n_qt >= 32 && (static_cast<long long>(splits) * R * Hkv) % 8 == 0) ? 1 : 0,
                 (cfg->flags & LAZYATTN_FLAG_EXACT_MAX) ? 1 : 0, scale * kLog2e, rope};
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(Hkv));
   const dim3 block(kPrefillThreads);

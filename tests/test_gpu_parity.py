@@ -536,6 +536,25 @@ def test_prefill_keys_once_ragged_edges_and_workspace_reuse():
     compare_prefill(small, spb, sout, sorc, label="smaller call in a reused workspace, keys once")
 
 
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_prefill_long_chunk_tiles_grouped_per_xcd(num_splits):
+    # a 2048-token chunk of the 8B shape spans 32 query tiles per (request, KV head) and the
+    # (split, request, KV head) units are a multiple of 8: every unit's tiles then run on one XCD
+    say(f"8B shape, 2048-token chunks over one document, {num_splits} splits: tiles grouped per XCD, "
+        "keys turned once / in the kernel / rotation-free")
+    wl = W.build_workload(W.spec(2, requests=[2], q_len=2048, docs=(1, 1)))
+    pb = wl.prefill_batch()
+    orc = OracleState(wl)
+    orc.append(pb)
+    rng = np.random.default_rng(11)
+    subset = {r: sample_tokens(2048, 12, rng) for r in range(2)}
+    pools = None
+    for pe, keys in (("rope", None), ("rope", "fused"), ("none", None)):
+        _, got, pools = run_prefill(wl, num_splits=num_splits, pe=pe, keys=keys, pools=pools, pb=pb)
+        compare_prefill(wl, pb, got, orc, token_subset=subset, pe=pe,
+                        label=f"2048-token chunks, splits={num_splits}, pe={pe}, keys={keys or 'auto'}")
+
+
 def test_prefill_request_order_is_bit_identical():
     say("prefill: requests taken longest first, reversed, in batch order, or through an out-of-range entry agree bit for bit")
     wl = W.build_workload(W.spec(5, skew=0.0, requests=[12, 1]))
