@@ -159,11 +159,12 @@ typedef struct {
   const int32_t* ctx_lens;         /* device [R] context length L_r, this call's new tokens included */
   const int32_t* frame_starts;     /* device [R][max_entries] or NULL (content-only pool) */
   const int32_t* req_order;        /* device [R], a permutation of 0..R-1, or NULL (batch order):
-                                      the order in which prefill work-groups take the requests.
-                                      Results do not depend on it; longest context first shortens
-                                      the tail of a batch of unequal requests.  An entry outside
-                                      0..R-1 stands for its own index; a list that is no
-                                      permutation leaves some rows unwritten.  Decode ignores it. */
+                                      the order in which prefill and decode work-groups take the
+                                      requests.  Results do not depend on it; longest context
+                                      first shortens the tail of a batch of unequal requests.  An
+                                      entry outside 0..R-1 stands for its own index; a list that is
+                                      no permutation leaves some rows unwritten.  The shared-run
+                                      decode ignores it. */
 } lazyattn_batch;
 
 /* ---- host-only helpers (no GPU needed) ---------------------------------- */

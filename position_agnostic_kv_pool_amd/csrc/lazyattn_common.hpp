@@ -50,7 +50,8 @@ size_t prefill_partials_bytes(const lazyattn_config* cfg, int total_q, int split
 size_t prefill_turned_keys_offset(size_t partials_bytes);
 size_t prefill_turned_keys_bytes(const lazyattn_config* cfg, int num_reqs, int max_entries);
 int decode_entries_per_split(int max_entries, int splits);
-// decode work-groups per (request, KV head, split): 2 for groups of more than 16 heads
+// decode work per (request, KV head, split) in 16-head work-groups: 2 for groups
+// of more than 16 heads
 int decode_halves(int group);
 
 }  // namespace lazyattn

@@ -106,6 +106,9 @@ size_t prefill_turned_keys_bytes(const lazyattn_config* cfg, int num_reqs, int m
          cfg->head_dim * sizeof(uint16_t);
 }
 
+// Decode work per (request, KV head, split) in units of one 16-head work-group:
+// groups of 17..32 heads take two (two work-groups of 16 heads, or one whose
+// waves hold 32 columns and do twice the work per entry)
 int decode_halves(int group) { return group > 16 ? 2 : 1; }
 
 int choose_decode_splits(const lazyattn_config* cfg, int num_reqs, int max_entries) {

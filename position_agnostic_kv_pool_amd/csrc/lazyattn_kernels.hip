@@ -1006,6 +1006,7 @@ struct DecodeArgs {
   const int32_t* n_ent;
   const int32_t* ctx;
   const int32_t* frames;         // [R][max_entries] frame starts (document-local frames) or NULL
+  const int32_t* order;          // [R] the order in which work-groups take the requests, or NULL
   const float* alibi;
   uint16_t* out;
   uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
@@ -1028,12 +1029,13 @@ static_assert(4 * kTab * 4 <= 4 * 16 * kOS * 4, "the staged table fits the wave-
 constexpr float kRescaleSlack = 8.0f;   // reference raised only when a score exceeds it by 2^8
 
 template <int PE, int NT, int KV8, int RUNS>
-__global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const DecodeArgs A) {
+__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(const DecodeArgs A) {
   extern __shared__ __attribute__((aligned(16))) float dsm[];
   float2* bsh = reinterpret_cast<float2*>(dsm);             // [4 waves][kRing][64]
   float* ml_s = dsm + 4 * kRing * 64 * 2;                     // [4][NT*16][2]
-  float* o_s = ml_s + 4 * NT * 16 * 2;                        // [4][Gw][kOS] (NT * 16 rows reserved)
-  float2* rtab = reinterpret_cast<float2*>(o_s + 4 * NT * 16 * kOS);  // [16][64] R(n), RoPE only
+  float* o_s = ml_s + 4 * NT * 16 * 2;                        // [4][16][kOS]: one 16-column tile at a time
+  float2* rtab = reinterpret_cast<float2*>(o_s + 4 * 16 * kOS);  // [16][64] R(n), RoPE only
+  uint4* qs = reinterpret_cast<uint4*>(rtab + 16 * 64);          // [NT][4][64] query fragments (NT > 1)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
@@ -1072,6 +1074,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
     const int rest = item / A.splits;
     kvh = rest % Hkv;
     r = rest / Hkv;
+  }
+  if (!runs && A.order) {
+    // the requests in the given order (an entry outside 0..R-1 stands for its own index)
+    const int o = A.order[r];
+    r = (o >= 0 && o < A.R) ? o : r;
   }
   const int hb = 16 * half;                          // first head column of this work-group
   // its head columns; a shared-run item's columns are (occurrence, head) pairs
@@ -1144,6 +1151,17 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       qb[nt][s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
     }
   }
+  // Two head tiles (NT > 1): the query fragments, the same for every wave, go to
+  // LDS and are read back at each entry instead of holding 32 registers
+  if (NT > 1) {
+    if (wave == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qs[(nt * 4 + s) * 64 + lane] = __builtin_bit_cast(uint4, qb[nt][s]);
+    }
+    __syncthreads();
+  }
   // R(n) of lane (g, n)'s key row n at pair 16g + i, as rtab[i][lane] (a lane's
   // 16 reads of one entry are then 64 consecutive float2 each); this lane's
   // pair for R(S - p)
@@ -1160,9 +1178,11 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   if (PE == LAZYATTN_PE_ROPE || PE == kPeFramed) my_rev = A.rope.rev[lane];
   // This lane's R(n) at its 16 pairs, held in registers: reading them from LDS
   // at each entry put an LDS round trip on every entry's path (the empty asm
-  // keeps the compiler from turning the copies back into LDS reads at the uses)
+  // keeps the compiler from turning the copies back into LDS reads at the uses).
+  // A wave of two head tiles (NT = 2) has no registers to spare for them and
+  // reads them from LDS; its rotation serves twice the heads.
   float2 rn[16];
-  if (PE == LAZYATTN_PE_ROPE) {
+  if (PE == LAZYATTN_PE_ROPE && NT == 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       rn[i] = rtab[i * 64 + lane];
@@ -1331,6 +1351,10 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       if (PE == LAZYATTN_PE_ROPE) {
         // R(S - p) at pair l, written by lane l when the slot was loaded
         const float2* bw = bsh + (wave * kRing + sl) * 64;
+        // two head tiles: R(n) read from LDS at each entry (an opaque lane index
+        // keeps the compiler from hoisting the reads into 32 live registers)
+        int rl = lane;
+        if (NT > 1) asm volatile("" : "+v"(rl));
         if (KV8) {
           // the lane's 32 codes are in k[0..1]
   #pragma unroll
@@ -1341,7 +1365,8 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
   #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               // pair 16g + 4s + jj
-              w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0, cmul(bw[c0(s) / 2 + jj], rn[4 * s + jj]));
+              w4[jj] = rotate_fp8_pair(jj < 2 ? c_lo : c_hi, (jj & 1) != 0,
+                                       cmul(bw[c0(s) / 2 + jj], NT == 1 ? rn[4 * s + jj] : rtab[(4 * s + jj) * 64 + rl]));
             }
             ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
           }
@@ -1351,9 +1376,12 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
             uint32_t w4[4] = {k[s].x, k[s].y, k[s].z, k[s].w};
   #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-              w4[jj] = rotate_pair(w4[jj], cmul(bw[c0(s) / 2 + jj], rn[4 * s + jj]));   // pair 16s + 4g + jj
+              w4[jj] = rotate_pair(w4[jj], cmul(bw[c0(s) / 2 + jj],
+                                                NT == 1 ? rn[4 * s + jj] : rtab[(4 * s + jj) * 64 + rl]));   // pair 16s + 4g + jj
             }
             ka[s] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+            // two head tiles: one contraction step's phases at a time (registers)
+            if (NT > 1) __builtin_amdgcn_sched_barrier(0);
           }
         }
       } else {
@@ -1378,9 +1406,15 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       for (int nt = 0; nt < NT; ++nt) {
         // scores relative to the reference: the chain starts from -m (FP8: the
         // row's scale multiplies the product first)
-        f32x4 S = KV8 ? f32x4{0.f, 0.f, 0.f, 0.f} : negm[nt];
+        f32x4 S = KV8 ? f32x4{0.f, 0.f, 0.f, 0.f}
+                      : (NT == 1 ? negm[nt] : f32x4{-m_use[nt], -m_use[nt], -m_use[nt], -m_use[nt]});
+        // (two head tiles: the query fragments from LDS, through an opaque lane index
+        // that keeps the compiler from hoisting them back into registers)
+        int ql = lane;
+        if (NT > 1) asm volatile("" : "+v"(ql));
   #pragma unroll
-        for (int s = 0; s < 4; ++s) S = mfma16x16x32(ka[s], qb[nt][s], S);
+        for (int s = 0; s < 4; ++s)
+          S = mfma16x16x32(ka[s], NT == 1 ? qb[nt][s] : __builtin_bit_cast(bf16x8, qs[(nt * 4 + s) * 64 + ql]), S);
         if (KV8) {
   #pragma unroll
           for (int j = 0; j < 4; ++j) S[j] = fmaf(S[j], exp_scale(kexp, j), negm[nt][j]);
@@ -1412,7 +1446,7 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
           l_run[nt] *= alpha;
           m_run[nt] = m_new;
           m_use[nt] = mu_new;
-          negm[nt] = f32x4{-mu_new, -mu_new, -mu_new, -mu_new};
+          if (NT == 1) negm[nt] = f32x4{-mu_new, -mu_new, -mu_new, -mu_new};
         }
         float pe[4];
   #pragma unroll
@@ -1530,41 +1564,44 @@ __global__ __launch_bounds__(256, NT == 1 ? 2 : 1) void decode_bf16_kernel(const
       ml_s[(wave * NT * 16 + nt * 16 + n) * 2 + 1] = lt;
     }
   }
-  __syncthreads();
+  // one 16-column tile at a time through the [4][16][kOS] buffer
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    __syncthreads();
     const int col = nt * 16 + n;
-    if (col >= Gw) continue;
-    float M = kNegInf;
+    if (col < Gw) {
+      float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[(w * NT * 16 + col) * 2]);
-    const float f = (M == kNegInf || m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - M);
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[(w * NT * 16 + col) * 2]);
+      const float f = (M == kNegInf || m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - M);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<f32x4*>(o_s + (wave * Gw + col) * kOS + 16 * dt + 4 * g) = O[dt][nt] * f;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < Gw * kPD; idx += 256) {
-    const int col = idx / kPD, d = idx - col * kPD;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[(w * NT * 16 + col) * 2]);
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = ml_s[(w * NT * 16 + col) * 2];
-      if (M != kNegInf && mw != kNegInf) lsum += __builtin_amdgcn_exp2f(mw - M) * ml_s[(w * NT * 16 + col) * 2 + 1];
-      osum += o_s[(w * Gw + col) * kOS + d];
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(o_s + (wave * 16 + n) * kOS + 16 * dt + 4 * g) = O[dt][nt] * f;
     }
-    const int h = kvh * G + hb + col;
-    const size_t rowoff = static_cast<size_t>(r) * Hq + h;
-    if (A.splits == 1) {
-      const float val = lsum > 0.f ? osum / lsum : 0.f;
-      A.out[rowoff * kPD + d] = static_cast<uint16_t>(pack_bf16x2(val, 0.f) & 0xffffu);
-    } else {
-      const size_t prow = static_cast<size_t>(split) * A.R * Hq + rowoff;
-      A.o_part[prow * kPD + d] = static_cast<uint16_t>(pack_f16x2(lsum > 0.f ? osum / lsum : 0.f, 0.f) & 0xffffu);
-      if (d == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(M, lsum);
+    __syncthreads();
+    for (int idx = tid; idx < 16 * kPD; idx += 256) {
+      const int c16 = idx / kPD, d = idx - c16 * kPD, col2 = nt * 16 + c16;
+      if (col2 >= Gw) break;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_s[(w * NT * 16 + col2) * 2]);
+      float lsum = 0.f, osum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = ml_s[(w * NT * 16 + col2) * 2];
+        if (M != kNegInf && mw != kNegInf) lsum += __builtin_amdgcn_exp2f(mw - M) * ml_s[(w * NT * 16 + col2) * 2 + 1];
+        osum += o_s[(w * 16 + c16) * kOS + d];
+      }
+      const int h = kvh * G + hb + col2;
+      const size_t rowoff = static_cast<size_t>(r) * Hq + h;
+      if (A.splits == 1) {
+        const float val = lsum > 0.f ? osum / lsum : 0.f;
+        A.out[rowoff * kPD + d] = static_cast<uint16_t>(pack_bf16x2(val, 0.f) & 0xffffu);
+      } else {
+        const size_t prow = static_cast<size_t>(split) * A.R * Hq + rowoff;
+        A.o_part[prow * kPD + d] = static_cast<uint16_t>(pack_f16x2(lsum > 0.f ? osum / lsum : 0.f, 0.f) & 0xffffu);
+        if (d == 0) *reinterpret_cast<float2*>(A.ml_part + prow * 2) = make_float2(M, lsum);
+      }
     }
   }
 }
@@ -1889,7 +1926,8 @@ static lazyattn_status check_batch(const lazyattn_batch* b) {
 constexpr size_t kDecodeLdsFloor = 56 * 1024;
 
 static size_t decode_lds_bytes(int nt) {
-  const size_t need = (4 * kRing * 64 * 2 + 4 * nt * 16 * 2 + 4 * static_cast<size_t>(nt) * 16 * kOS + 16 * 64 * 2) *
+  const size_t need = (4 * kRing * 64 * 2 + 4 * static_cast<size_t>(nt) * 16 * 2 + 4 * 16 * kOS + 16 * 64 * 2 +
+                       (nt > 1 ? static_cast<size_t>(nt) * 4 * 64 * 4 : 0)) *
                       sizeof(float);
   return need > kDecodeLdsFloor ? need : kDecodeLdsFloor;
 }
@@ -2001,6 +2039,16 @@ static void launch_decode_one(dim3 grid, size_t lds, hipStream_t stream, const D
   hipLaunchKernelGGL((decode_bf16_kernel<PEV, NTV, KV8, RUNS>), grid, dim3(256), lds, stream, a);
 }
 
+// Groups of 17..32 heads over a plain bf16 content-only pool: one wave holds
+// all of them (two 16-column tiles), so every block is read and turned once
+static void launch_decode_wide(int pe_sel, dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
+  switch (pe_sel) {
+    case LAZYATTN_PE_ROPE: launch_decode_one<LAZYATTN_PE_ROPE, 2, 0, 0>(grid, lds, stream, a); break;
+    case LAZYATTN_PE_NONE: launch_decode_one<LAZYATTN_PE_NONE, 2, 0, 0>(grid, lds, stream, a); break;
+    default: launch_decode_one<LAZYATTN_PE_ALIBI, 2, 0, 0>(grid, lds, stream, a); break;
+  }
+}
+
 // RUNS: the shared-run decode (a content-only pool: no framed instantiation)
 template <int KV8, int RUNS>
 static void launch_decode(int pe_sel, dim3 grid, size_t lds, hipStream_t stream, const DecodeArgs& a) {
@@ -2050,18 +2098,24 @@ static lazyattn_status decode_attend(const lazyattn_config* cfg, const void* q, 
   float* ml_part = splits > 1 ? reinterpret_cast<float*>(o_part + static_cast<size_t>(splits) * R * Hq * kPD) : nullptr;
   DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                static_cast<const uint16_t*>(v_pool), batch->block_tables, batch->num_entries, batch->ctx_lens,
-               batch->frame_starts, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part, ml_part, R, Hq, Hkv, G,
-               batch->max_entries, decode_entries_per_split(batch->max_entries, splits), splits,
-               decode_halves(G), scale * kLog2e, rope};
+               batch->frame_starts, batch->req_order, cfg->alibi_slopes, static_cast<uint16_t*>(out), o_part,
+               ml_part, R, Hq, Hkv, G, batch->max_entries, decode_entries_per_split(batch->max_entries, splits),
+               splits, 1, scale * kLog2e, rope};
+  // groups of 17..32 heads: one wave of two head tiles (plain bf16 content-only
+  // pool), else two work-groups of 16 heads
+  const bool wide = G > 16 && !framed && cfg->kv_format == LAZYATTN_KV_PLAIN;
+  a.halves = (G > 16 && !wide) ? 2 : 1;
   dim3 grid(splits, Hkv, R);
   if (a.halves == 2) {
     const long long items = static_cast<long long>(splits) * Hkv * R;
     if ((items + 7) / 8 * 16 > 0x7fffffffLL) return LAZYATTN_EUNSUPPORTED;
     grid = dim3(static_cast<unsigned>((items + 7) / 8 * 16), 1, 1);
   }
-  const size_t lds = decode_lds_bytes(1);
+  const size_t lds = decode_lds_bytes(wide ? 2 : 1);
   const int pe_sel = framed ? kPeFramed : cfg->pe;
-  if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3)
+  if (wide)
+    launch_decode_wide(pe_sel, grid, lds, stream, a);
+  else if (cfg->kv_format == LAZYATTN_KV_FP8_E4M3)
     launch_decode<1, 0>(pe_sel, grid, lds, stream, a);
   else
     launch_decode<0, 0>(pe_sel, grid, lds, stream, a);
@@ -2166,7 +2220,8 @@ lazyattn_status lazyattn_decode_runs(const lazyattn_config* cfg, const void* q, 
     // pointers stand in for them all the same
     DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                  static_cast<const uint16_t*>(v_pool), reinterpret_cast<const uint64_t*>(plan->items),
-                 plan->req_ref_begin, plan->req_ref_begin, nullptr, cfg->alibi_slopes, static_cast<uint16_t*>(out),
+                 plan->req_ref_begin, plan->req_ref_begin, nullptr, nullptr, cfg->alibi_slopes,
+                 static_cast<uint16_t*>(out),
                  o_part, ml_part, num_reqs, Hq, Hkv, G, 1, 1, 1, 1, softmax_scale_of(cfg) * kLog2e,
                  make_rope_rev(cfg), plan->items, plan->words, plan->refs};
     const dim3 grid(static_cast<unsigned>(plan->num_items / 4), static_cast<unsigned>(Hkv));

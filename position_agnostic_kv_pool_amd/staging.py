@@ -231,9 +231,13 @@ class DecodeCall:
     """Device inputs and output/workspace buffers of one decode step."""
 
     def __init__(self, cfg, spec, inputs: dict, device="cuda", num_splits: int = 0, block_permutation=None,
-                 framed: bool = False):
+                 framed: bool = False, req_order="longest_first"):
+        """req_order: the order in which the work-groups take the requests, as for PrefillCall."""
         self.cfg = cfg
-        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation, framed)
+        order = longest_first(inputs["num_entries"]) if isinstance(req_order, str) else req_order
+        if isinstance(req_order, str) and req_order != "longest_first":
+            raise ValueError(f"unknown request order {req_order!r}")
+        self.tables = DeviceTables.from_inputs(inputs, device, block_permutation, framed, order)
         self.q = to_device(inputs["q"], spec.dtype, device)
         self.out = torch.empty_like(self.q)
         self.num_splits = num_splits

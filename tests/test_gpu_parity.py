@@ -555,6 +555,28 @@ def test_prefill_long_chunk_tiles_grouped_per_xcd(num_splits):
                         label=f"2048-token chunks, splits={num_splits}, pe={pe}, keys={keys or 'auto'}")
 
 
+def test_decode_request_order_is_bit_identical():
+    say("decode (MQA: 32-column waves; 8B: 16-column waves): requests longest first, reversed, in batch order, "
+        "or through an out-of-range entry agree bit for bit")
+    for cid, kw in ((5, dict(skew=1.2, requests=[0, 24])), (3, dict(requests=[16], n_decode=1))):
+        wl = W.build_workload(W.spec(cid, **kw))
+        s = wl.spec
+        cfg = staging.config_for(s)
+        pools = staging.DevicePools(wl, DEV)
+        staging.append_tokens(cfg, pools, wl.tokens_before_step(1), s.dtype, DEV)
+        d = wl.decode_step(0)
+        staging.append_tokens(cfg, pools, d, s.dtype, DEV)
+        R = len(d["ctx_lens"])
+        odd = np.arange(R, dtype=np.int32)
+        odd[1] = -3                                     # stands for its own index, 1
+        orders = [None, "longest_first", np.arange(R, dtype=np.int32)[::-1].copy(), odd]
+        for splits in (1, 5):
+            outs = [staging.DecodeCall(cfg, s, d, DEV, splits, req_order=o).run(pools).clone() for o in orders]
+            sync()
+            for o in outs[1:]:
+                assert torch.equal(o, outs[0])
+
+
 def test_prefill_request_order_is_bit_identical():
     say("prefill: requests taken longest first, reversed, in batch order, or through an out-of-range entry agree bit for bit")
     wl = W.build_workload(W.spec(5, skew=0.0, requests=[12, 1]))
