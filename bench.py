@@ -53,7 +53,8 @@ COUNTERS = {
 }
 HEADLINE_WORKLOAD = ("prefill, Llama-3.1-70B attention layer (Hq 64, Hkv 8, d 128, RoPE theta 5e5, block 16): "
                      "2048-token causal chunk of each of 4 requests over 64 Zipf(1.0) documents x 512 tokens "
-                     "(32k context); content-only pool, RoPE applied in-kernel; cold (a 1 GiB read evicts the "
+                     "(32k context); content-only pool, RoPE applied at attention time (each request's keys "
+                     "turned once per call, queries in the attention kernel); cold (a 1 GiB read evicts the "
                      "last-level cache before each step)")
 
 
@@ -463,7 +464,8 @@ def headline_json(h, args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": HEADLINE_WORKLOAD, "global_batch": pre["R"], "seq_len": pre["seq_len"],
                    "parallelism": "single-gpu", "key_splits": pre["splits"],
-                   "step": "one prefill call (attention kernel; the merge too when the key range is split)"},
+                   "step": "one prefill call (key-turning kernel and attention kernel; the merge too when the key "
+                           "range is split)"},
         "roofline": roofline,
         "rope_overhead": rope_overhead,
         "decode": decode,
