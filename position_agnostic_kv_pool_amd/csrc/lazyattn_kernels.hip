@@ -12,6 +12,10 @@
 //    tile base) while it is staged into LDS, and that rotated tile is shared
 //    by every query row and every head of the KV group (gist.science,
 //    Technical Implementation > Prefilling: one relative rotation per tile);
+//    a chunk of many query tiles instead has every key of a request turned
+//    once by R(t - c) (c = the request's first new position) in a pass of its
+//    own (turn_keys_kernel), and the attention kernel turns only the queries,
+//    by R(m - c);
 //  - decode: each key row r of a block starting at S is rotated by
 //    R(S - p + r) = R(S - p) R(r); R(S - p) is formed once per block and
 //    R(r) is a per-lane constant (gist.science, Technical Implementation >
