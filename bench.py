@@ -58,9 +58,35 @@ HEADLINE_WORKLOAD = ("prefill, Llama-3.1-70B attention layer (Hq 64, Hkv 8, d 12
                      "last-level cache before each step)")
 
 
+def kernel_code(text: str) -> str:
+    """The kernel source without its comments and with runs of whitespace collapsed: what the
+    compiler sees, so that a comment edit does not orphan counter summaries taken on the same code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256/16 of the kernel code (comments and layout stripped, see kernel_code)."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        return hashlib.sha256(kernel_code(f.read()).encode()).hexdigest()[:16]
 
 
 def read_counter_summary(path: str):
@@ -74,7 +100,7 @@ def read_counter_summary(path: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_code_sha256_16") != kernel_source_hash():
         return None
     try:
         fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
