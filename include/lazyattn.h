@@ -95,7 +95,10 @@ typedef enum { LAZYATTN_PE_ROPE = 0, LAZYATTN_PE_NONE = 1, LAZYATTN_PE_ALIBI = 2
  * never written.  KEYS_FUSED keeps the rotation inside the attention kernel.
  * With neither flag the library turns the keys once when a request spans at
  * least LAZYATTN_KEYS_ONCE_TILES query tiles of 256 rows (ceil(max_q_len /
- * floor(256 / G)) >= 8), where it measured faster.  Both flags set:
+ * floor(256 / G)) >= 8), where it measured faster.  The choice is made per
+ * call from max_q_len, so in a batch mixing one long chunk with short requests
+ * every request's keys are turned once (the short ones gain nothing from it;
+ * such callers can pass KEYS_FUSED or split the batch).  Both flags set:
  * LAZYATTN_EINVAL.  The two routes give the same result up to rounding; other
  * encodings, FP8 pools, framed batches and the decode ignore both flags. */
 #define LAZYATTN_FLAG_KEYS_FUSED 2
