@@ -485,6 +485,15 @@ def test_prefill_keys_once_llama8b_full(num_splits):
     assert mx <= 2e-2 and mn <= 1e-3
 
 
+def test_prefill_keys_once_exact_maximum_route():
+    say("8B prefill, keys turned once (forced) on the two-pass exact-maximum route")
+    wl = W.build_workload(W.spec(2, requests=[6]))
+    pb, got, _ = run_prefill(wl, num_splits=2, keys="once", exact_max=True)
+    orc = OracleState(wl)
+    orc.append(pb)
+    compare_prefill(wl, pb, got, orc, label="8B prefill, keys once, exact route")
+
+
 def test_prefill_keys_once_ragged_edges_and_workspace_reuse():
     say("keys turned once: ragged query tiles, long chunk over few documents, requests without documents, "
         "a zero-length request, one workspace reused by a smaller call")
