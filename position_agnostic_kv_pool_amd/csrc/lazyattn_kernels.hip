@@ -994,7 +994,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint16_t* o_part, cons
 // entries e_begin + w, + 4, ...  Per block (16 keys) a wave computes
 //   S^T (16 keys x 16 heads) = K~ (16 x D) . q^T            4 x 16x16x32 MFMA
 //   O^T (D x 16 heads)      += V^T (D x 16 keys) . P^T      8 x 16x16x16 MFMA
-// with the group's G heads padded to NT tiles of 16.  Lane (g, n) loads key
+// with the group's G heads padded to NT tiles of 16 (NT = 2 for groups of 17..32
+// heads over a plain content-only pool: every block is read and turned once for
+// all of them; over FP8 pools and framed batches such groups run as two
+// work-groups of 16 heads instead).  Lane (g, n) loads key
 // row n, channels 32g..32g+31 (64 contiguous bytes) and V channel rows
 // 16dt + n, keys 4g..4g+3 (8 bytes each); the whole 8 KB block is read once.
 // Scores are formed relative to a per-head reference m that enters the QK
@@ -1016,7 +1019,7 @@ struct DecodeArgs {
   uint16_t* o_part;              // split partials: o / l in fp16 [splits][rows][Hq][D]
   float* ml_part;                // and (m, l) [splits][rows][Hq][2]
   int32_t R, Hq, Hkv, G, max_entries, eps, splits;
-  int32_t halves;                // 2: groups of 17..32 heads, one work-group per 16-head half
+  int32_t halves;                // 2: groups of 17..32 heads as one work-group per 16-head half (FP8, framed)
   float scale_log2;
   RopeRev rope;
   // shared-run decode (items != NULL): work-group (item, KV head) instead of
@@ -1044,7 +1047,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(const DecodeArgs A)
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int G = A.G, Hq = A.Hq, Hkv = A.Hkv;
-  // Groups of more than 16 heads run as two work-groups of 16 heads each over
+  // With halves == 2, groups of more than 16 heads run as two work-groups of 16 heads each over
   // the same entries.  Their linear ids differ by 8, so round-robin dispatch
   // puts them on one XCD at about the same time and the second read of each
   // block hits that XCD's L2: ids 16 j + i and 16 j + 8 + i (i < 8) are the
