@@ -1173,17 +1173,21 @@ def test_fp8_framed_pool_append_prefill_and_decode():
     say(f"framed FP8 decode step 2: max {mx:.2e} mean {mn:.2e}")
 
 
-@pytest.mark.parametrize("hq,fmt,framed", [(24, "plain", False), (24, "fp8", False), (32, "plain", True),
-                                           (24, "fp8", True)])
-def test_decode_group_halves(hq, fmt, framed):
-    # Groups of 17..32 query heads decode as two work-groups of 16 heads each over
+@pytest.mark.parametrize("hq,fmt,framed,pe", [(24, "plain", False, "rope"), (17, "plain", False, "rope"),
+                                              (31, "plain", False, "alibi"), (32, "plain", False, "none"),
+                                              (24, "fp8", False, "rope"), (32, "plain", True, "rope"),
+                                              (24, "fp8", True, "rope")])
+def test_decode_group_halves(hq, fmt, framed, pe):
+    # Groups of 17..32 query heads: over a plain content-only pool one wave holds
+    # them all as two 16-column tiles (17 heads: the second tile holds 1); over FP8
+    # pools and framed batches they decode as two work-groups of 16 heads each over
     # the same entries (24 heads: the second holds 8).  MQA shape, 8 decode
     # requests, step 1, with the heuristic's splits and forced 1 and 5.
-    say(f"decode in head halves: Hq={hq}, Hkv=1, pool {fmt}, framed={framed}")
+    say(f"decode of a group of more than 16 heads: Hq={hq}, Hkv=1, pool {fmt}, framed={framed}, pe={pe}")
     spec = dataclasses.replace(W.spec(5, requests=[0, 8], n_decode=2, skew=1.2), num_q_heads=hq)
     wl = W.build_workload(spec)
     s = wl.spec
-    cfg = staging.config_for(s, kv_format=fmt)
+    cfg = staging.config_for(s, kv_format=fmt, pe=pe)
     pools = (staging.FramedPools if framed else staging.WrittenPools)(wl, cfg, DEV)
     orc = OracleFp8State(wl, framed=framed) if fmt == "fp8" else OracleState(wl)
     hist = wl.tokens_before_step(0)
@@ -1193,13 +1197,13 @@ def test_decode_group_halves(hq, fmt, framed):
         d = wl.decode_step(step)
         staging.append_tokens(cfg, pools, d, s.dtype, DEV)
         orc.append(d)
-    ref = orc.decode(d)
+    ref = orc.decode(d) if fmt == "fp8" else orc.decode(d, pe=pe)
     ref = np.stack([ref[r] for r in range(len(ref))])
     for splits in (0, 1, 5):
         call = staging.DecodeCall(cfg, s, d, DEV, num_splits=splits, framed=framed)
         out = gpu_f64(call.run(pools))
-        mx, mn = assert_parity(out, ref, "bf16", f"halves Hq={hq} {fmt} framed={framed} splits={splits}")
-        say(f"halves Hq={hq} {fmt} framed={framed} splits={call.splits}: max {mx:.2e} mean {mn:.2e}")
+        mx, mn = assert_parity(out, ref, "bf16", f"halves Hq={hq} {fmt} framed={framed} pe={pe} splits={splits}")
+        say(f"halves Hq={hq} {fmt} framed={framed} pe={pe} splits={call.splits}: max {mx:.2e} mean {mn:.2e}")
 
 
 def test_fp8_decode_llama8b():
