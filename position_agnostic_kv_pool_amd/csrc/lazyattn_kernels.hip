@@ -280,14 +280,23 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_bf16_kernel(const Pre
   int kvh = blockIdx.z;
   int r = blockIdx.y;
   if (A.xcd_units) {
-    // work-group L of the dispatch order runs on XCD L % 8: give XCD x the units
-    // (split, request, KV head) u = x, x + 8, ... with all query tiles of each,
-    // so that those tiles, which read the same keys, share one L2 (the host sets
-    // this only when the number of units is a multiple of 8)
+    // work-group L of the dispatch order runs on XCD L % 8.  With U units
+    // (split, request, KV head) a multiple of 8, XCD x takes the units u = x,
+    // x + 8, ... with all query tiles of each, so that those tiles, which read
+    // the same keys, share one L2; with U = 1, 2 or 4 (the host sets this only
+    // when the tiles divide evenly), unit x % U is spread over the 8 / U XCDs
+    // x % U, x % U + U, ... instead of all eight
     const int L = static_cast<int>(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
-    const int k = L >> 3;
-    const int u = (L & 7) + 8 * (k / A.n_qt);
-    qt = k % A.n_qt;
+    const int k = L >> 3, x = L & 7;
+    const int U = A.splits * static_cast<int>(gridDim.y) * static_cast<int>(gridDim.z);
+    int u;
+    if (U % 8 == 0) {
+      u = x + 8 * (k / A.n_qt);
+      qt = k % A.n_qt;
+    } else {
+      u = x % U;
+      qt = x / U + (8 / U) * k;
+    }
     split = u % A.splits;
     r = (u / A.splits) % static_cast<int>(gridDim.y);
     kvh = u / (A.splits * static_cast<int>(gridDim.y));
@@ -1955,6 +1964,15 @@ static lazyattn_status merge_launch(int rows_total, int splits, const void* work
   return launched();
 }
 
+// Whether the prefill groups the query tiles of a (split, request, KV head)
+// unit per XCD: units of at least 32 tiles, U units a multiple of 8, or U
+// dividing 8 with the tiles divisible by 8 / U
+static bool xcd_grouping(long long n_qt, long long U) {
+  if (n_qt < 32 || U < 1) return false;
+  if (U % 8 == 0) return true;
+  return 8 % U == 0 && n_qt % (8 / U) == 0;
+}
+
 // Validates and launches the prefill attention kernel; *splits_out = splits used.
 static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q, const int32_t* cu_q_lens,
                                       int32_t total_q, int32_t max_q_len, const void* k_pool, const void* v_pool,
@@ -2009,7 +2027,7 @@ static lazyattn_status prefill_attend(const lazyattn_config* cfg, const void* q,
                      : nullptr,
                 Hq, Hkv, G, batch->max_entries, total_q, m_q,
                 prefill_entries_per_split(batch->max_entries, splits), splits, static_cast<int32_t>(n_qt),
-                (n_qt >= 32 && (static_cast<long long>(splits) * R * Hkv) % 8 == 0) ? 1 : 0,
+                xcd_grouping(n_qt, static_cast<long long>(splits) * R * Hkv) ? 1 : 0,
                 (cfg->flags & LAZYATTN_FLAG_EXACT_MAX) ? 1 : 0, scale * kLog2e, rope};
   const dim3 grid(static_cast<unsigned>(gx), R, static_cast<unsigned>(Hkv));
   const dim3 block(kPrefillThreads);

@@ -545,23 +545,28 @@ def test_prefill_keys_once_ragged_edges_and_workspace_reuse():
     compare_prefill(small, spb, sout, sorc, label="smaller call in a reused workspace, keys once")
 
 
-@pytest.mark.parametrize("num_splits", [1, 3])
-def test_prefill_long_chunk_tiles_grouped_per_xcd(num_splits):
-    # a 2048-token chunk of the 8B shape spans 32 query tiles per (request, KV head) and the
-    # (split, request, KV head) units are a multiple of 8: every unit's tiles then run on one XCD
-    say(f"8B shape, 2048-token chunks over one document, {num_splits} splits: tiles grouped per XCD, "
+@pytest.mark.parametrize("num_splits,heads", [(1, (32, 8)), (3, (32, 8)), (1, (8, 1))])
+def test_prefill_long_chunk_tiles_grouped_per_xcd(num_splits, heads):
+    # 8B shape: a 2048-token chunk spans 32 query tiles per (request, KV head) and the
+    # (split, request, KV head) units are a multiple of 8, so every unit's tiles run on one
+    # XCD.  Hq 8, Hkv 1 (one GPU's share under 8-way tensor parallelism): 1024 tokens make
+    # 32 tiles and the 2 requests 2 units, each spread over 4 XCDs
+    hq, hkv = heads
+    say(f"Hq {hq} Hkv {hkv}, long chunks over one document, {num_splits} splits: tiles grouped per XCD, "
         "keys turned once / in the kernel / rotation-free")
-    wl = W.build_workload(W.spec(2, requests=[2], q_len=2048, docs=(1, 1)))
+    spec = W.spec(2, requests=[2], q_len=2048 if hkv == 8 else 1024, docs=(1, 1))
+    wl = W.build_workload(dataclasses.replace(spec, num_q_heads=hq, num_kv_heads=hkv))
     pb = wl.prefill_batch()
     orc = OracleState(wl)
     orc.append(pb)
     rng = np.random.default_rng(11)
-    subset = {r: sample_tokens(2048, 12, rng) for r in range(2)}
+    subset = {r: sample_tokens(int(pb["max_q_len"]), 12, rng) for r in range(2)}
     pools = None
     for pe, keys in (("rope", None), ("rope", "fused"), ("none", None)):
         _, got, pools = run_prefill(wl, num_splits=num_splits, pe=pe, keys=keys, pools=pools, pb=pb)
         compare_prefill(wl, pb, got, orc, token_subset=subset, pe=pe,
-                        label=f"2048-token chunks, splits={num_splits}, pe={pe}, keys={keys or 'auto'}")
+                        label=f"{int(pb['max_q_len'])}-token chunks, Hq={hq}, splits={num_splits}, pe={pe}, "
+                              f"keys={keys or 'auto'}")
 
 
 def test_decode_request_order_is_bit_identical():
