@@ -50,6 +50,7 @@ COUNTERS = {
     "decode70b": os.path.join(ROOT, "profiles", "decode_bf16_llama70b_counters.txt"),
     "prefill8b": os.path.join(ROOT, "profiles", "prefill_bf16_llama8b_counters.txt"),
     "decode8b": os.path.join(ROOT, "profiles", "decode_bf16_llama8b_counters.txt"),
+    "mqa": os.path.join(ROOT, "profiles", "prefill_decode_mqa_counters_and_trace.txt"),
 }
 HEADLINE_WORKLOAD = ("prefill, Llama-3.1-70B attention layer (Hq 64, Hkv 8, d 128, RoPE theta 5e5, block 16): "
                      "2048-token causal chunk of each of 4 requests over 64 Zipf(1.0) documents x 512 tokens "
@@ -87,6 +88,25 @@ def kernel_source_hash() -> str:
     """sha256/16 of the kernel code (comments and layout stripped, see kernel_code)."""
     with open(KERNEL_SRC, encoding="utf-8") as f:
         return hashlib.sha256(kernel_code(f.read()).encode()).hexdigest()[:16]
+
+
+def read_mqa_decode_counters(path: str):
+    """{skew: fetch + write bytes per RoPE decode step} from the committed MQA summary, if it
+    was taken on the current kernel code; else {}."""
+    if not os.path.exists(path):
+        return {}
+    out, sha = {}, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("kernel_code_sha256_16:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith("decode RoPE"):
+                parts = line.split()
+                skew = parts[3].rstrip(":")
+                fetch = float(parts[parts.index("fetch_GB") + 1])
+                write = float(parts[parts.index("write_GB") + 1])
+                out[skew] = (fetch + write) * 1e9
+    return out if sha == kernel_source_hash() else {}
 
 
 def read_counter_summary(path: str):
@@ -747,6 +767,10 @@ def bench_mqa_mixed(torch, W, staging, _abi) -> dict:
         row["mixed_rope_overhead"] = round(row["rope"]["mixed_step_us"] / row["none"]["mixed_step_us"] - 1.0, 4)
         row["decode_GB_unique"] = round(by["unique"] / 1e9, 4)
         row["decode_GB_logical"] = round(by["logical"] / 1e9, 4)
+        cb = read_mqa_decode_counters(COUNTERS["mqa"]).get(f"{skew:.1f}")
+        # FETCH + WRITE per step (the committed rocprofv3 summary) over this run's step time
+        row["decode_counter_GB"] = round(cb / 1e9, 4) if cb else None
+        row["decode_counter_GBps"] = round(cb / (row["rope"]["decode_us"] * 1e-6) / 1e9, 1) if cb else None
         row["prefill_GFLOP"] = round(flops / 1e9, 1)
         out[f"skew{skew}"] = row
         del pools, pc_fused
