@@ -854,6 +854,28 @@ def test_framed_prefill_llama8b_full(num_splits):
     say(f"framed vs content-only kernel: max {mx:.2e} mean {mn:.2e}")
 
 
+def test_framed_prefill_long_chunks_ignore_the_key_turning_route():
+    # MQA stress shape (16 query tiles per request): the content-only pool would take the
+    # keys-turned-once route; a framed batch keeps its own kernel, even with KEYS_ONCE set
+    say("framed MQA prefill (16 query tiles per request), library choice and KEYS_ONCE forced: framed kernel")
+    wl = W.build_workload(W.spec(5, skew=1.2, requests=[6, 0]))
+    s = wl.spec
+    orc = OracleState(wl)
+    rng = np.random.default_rng(9)
+    ref = None
+    for keys in (None, "once"):
+        cfg = staging.config_for(s, keys=keys)
+        pools = staging.FramedPools(wl, cfg, DEV)
+        pb = wl.prefill_batch()
+        staging.append_tokens(cfg, pools, pb, s.dtype, DEV)
+        if ref is None:
+            orc.append(pb)
+            subset = {r: sample_tokens(128, 16, rng) for r in range(len(pb["ctx_lens"]))}
+        out = gpu_f64(staging.PrefillCall(cfg, s, pb, DEV, framed=True).run(pools))
+        _, ref = compare_prefill(wl, pb, out, orc, token_subset=subset, ref=ref,
+                                 label=f"framed MQA prefill, keys={keys or 'auto'}")
+
+
 def test_framed_prefill_exact_maximum_route():
     say("framed 8B prefill, exact-maximum route")
     wl = W.build_workload(W.spec(2, requests=[3]))
